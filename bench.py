@@ -1,0 +1,254 @@
+"""Benchmark of absorbed-MQA MLA decode on one MI355X (gfx950).
+
+One step = one mla_decode_partial call over the whole batch: the device
+planner, the split-KV decode kernel (paged latent KV streamed HBM -> LDS,
+QK^T and PV on MFMA, online softmax) and the split combine.  Inputs are
+synthetic and already resident in HBM when the timed region starts; the cache
+rotates over several copies so that repeated steps do not re-read it from the
+256 MB Infinity Cache.
+
+Default workload: the DeepSeek-V3-shape decode (batch 64, q_len 1, 128 heads,
+576/512 latent dims, seq_len 4096, bf16, 64-token pages).  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config c2] [--num-splits 0]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode KV-cache GB/s + TFLOP/s (fraction of MI355X HBM/MFMA roofline)"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+FLOP_PER_ROW_TOKEN = 2 * (576 + 512)
+KERNEL_SRC = os.path.join(ROOT, "mla_latent_decode_absorbed_amd", "csrc", "mla_kernels.hip")
+PMC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_c2_pmc.json")
+
+WORKLOAD_NAMES = {
+    "c2": "DeepSeek-V3-shape decode on one unsharded cache: batch 64, q_len 1, 128 heads, "
+          "576 (512 latent + 64 rope) per token, seq_len 4096, bf16 cache, 64-token pages",
+    "c3": "one DCP rank's share: batch 32, q_len 1, 512 heads (128 x 4), 8192 local tokens of "
+          "32768, bf16 cache, 64-token pages",
+    "c4": "fp8 e4m3 cache: batch 128, q_len 1, 128 heads, seq_len uniform in [1024, 16384]",
+    "c5": "long context: batch 4, q_len 2 (causal), 128 heads, seq_len 131072, bf16 cache",
+}
+
+
+class HipEvents:
+    """hipEvent_t pairs from the HIP runtime (the library records them on the stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev: int) -> None:
+        self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def workload_accounting(inp) -> dict:
+    """Algorithmic bytes and flops of one step (valid tokens only)."""
+    import numpy as np
+    sl = inp.seq_lens.cpu().numpy().astype(np.int64)
+    B, T, H = inp.batch, inp.q_len, inp.heads
+    e = 2 if inp.dtype == "bf16" else 1
+    tokens = int(sl.sum())
+    if inp.causal and T > 1:
+        vis = sum(max(int(n) - (T - 1 - t), 0) for n in sl for t in range(T))
+    else:
+        vis = tokens * T
+    rows = B * T * H
+    kv_bytes = tokens * 576 * e
+    q_bytes = rows * 576 * e
+    bt_bytes = int(((sl + 63) // 64).sum()) * 4 + B * 4
+    out_bytes = rows * 512 * 4 + rows * 4
+    flops = vis * H * FLOP_PER_ROW_TOKEN
+    return dict(kv_bytes=kv_bytes, q_bytes=q_bytes, bt_bytes=bt_bytes, out_bytes=out_bytes,
+                flops=flops, rows=rows, tokens=tokens)
+
+
+def cpu_baseline(inp, budget_s: float = 20.0) -> dict:
+    """The fp64 oracle on this host's cores over whole requests of the same workload
+    (as many as fit a ~budget_s time box, at least one)."""
+    import numpy as np
+    import torch
+    from oracle import bf16_bits_to_f64, decode_partial_ref, e4m3_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        threads = os.cpu_count()
+    bt_all = inp.block_table.cpu().numpy()
+    sl_all = inp.seq_lens.cpu().numpy()
+    dec = bf16_bits_to_f64 if inp.dtype == "bf16" else e4m3_bits_to_f64
+    view = (lambda x: x.view(torch.int16)) if inp.dtype == "bf16" else (lambda x: x)
+    done_bytes, done_req, spent = 0, 0, 0.0
+    e = 2 if inp.dtype == "bf16" else 1
+    for b in range(inp.batch):
+        n = int(sl_all[b])
+        pages = bt_all[b][: (n + 63) // 64]
+        kv_host = view(inp.kv_cache[torch.as_tensor(pages, dtype=torch.long, device=inp.kv_cache.device)]).cpu().numpy()
+        q_host = view(inp.q[b:b + 1]).cpu().numpy()
+        t0 = time.perf_counter()
+        q64 = dec(q_host)
+        kv64 = dec(kv_host)
+        decode_partial_ref(q64, kv64, np.arange(len(pages))[None, :], np.array([n]), inp.scale,
+                           kv_scale=inp.kv_scale_value, causal=inp.causal)
+        spent += time.perf_counter() - t0
+        done_bytes += n * 576 * e
+        done_req += 1
+        if spent >= budget_s:
+            break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done_req} of {inp.batch} requests (whole requests, all heads), "
+                      f"{done_bytes / 1e6:.1f} MB of KV, {spent:.2f} s of fp64 numpy on the host"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over the steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=None)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "DCP shards are materialised on one device, so run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import mla_latent_decode_absorbed_amd as mla
+    import workloads
+
+    dev = torch.device("cuda:0")
+    t_setup = time.perf_counter()
+    if args.config == "c3":
+        inp = workloads.make_config("c3", seed=args.seed, device=dev, poison=False, extra_pages=0,
+                                    shard_only=0)
+    else:
+        inp = workloads.make_config(args.config, seed=args.seed, device=dev, poison=False, extra_pages=0)
+    acc = workload_accounting(inp)
+    desc = mla.make_desc(inp.batch, inp.q_len, inp.heads, inp.kv_cache.shape[0], inp.block_table.shape[1],
+                         kv_dtype=mla.BF16 if inp.dtype == "bf16" else mla.FP8_E4M3,
+                         causal=1 if inp.causal else 0, num_splits=args.num_splits)
+    dec = mla.Decoder(desc, device=dev)
+    copies = [inp.kv_cache] + [inp.kv_cache.clone() for _ in range(max(args.copies, 1) - 1)]
+    out = torch.empty((inp.batch, inp.q_len, inp.heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((inp.batch, inp.q_len, inp.heads), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    hev = HipEvents()
+    evs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        dec(inp.q, copies[i % len(copies)], inp.block_table, inp.seq_lens, inp.scale,
+            kv_scale=inp.kv_scale, out=out, lse=lse, stream=stream, events=events)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [hev.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hev.destroy(a)
+        hev.destroy(b)
+
+    ms_per_step = wall * 1e3 / args.steps
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    kv_gbs = acc["kv_bytes"] / (ms_per_step * 1e-3) / 1e9
+    tflops = acc["flops"] / (ms_per_step * 1e-3) / 1e12
+    total_gbs = (acc["kv_bytes"] + acc["q_bytes"] + acc["bt_bytes"] + acc["out_bytes"]) / (ms_per_step * 1e-3) / 1e9
+    peak_tf = MFMA_PEAK_TFLOPS[inp.dtype]
+    ai = acc["flops"] / (acc["kv_bytes"] + acc["q_bytes"])
+    bound = "hbm" if ai < peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
+    # dominant kernel: the split-KV decode kernel; its algorithmic reads are KV + q + live block-table rows
+    k_bytes = acc["kv_bytes"] + acc["q_bytes"] + acc["bt_bytes"]
+    if bound == "hbm":
+        achieved = k_bytes / (kern_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = acc["flops"] / (kern_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_tf, 4)}
+    traffic = None
+    if os.path.exists(PMC_FILE) and args.config == "c2" and args.num_splits == 0:
+        pmc = json.load(open(PMC_FILE))
+        if pmc.get("kernel_source_sha256_16") == kernel_source_hash():
+            traffic = pmc.get("hbm_bytes_per_launch")
+    roof["traffic"] = traffic
+    roof["kernel_ms"] = round(kern_avg_ms, 5)
+    roof["algorithmic_bytes_per_launch"] = k_bytes
+
+    res = {
+        "metric": METRIC,
+        "value": round(kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": inp.dtype,
+        "data": "synthetic (seeded N(0,1) query and latent cache, shuffled 64-token pages)",
+        "config": {"workload": f"{args.config}: {WORKLOAD_NAMES[args.config]}", "batch": inp.batch,
+                   "q_len": inp.q_len, "heads": inp.heads, "seq_lens_total": acc["tokens"],
+                   "num_splits": args.num_splits or "auto", "cache_copies_rotated": len(copies)},
+        "tflops": round(tflops, 2),
+        "fractions": {"hbm_kv_only": round(kv_gbs / HBM_PEAK_GBS, 4),
+                      "hbm_all_algorithmic_bytes": round(total_gbs / HBM_PEAK_GBS, 4),
+                      "mfma": round(tflops / peak_tf, 4),
+                      "binding_roof": round(max(acc["kv_bytes"] / (HBM_PEAK_GBS * 1e9),
+                                                acc["flops"] / (peak_tf * 1e12)) / (ms_per_step * 1e-3), 4)},
+        "roofline": roof,
+        "setup_s": round(setup_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,162 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) absorbed-MQA MLA decode library.
+ *
+ * What the library computes
+ * -------------------------
+ * Multi-head Latent Attention decode in its absorbed-MQA form: the KV cache is
+ * ONE latent head of 576 values per token (kv_c 512 + k_pe 64), and the query
+ * has been absorbed into that latent space (512 + 64 = 576 per head), so no
+ * per-head K/V is ever expanded (page 4, "MLA Prefill vs Decode", the
+ * Prefill/Decode table and the two paragraphs under it; page 1, "实现拆解"
+ * item 5, the W_UK_T matmul).  For every query row r = (request b, query
+ * token t, head h) and the n visible cache tokens j of this shard:
+ *     s_j   = scale * kv_scale * <q_r, k_j>            (all 576 dims)
+ *     lse_r = ln sum_j exp(s_j)                         (natural log)
+ *     o_r   = kv_scale * sum_j exp(s_j - lse_r) * k_j[0:512]
+ * The decode returns BOTH o and lse (page 2, the forward_mqa line of the
+ * forward_impl excerpt), because under Decode Context Parallelism each rank
+ * holds a sequence shard of the cache, computes partial attention over it,
+ * and the partials are merged with LSE weights (page 4, "什么是 DCP" and
+ * "DCP 在 Prefill 与 Decode 中的不同角色").  The merge is the elementwise LSE
+ * rescaling of merge_attn_states (page 4, "Chunked Prefill 与 LSE Merge").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument named as device memory must point to memory the
+ *    current HIP device can access; the CALLER owns all buffers, including the
+ *    workspace.  The library allocates and frees nothing in these calls and
+ *    keeps no per-call state, so calls on different streams do not interfere
+ *    (two calls sharing one workspace must not overlap in time).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues work: it never synchronises the host.  Results
+ *    are valid once the stream has reached the call.
+ *  - Host-checkable argument errors are reported by the return value BEFORE
+ *    any device work is enqueued (see mla_status).  A failed kernel launch
+ *    returns MLA_ERR_HIP.  Contract violations that only the device could see
+ *    (a live block-table entry outside [0, num_pages), a seq_len beyond
+ *    max_pages_per_seq * page_size) are not checked: seq_lens are clamped to
+ *    the block-table capacity, and a bad page id is undefined behaviour.
+ *  - Layouts are dense, row-major, with no padding unless stated.  Query and
+ *    output rows of a request are ordered (query token t, head h).
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum {
+    MLA_BF16 = 0,      /* bfloat16 */
+    MLA_FP8_E4M3 = 1,  /* OCP FP8 E4M3 ("e4m3fn"), the gfx950 native fp8 */
+    MLA_F32 = 2        /* IEEE binary32 */
+} mla_dtype;
+
+/* Return codes. */
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or shape */
+    MLA_ERR_UNSUPPORTED = -2,  /* valid but not supported combination */
+    MLA_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+    MLA_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed */
+} mla_status;
+
+/* Fixed model dimensions of the latent cache (page 4: 512 + 64 = 576). */
+#define MLA_LATENT_DIM 512
+#define MLA_ROPE_DIM 64
+#define MLA_QK_DIM 576
+/* The only supported page size (tokens per cache page). */
+#define MLA_PAGE_SIZE 64
+
+/* Shape and type descriptor of one decode call (one DCP shard).
+ * The decode schedule is sized by q_len * num_heads rows per request, with ONE
+ * KV head; under DCP the gathered or replicated query carries num_heads already
+ * multiplied by the DCP world size (page 2, "实现拆解" item 2 and the
+ * FlashMLA _build_decode excerpt). */
+typedef struct mla_decode_desc {
+    int32_t batch;              /* B >= 1 requests */
+    int32_t q_len;              /* query tokens per request, 1 .. 16 */
+    int32_t num_heads;          /* H >= 1 query heads (x DCP world size if gathered) */
+    int32_t page_size;          /* must be MLA_PAGE_SIZE */
+    int32_t num_pages;          /* pages in the cache pool, >= 1 */
+    int32_t max_pages_per_seq;  /* row stride of block_table, >= 1 */
+    int32_t kv_dtype;           /* MLA_BF16 or MLA_FP8_E4M3; q has the same dtype */
+    int32_t out_dtype;          /* MLA_F32 or MLA_BF16 for `out` */
+    int32_t causal;             /* q_len > 1 only: 1 = query token t sees the first
+                                   seq_len - (q_len - 1 - t) tokens; 0 = all tokens */
+    int32_t num_splits;         /* 0 = automatic split-KV; k > 0 = exactly
+                                   min(k, pages of the request) splits per request */
+} mla_decode_desc;
+
+/* Bytes of device workspace mla_decode_partial needs for `desc`.
+ * Depends only on the descriptor (never on seq_lens), so a caller can size it
+ * once.  Returns MLA_OK, or MLA_ERR_INVALID_ARG / MLA_ERR_UNSUPPORTED for a bad
+ * descriptor.  No device access. */
+int mla_decode_workspace_size(const mla_decode_desc* desc, size_t* bytes);
+
+/* Absorbed-MQA decode of one KV shard: partial output + LSE per query row.
+ * (page 4, "MLA Prefill vs Decode"; page 2, the forward_mqa call that returns
+ *  attn_out and lse; page 2 FlashMLA excerpt for the per-step split metadata
+ *  built from seq_lens and q_len x heads with one KV head.)
+ *
+ *   q           device, [B][q_len][H][576] of kv_dtype (bf16, or e4m3 codes);
+ *               16-byte aligned.  For fp8 the caller folds its per-tensor query
+ *               scale into `scale`.
+ *   kv_cache    device, [num_pages][64][576] of kv_dtype, 16-byte aligned.
+ *               Token j of request b is row j % 64 of page block_table[b][j / 64].
+ *               Cache rows past seq_len and unused pages are never used.
+ *   kv_scale    device float[1]: the per-tensor cache scale for MLA_FP8_E4M3
+ *               (required); must be NULL for MLA_BF16.
+ *   block_table device int32 [B][max_pages_per_seq]; entries at or beyond
+ *               ceil(seq_len / 64) are never read (may be -1).
+ *   seq_lens    device int32 [B]: cache tokens per request in this shard,
+ *               including the q_len new ones; 0 is allowed (empty shard).
+ *   scale       softmax scale applied to q.k (e.g. 1/sqrt(192)).
+ *   out         device, [B][q_len][H][512] of out_dtype, 16-byte aligned.
+ *   lse         device float [B][q_len][H]: natural-log LSE of the scaled
+ *               logits; -inf (and out = 0) for a row that sees no token.
+ *   workspace   device, >= mla_decode_workspace_size() bytes, 256-byte aligned.
+ * Work: a planning kernel reads seq_lens on the device and writes the split
+ * list into the workspace; the split-KV decode kernel streams the pages; a
+ * combine kernel LSE-merges the splits of each row into `out` / `lse`.
+ * Returns MLA_OK or a negative mla_status (before any device work on a bad
+ * argument). */
+int mla_decode_partial(const mla_decode_desc* desc, const void* q, const void* kv_cache,
+                       const float* kv_scale, const int32_t* block_table,
+                       const int32_t* seq_lens, float scale, void* out, float* lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same as mla_decode_partial; additionally records the two hipEvent_t
+ * (passed as void*, either may be NULL) on `stream` immediately before and
+ * after the split-KV decode kernel, so a caller can time that kernel alone. */
+int mla_decode_partial_timed(const mla_decode_desc* desc, const void* q, const void* kv_cache,
+                             const float* kv_scale, const int32_t* block_table,
+                             const int32_t* seq_lens, float scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* event_before_decode, void* event_after_decode);
+
+/* LSE merge of n partial results per row (page 4, "Chunked Prefill 与 LSE
+ * Merge": merge_attn_states' elementwise LSE rescaling; "DCP 在 Prefill 与
+ * Decode 中的不同角色": DCP decode merges per-rank partials with LSE weights).
+ *   outs   device float [n][rows][512], 16-byte aligned (partial i at outs + i*rows*512)
+ *   lses   device float [n][rows] (natural log; -inf marks an empty partial)
+ *   out    device [rows][512] of out_dtype (MLA_F32 or MLA_BF16), 16-byte aligned
+ *   lse    device float [rows]
+ * Per row: lse = ln sum_i exp(lse_i); out = sum_i exp(lse_i - lse) * outs_i;
+ * a row whose inputs are all empty gets out = 0, lse = -inf.
+ * n in 1 .. 4096, rows >= 0.  out/lse must not overlap the inputs. */
+int mla_merge_states(const float* outs, const float* lses, int32_t n, int32_t rows,
+                     void* out, float* lse, int32_t out_dtype, void* stream);
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char* mla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,183 @@
+"""Python binding of libmla_decode.so: absorbed-MQA MLA decode + LSE merge on gfx950.
+
+Argument marshalling only.  Every step of the decode (planning, paged KV
+streaming, both contractions, the online softmax, the split combine and the
+shard merge) runs in the library's HIP kernels; PyTorch supplies device memory
+and the current stream.  The entry points mirror include/mla_decode.h:
+
+    workspace_size(desc) -> int
+    decode_partial(desc, q, kv_cache, kv_scale, block_table, seq_lens, scale,
+                   out, lse, workspace, stream=None)
+    merge_states(outs, lses, n, rows, out, lse, out_dtype=F32, stream=None)
+
+plus ``Decoder``, which owns a workspace and allocates outputs.
+
+Importing this package loads the shared library and raises if it is missing
+or unloadable: there is no fallback implementation.
+
+PyTorch is imported before the library is loaded.  PyTorch ships its own HIP
+runtime with the same soname (libamdhip64.so.7) as the system one the library
+is linked against; whichever is loaded first serves the whole process.  Loading
+PyTorch's first makes the library run on the runtime that owns the tensors
+and streams it is handed (the other order makes kernel launches fail).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (must precede the library load, see above)
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmla_decode.so")
+
+BF16, FP8_E4M3, F32 = 0, 1, 2
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+LATENT_DIM, ROPE_DIM, QK_DIM, PAGE_SIZE = 512, 64, 576, 64
+
+#: every symbol include/mla_decode.h declares
+EXPORTS = (
+    "mla_decode_workspace_size",
+    "mla_decode_partial",
+    "mla_decode_partial_timed",
+    "mla_merge_states",
+    "mla_status_string",
+)
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class DecodeDesc(ctypes.Structure):
+    """mla_decode_desc of include/mla_decode.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+    def __repr__(self):
+        return "DecodeDesc(" + ", ".join(f"{k}={getattr(self, k)}" for k, _ in self._fields_) + ")"
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m mla_latent_decode_absorbed_amd.build` "
+                          "or __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
+    pdesc = ctypes.POINTER(DecodeDesc)
+    lib.mla_decode_workspace_size.argtypes = [pdesc, ctypes.POINTER(sz)]
+    lib.mla_decode_workspace_size.restype = ctypes.c_int
+    dec_args = [pdesc, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
+    lib.mla_decode_partial.argtypes = dec_args
+    lib.mla_decode_partial.restype = ctypes.c_int
+    lib.mla_decode_partial_timed.argtypes = dec_args + [vp, vp]
+    lib.mla_decode_partial_timed.restype = ctypes.c_int
+    lib.mla_merge_states.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp]
+    lib.mla_merge_states.restype = ctypes.c_int
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.mla_status_string(int(status)).decode()
+
+
+def _ptr(x) -> int | None:
+    """Device address of a tensor (or a raw int / None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_desc(batch, q_len, num_heads, num_pages, max_pages_per_seq, kv_dtype=BF16,
+              out_dtype=F32, causal=None, num_splits=0, page_size=PAGE_SIZE) -> DecodeDesc:
+    if causal is None:
+        causal = 1 if q_len > 1 else 0
+    return DecodeDesc(int(batch), int(q_len), int(num_heads), int(page_size), int(num_pages),
+                      int(max_pages_per_seq), int(kv_dtype), int(out_dtype), int(causal),
+                      int(num_splits))
+
+
+def workspace_size(desc: DecodeDesc) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib.mla_decode_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != OK:
+        raise MlaError(st, "mla_decode_workspace_size")
+    return n.value
+
+
+def decode_partial(desc: DecodeDesc, q, kv_cache, kv_scale, block_table, seq_lens, scale: float,
+                   out, lse, workspace, workspace_bytes: int | None = None, stream=None,
+                   events=None) -> None:
+    """Enqueue mla_decode_partial on ``stream`` (default: torch's current stream)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    args = [ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(kv_scale), _ptr(block_table),
+            _ptr(seq_lens), ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+            ctypes.c_size_t(workspace_bytes), _stream(stream)]
+    if events is None:
+        st = lib.mla_decode_partial(*args)
+    else:
+        st = lib.mla_decode_partial_timed(*args, events[0], events[1])
+    if st != OK:
+        raise MlaError(st, "mla_decode_partial")
+
+
+def merge_states(outs, lses, n: int, rows: int, out, lse, out_dtype: int = F32, stream=None) -> None:
+    """Enqueue mla_merge_states: outs [n][rows][512] f32, lses [n][rows] -> out, lse."""
+    st = lib.mla_merge_states(_ptr(outs), _ptr(lses), int(n), int(rows), _ptr(out), _ptr(lse),
+                              int(out_dtype), _stream(stream))
+    if st != OK:
+        raise MlaError(st, "mla_merge_states")
+
+
+class Decoder:
+    """Owns the workspace for one descriptor and allocates outputs (torch tensors)."""
+
+    def __init__(self, desc: DecodeDesc, device="cuda"):
+        import torch
+        self.desc = desc
+        self.ws_bytes = workspace_size(desc)
+        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
+
+    def __call__(self, q, kv_cache, block_table, seq_lens, scale: float, kv_scale=None,
+                 out=None, lse=None, stream=None, events=None):
+        import torch
+        d = self.desc
+        rows = d.q_len * d.num_heads
+        if out is None:
+            dt = torch.float32 if d.out_dtype == F32 else torch.bfloat16
+            out = torch.empty((d.batch, d.q_len, d.num_heads, LATENT_DIM), dtype=dt, device=q.device)
+        if lse is None:
+            lse = torch.empty((d.batch, d.q_len, d.num_heads), dtype=torch.float32, device=q.device)
+        assert out.numel() == d.batch * rows * LATENT_DIM and lse.numel() == d.batch * rows
+        decode_partial(d, q, kv_cache, kv_scale, block_table, seq_lens, scale, out, lse,
+                       self.workspace, self.ws_bytes, stream=stream, events=events)
+        return out, lse

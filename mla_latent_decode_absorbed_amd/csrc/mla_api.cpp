@@ -1,0 +1,189 @@
+// C ABI of the gfx950 MLA decode library: argument validation, workspace
+// layout and kernel launches.  Declarations and contracts: include/mla_decode.h.
+#include "mla_decode.h"
+#include "mla_internal.h"
+
+#include <math.h>
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Byte offsets of the workspace regions for one descriptor.
+struct WorkspaceLayout {
+    size_t req_info, work, ws_lse, ws_o, total;
+    int64_t units_max;
+    int m_tiles;
+};
+
+int check_desc(const mla_decode_desc* d) {
+    if (!d) return MLA_ERR_INVALID_ARG;
+    if (d->batch < 1 || d->q_len < 1 || d->num_heads < 1) return MLA_ERR_INVALID_ARG;
+    if (d->num_pages < 1 || d->max_pages_per_seq < 1) return MLA_ERR_INVALID_ARG;
+    if (d->num_splits < 0 || (d->causal != 0 && d->causal != 1)) return MLA_ERR_INVALID_ARG;
+    if (d->kv_dtype != MLA_BF16 && d->kv_dtype != MLA_FP8_E4M3) return MLA_ERR_INVALID_ARG;
+    if (d->out_dtype != MLA_F32 && d->out_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
+    if (d->page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+    if (d->q_len > 16) return MLA_ERR_UNSUPPORTED;
+    if (d->kv_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+    const int64_t rows = (int64_t)d->q_len * d->num_heads;
+    if (rows > (1 << 20)) return MLA_ERR_UNSUPPORTED;
+    if ((int64_t)d->max_pages_per_seq * MLA_PAGE_SIZE > INT32_MAX / 2) return MLA_ERR_UNSUPPORTED;
+    if ((int64_t)d->batch * d->max_pages_per_seq > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+    if (d->batch > (1 << 20)) return MLA_ERR_UNSUPPORTED;
+    return MLA_OK;
+}
+
+WorkspaceLayout layout_for(const mla_decode_desc* d) {
+    WorkspaceLayout L;
+    const int rows = d->q_len * d->num_heads;
+    L.m_tiles = (rows + mla::kMTile - 1) / mla::kMTile;
+    L.units_max = mla::units_bound(d->batch, L.m_tiles, d->max_pages_per_seq, d->num_splits);
+    size_t off = 0;
+    L.req_info = off;
+    off = align_up(off + sizeof(int32_t) * 2 * (size_t)d->batch);
+    L.work = off;
+    off = align_up(off + sizeof(mla::WorkItem) * (size_t)L.units_max);
+    L.ws_lse = off;
+    off = align_up(off + sizeof(float) * (size_t)L.units_max * mla::kMTile);
+    L.ws_o = off;
+    off = align_up(off + sizeof(float) * (size_t)L.units_max * mla::kMTile * mla::kV);
+    L.total = off;
+    return L;
+}
+
+int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const float* kv_scale,
+                const int32_t* block_table, const int32_t* seq_lens, float scale, void* out,
+                float* lse, void* workspace, size_t workspace_bytes, void* stream, void* ev0,
+                void* ev1) {
+    int st = check_desc(d);
+    if (st != MLA_OK) return st;
+    if (!q || !kv || !block_table || !seq_lens || !out || !lse) return MLA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
+        !aligned(block_table, 4) || !aligned(seq_lens, 4))
+        return MLA_ERR_INVALID_ARG;
+    if (d->kv_dtype == MLA_FP8_E4M3 ? (kv_scale == nullptr) : (kv_scale != nullptr))
+        return MLA_ERR_INVALID_ARG;
+    if (!isfinite(scale)) return MLA_ERR_INVALID_ARG;
+    const WorkspaceLayout L = layout_for(d);
+    if (!workspace || !aligned(workspace, kAlign)) return MLA_ERR_WORKSPACE;
+    if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+    if (L.units_max > INT32_MAX / mla::kMTile) return MLA_ERR_UNSUPPORTED;
+
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    int32_t* req_info = (int32_t*)(ws + L.req_info);
+    mla::WorkItem* work = (mla::WorkItem*)(ws + L.work);
+    const int rows = d->q_len * d->num_heads;
+
+    mla::PlanParams pp;
+    pp.batch = d->batch;
+    pp.rows = rows;
+    pp.m_tiles = L.m_tiles;
+    pp.max_pages = d->max_pages_per_seq;
+    pp.num_splits = d->num_splits;
+    pp.target_units = mla::kTargetUnits;
+    pp.min_chunk = mla::kMinChunkPages;
+    pp.units_max = (int32_t)L.units_max;
+    if (mla::launch_plan(pp, seq_lens, req_info, work, s) != hipSuccess) return MLA_ERR_HIP;
+
+    mla::DecodeParams dp;
+    dp.q = q;
+    dp.kv = kv;
+    dp.kv_scale = kv_scale;
+    dp.block_table = block_table;
+    dp.seq_lens = seq_lens;
+    dp.work = work;
+    dp.out = out;
+    dp.lse = lse;
+    dp.ws_o = (float*)(ws + L.ws_o);
+    dp.ws_lse = (float*)(ws + L.ws_lse);
+    dp.scale_log2 = scale * 1.4426950408889634f;
+    dp.rows = rows;
+    dp.heads = d->num_heads;
+    dp.q_len = d->q_len;
+    dp.causal = d->q_len > 1 ? d->causal : 0;
+    dp.max_pages = d->max_pages_per_seq;
+    dp.out_bf16 = d->out_dtype == MLA_BF16;
+    if (mla::launch_decode_bf16(dp, (int)L.units_max, s, (hipEvent_t)ev0, (hipEvent_t)ev1) != hipSuccess)
+        return MLA_ERR_HIP;
+
+    mla::CombineParams cp;
+    cp.req_info = req_info;
+    cp.ws_o = dp.ws_o;
+    cp.ws_lse = dp.ws_lse;
+    cp.out = out;
+    cp.lse = lse;
+    cp.batch = d->batch;
+    cp.rows = rows;
+    cp.m_tiles = L.m_tiles;
+    cp.out_bf16 = dp.out_bf16;
+    if (mla::launch_combine(cp, s) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_workspace_size(const mla_decode_desc* desc, size_t* bytes) {
+    if (!bytes) return MLA_ERR_INVALID_ARG;
+    const int st = check_desc(desc);
+    if (st != MLA_OK) return st;
+    *bytes = layout_for(desc).total;
+    return MLA_OK;
+}
+
+int mla_decode_partial(const mla_decode_desc* desc, const void* q, const void* kv_cache,
+                       const float* kv_scale, const int32_t* block_table, const int32_t* seq_lens,
+                       float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    return decode_impl(desc, q, kv_cache, kv_scale, block_table, seq_lens, scale, out, lse,
+                       workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int mla_decode_partial_timed(const mla_decode_desc* desc, const void* q, const void* kv_cache,
+                             const float* kv_scale, const int32_t* block_table,
+                             const int32_t* seq_lens, float scale, void* out, float* lse,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* event_before_decode, void* event_after_decode) {
+    return decode_impl(desc, q, kv_cache, kv_scale, block_table, seq_lens, scale, out, lse,
+                       workspace, workspace_bytes, stream, event_before_decode, event_after_decode);
+}
+
+int mla_merge_states(const float* outs, const float* lses, int32_t n, int32_t rows, void* out,
+                     float* lse, int32_t out_dtype, void* stream) {
+    if (n < 1 || n > 4096 || rows < 0) return MLA_ERR_INVALID_ARG;
+    if (out_dtype != MLA_F32 && out_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
+    if (rows == 0) return MLA_OK;
+    if (!outs || !lses || !out || !lse) return MLA_ERR_INVALID_ARG;
+    if (!aligned(outs, 16) || !aligned(out, 16) || !aligned(lses, 4) || !aligned(lse, 4))
+        return MLA_ERR_INVALID_ARG;
+    mla::MergeParams mp;
+    mp.outs = outs;
+    mp.lses = lses;
+    mp.out = out;
+    mp.lse = lse;
+    mp.n = n;
+    mp.rows = rows;
+    mp.out_bf16 = out_dtype == MLA_BF16;
+    if (mla::launch_merge(mp, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+const char* mla_status_string(int status) {
+    switch (status) {
+        case MLA_OK: return "ok";
+        case MLA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, bad size or shape)";
+        case MLA_ERR_UNSUPPORTED: return "unsupported combination (page size, q_len, dtype or size limit)";
+        case MLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case MLA_ERR_HIP: return "HIP runtime error or kernel launch failure";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

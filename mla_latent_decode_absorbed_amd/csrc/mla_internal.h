@@ -1,0 +1,93 @@
+// Internal declarations shared by the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kQK = 576;          // latent 512 + rope 64
+constexpr int kV = 512;           // V = the latent part of the same cache row
+constexpr int kPage = 64;         // tokens per cache page
+constexpr int kMTile = 64;        // query rows per decode workgroup (heads x query tokens)
+constexpr int kTargetUnits = 256; // automatic split target: one workgroup per CU (256 CUs)
+constexpr int kMinChunkPages = 2; // smallest automatic split, in pages
+
+// One unit of split-KV work: rows [mt*kMTile, +kMTile) of request b over the
+// pages [page_begin, page_end) of its block table.  b < 0 marks an empty slot.
+struct WorkItem {
+    int32_t b, mt, split, page_begin, page_end, nsplit, pad0, pad1;
+};
+
+struct PlanParams {
+    int32_t batch, rows, m_tiles, max_pages, num_splits, target_units, min_chunk, units_max;
+};
+
+struct DecodeParams {
+    const void* q;              // [B][M][576]
+    const void* kv;             // [P][64][576]
+    const float* kv_scale;      // fp8 only
+    const int32_t* block_table; // [B][max_pages]
+    const int32_t* seq_lens;    // [B]
+    const WorkItem* work;       // [units_max]
+    void* out;                  // [B][M][512] of out_dtype
+    float* lse;                 // [B][M]
+    float* ws_o;                // [units_max][kMTile][512]
+    float* ws_lse;              // [units_max][kMTile]
+    float scale_log2;           // scale * log2(e)
+    int32_t rows;               // M = q_len * H
+    int32_t heads;
+    int32_t q_len;
+    int32_t causal;
+    int32_t max_pages;
+    int32_t out_bf16;
+};
+
+struct CombineParams {
+    const int32_t* req_info;    // [B][2]: splits, first kv-unit index
+    const float* ws_o;
+    const float* ws_lse;
+    void* out;
+    float* lse;
+    int32_t batch, rows, m_tiles, out_bf16;
+};
+
+struct MergeParams {
+    const float* outs;          // [n][rows][512]
+    const float* lses;          // [n][rows]
+    void* out;
+    float* lse;
+    int32_t n, rows, out_bf16;
+};
+
+// Unit index of kv-unit k (one request x split) for M-tile mt: kv-units are
+// dealt to the 8 XCDs round-robin and the m_tiles M-tiles of one kv-unit land
+// on the same XCD in consecutive dispatch slots, so they share its L2.
+__host__ __device__ inline int unit_index(int k, int mt, int m_tiles) {
+    return ((k >> 3) * m_tiles + mt) * 8 + (k & 7);
+}
+
+// Upper bound on kv-units (request x split) for a descriptor.
+inline int64_t kv_units_bound(int batch, int m_tiles, int max_pages, int num_splits) {
+    if (num_splits > 0) {
+        int64_t per = num_splits < max_pages ? num_splits : max_pages;
+        if (per < 1) per = 1;
+        return (int64_t)batch * per;
+    }
+    return (int64_t)kTargetUnits / m_tiles + batch;
+}
+
+inline int64_t units_bound(int batch, int m_tiles, int max_pages, int num_splits) {
+    int64_t k = kv_units_bound(batch, m_tiles, max_pages, num_splits);
+    return ((k + 7) / 8) * 8 * m_tiles;
+}
+
+hipError_t launch_plan(const PlanParams& p, const int32_t* seq_lens, int32_t* req_info,
+                       WorkItem* work, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeParams& p, int units, hipStream_t stream,
+                              hipEvent_t ev_before, hipEvent_t ev_after);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+
+}  // namespace mla

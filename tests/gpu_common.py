@@ -1,0 +1,94 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI,
+run the oracle on the exact same bytes, compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import bf16_bits_to_f64, decode_partial_ref, e4m3_bits_to_f64, merge_ref
+
+#: max-abs-error bars (bf16: out 1e-2, lse 1e-3; fp8 cache: out 3e-2)
+TOL = {"bf16": (1e-2, 1e-3), "fp8": (3e-2, 1e-2)}
+
+
+def say(msg: str) -> None:
+    """Name the case on stdout before any GPU work, so a fault can be attributed."""
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def run_hip(inp, num_splits: int = 0, out_dtype=None, stream=None):
+    import mla_latent_decode_absorbed_amd as mla
+    if out_dtype is None:
+        out_dtype = mla.F32
+    desc = mla.make_desc(inp.batch, inp.q_len, inp.heads, inp.kv_cache.shape[0],
+                         inp.block_table.shape[1],
+                         kv_dtype=mla.BF16 if inp.dtype == "bf16" else mla.FP8_E4M3,
+                         out_dtype=out_dtype, causal=1 if inp.causal else 0, num_splits=num_splits)
+    dec = mla.Decoder(desc, device=inp.q.device)
+    out, lse = dec(inp.q, inp.kv_cache, inp.block_table, inp.seq_lens, inp.scale,
+                   kv_scale=inp.kv_scale, stream=stream)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def to_f64_q(inp, requests=None):
+    q = inp.q if requests is None else inp.q[requests]
+    if inp.dtype == "bf16":
+        return bf16_bits_to_f64(q.view(torch.int16).cpu().numpy())
+    return e4m3_bits_to_f64(q.cpu().numpy())
+
+
+def cache_f64(inp, pages=None):
+    kv = inp.kv_cache if pages is None else inp.kv_cache[pages]
+    if inp.dtype == "bf16":
+        return bf16_bits_to_f64(kv.view(torch.int16).cpu().numpy())
+    return e4m3_bits_to_f64(kv.cpu().numpy())
+
+
+def run_oracle(inp, requests=None):
+    """Oracle on the device bytes; ``requests`` restricts to a sample (others NaN)."""
+    bt = inp.block_table.cpu().numpy()
+    sl = inp.seq_lens.cpu().numpy()
+    if requests is None:
+        q = to_f64_q(inp)
+        kv = cache_f64(inp)
+        return decode_partial_ref(q, kv, bt, sl, inp.scale, kv_scale=inp.kv_scale_value,
+                                  causal=inp.causal)
+    # copy back only the sampled requests' pages
+    req = list(requests)
+    pages = sorted({int(p) for b in req for p in bt[b][: (int(sl[b]) + 63) // 64]})
+    remap = {p: i for i, p in enumerate(pages)}
+    kv = cache_f64(inp, torch.tensor(pages, dtype=torch.long, device=inp.kv_cache.device))
+    bt_s = np.full((len(req), bt.shape[1]), -1, dtype=np.int64)
+    for i, b in enumerate(req):
+        for j in range((int(sl[b]) + 63) // 64):
+            bt_s[i, j] = remap[int(bt[b][j])]
+    q = to_f64_q(inp, torch.tensor(req, dtype=torch.long, device=inp.q.device))
+    return decode_partial_ref(q, kv, bt_s, sl[req], inp.scale, kv_scale=inp.kv_scale_value,
+                              causal=inp.causal)
+
+
+def compare(out, lse, o_ref, l_ref, dtype="bf16", what=""):
+    """Element-by-element max-abs check of out and lse, -inf rows included."""
+    o = out.double().cpu().numpy()
+    l = lse.double().cpu().numpy()
+    tol_o, tol_l = TOL[dtype]
+    assert o.shape == o_ref.shape, (o.shape, o_ref.shape)
+    ninf_ref = np.isneginf(l_ref)
+    assert np.array_equal(np.isneginf(l), ninf_ref), f"{what}: empty-row pattern differs"
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    err_o = float(np.max(np.abs(o - o_ref))) if o.size else 0.0
+    fin = ~ninf_ref
+    err_l = float(np.max(np.abs(l[fin] - l_ref[fin]))) if fin.any() else 0.0
+    print(f"  {what}: max|dout| = {err_o:.3e} (bar {tol_o}), max|dlse| = {err_l:.3e} (bar {tol_l})",
+          flush=True)
+    assert err_o <= tol_o, f"{what}: out error {err_o} > {tol_o}"
+    assert err_l <= tol_l, f"{what}: lse error {err_l} > {tol_l}"
+    return err_o, err_l
+
+
+def merge_oracle_rows(outs, lses):
+    return merge_ref(np.stack(outs), np.stack(lses))

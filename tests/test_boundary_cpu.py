@@ -1,0 +1,127 @@
+"""The C-ABI library loads, exports every symbol include/mla_decode.h declares,
+and rejects bad arguments with the documented status before any device work.
+
+No GPU is needed: every call here fails host-side validation (or only sizes the
+workspace), so nothing is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_latent_decode_absorbed_amd as mla
+
+pytestmark = pytest.mark.cpu
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla_decode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(mla.EXPORTS)
+
+
+@pytest.mark.parametrize("name", sorted(mla.EXPORTS))
+def test_library_exports_symbol(name):
+    lib = ctypes.CDLL(mla.LIB_PATH)
+    assert hasattr(lib, name)
+
+
+def test_status_strings():
+    for st in (mla.OK, mla.ERR_INVALID_ARG, mla.ERR_UNSUPPORTED, mla.ERR_WORKSPACE, mla.ERR_HIP):
+        assert mla.status_string(st) and "unknown" not in mla.status_string(st)
+    assert "unknown" in mla.status_string(12345)
+
+
+def good_desc(**kw):
+    d = dict(batch=2, q_len=1, num_heads=16, num_pages=6, max_pages_per_seq=2)
+    d.update(kw)
+    return mla.make_desc(**d)
+
+
+def test_workspace_size_is_positive_and_descriptor_only():
+    a = mla.workspace_size(good_desc())
+    b = mla.workspace_size(good_desc(num_pages=6000))      # pool size does not matter
+    assert a > 0 and a == b
+    assert mla.workspace_size(good_desc(num_splits=4)) > 0
+    big = mla.workspace_size(good_desc(batch=64, num_heads=128, max_pages_per_seq=64))
+    assert big > a
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, mla.ERR_INVALID_ARG),
+    ("q_len", 0, mla.ERR_INVALID_ARG),
+    ("num_heads", -1, mla.ERR_INVALID_ARG),
+    ("num_pages", 0, mla.ERR_INVALID_ARG),
+    ("max_pages_per_seq", 0, mla.ERR_INVALID_ARG),
+    ("kv_dtype", 7, mla.ERR_INVALID_ARG),
+    ("out_dtype", mla.FP8_E4M3, mla.ERR_INVALID_ARG),
+    ("causal", 2, mla.ERR_INVALID_ARG),
+    ("num_splits", -1, mla.ERR_INVALID_ARG),
+    ("page_size", 32, mla.ERR_UNSUPPORTED),
+    ("q_len", 17, mla.ERR_UNSUPPORTED),
+])
+def test_bad_descriptor_rejected(field, value, status):
+    d = good_desc()
+    setattr(d, field, value)
+    n = ctypes.c_size_t(0)
+    assert mla.lib.mla_decode_workspace_size(ctypes.byref(d), ctypes.byref(n)) == status
+    rc = mla.lib.mla_decode_partial(ctypes.byref(d), 4096, 4096, None, 4096, 4096, ctypes.c_float(0.1),
+                                    4096, 4096, 4096, ctypes.c_size_t(1 << 30), None)
+    assert rc == status
+
+
+def _call(desc, q=4096, kv=4096, kv_scale=None, bt=4096, sl=4096, scale=0.1, out=4096, lse=4096,
+          ws=4096, ws_bytes=1 << 34):
+    return mla.lib.mla_decode_partial(ctypes.byref(desc), q, kv, kv_scale, bt, sl, ctypes.c_float(scale),
+                                      out, lse, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_null_and_misaligned_pointers_rejected():
+    d = good_desc()
+    assert _call(d, q=None) == mla.ERR_INVALID_ARG
+    assert _call(d, kv=None) == mla.ERR_INVALID_ARG
+    assert _call(d, bt=None) == mla.ERR_INVALID_ARG
+    assert _call(d, sl=None) == mla.ERR_INVALID_ARG
+    assert _call(d, out=None) == mla.ERR_INVALID_ARG
+    assert _call(d, lse=None) == mla.ERR_INVALID_ARG
+    assert _call(d, q=4096 + 8) == mla.ERR_INVALID_ARG
+    assert _call(d, kv=4096 + 4) == mla.ERR_INVALID_ARG
+    assert _call(d, out=4096 + 4) == mla.ERR_INVALID_ARG
+    assert _call(d, bt=4096 + 2) == mla.ERR_INVALID_ARG
+    assert _call(d, scale=float("nan")) == mla.ERR_INVALID_ARG
+    assert _call(d, kv_scale=4096) == mla.ERR_INVALID_ARG          # bf16 takes no kv_scale
+
+
+def test_workspace_checks():
+    d = good_desc()
+    need = mla.workspace_size(d)
+    assert _call(d, ws=None) == mla.ERR_WORKSPACE
+    assert _call(d, ws=4096 + 128) == mla.ERR_WORKSPACE              # not 256-byte aligned
+    assert _call(d, ws_bytes=need - 1) == mla.ERR_WORKSPACE
+
+
+def test_fp8_requires_kv_scale():
+    d = good_desc(kv_dtype=mla.FP8_E4M3)
+    n = ctypes.c_size_t(0)
+    st = mla.lib.mla_decode_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    if st == mla.ERR_UNSUPPORTED:
+        pytest.skip("fp8 path not built into this library")
+    assert _call(d, kv_scale=None) == mla.ERR_INVALID_ARG
+
+
+def test_merge_argument_checks():
+    f = mla.lib.mla_merge_states
+    assert f(4096, 4096, 0, 10, 4096, 4096, mla.F32, None) == mla.ERR_INVALID_ARG
+    assert f(4096, 4096, 4097, 10, 4096, 4096, mla.F32, None) == mla.ERR_INVALID_ARG
+    assert f(4096, 4096, 2, -1, 4096, 4096, mla.F32, None) == mla.ERR_INVALID_ARG
+    assert f(4096, 4096, 2, 10, 4096, 4096, mla.FP8_E4M3, None) == mla.ERR_INVALID_ARG
+    assert f(None, 4096, 2, 10, 4096, 4096, mla.F32, None) == mla.ERR_INVALID_ARG
+    assert f(4096 + 4, 4096, 2, 10, 4096, 4096, mla.F32, None) == mla.ERR_INVALID_ARG
+    assert f(4096, 4096, 2, 0, None, None, mla.F32, None) == mla.OK          # nothing to do

@@ -1,0 +1,151 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases compare every element; they span several 64-row M-tiles, several
+pages and splits, ragged last pages (NaN-poisoned slack and unused pages),
+empty sequences, q_len 2 with the causal limit, and both output dtypes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests.gpu_common import compare, run_hip, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    import mla_latent_decode_absorbed_amd  # noqa: F401  (fails loudly when not built)
+    yield
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 3])
+def test_tiny_config_all_elements(num_splits):
+    """Tiny workload: batch 2, 16 heads, seq_lens 37 and 100, shuffled pages, NaN slack."""
+    say(f"tiny num_splits={num_splits}")
+    g, _ = workloads.make_config("c1", device=dev())
+    out, lse = run_hip(g, num_splits=num_splits)
+    o_ref, l_ref = run_oracle(g)
+    compare(out, lse, o_ref, l_ref, what=f"tiny splits={num_splits}")
+
+
+def test_tiny_config_dcp2_shards_merged():
+    """The same workload as two t mod 2 shards, each decoded, then merged on device."""
+    import mla_latent_decode_absorbed_amd as mla
+    say("tiny dcp=2 shards + merge")
+    g, shards = workloads.make_config("c1", device=dev())
+    outs, lses = [], []
+    for sh in shards:
+        o, l = run_hip(sh)
+        o_ref, l_ref = run_oracle(sh)
+        compare(o, l, o_ref, l_ref, what=f"shard {sh.meta['rank']}")
+        outs.append(o.reshape(-1, 512))
+        lses.append(l.reshape(-1))
+    rows = outs[0].shape[0]
+    stk_o = torch.stack(outs).contiguous()
+    stk_l = torch.stack(lses).contiguous()
+    mo = torch.empty((rows, 512), dtype=torch.float32, device=dev())
+    ml = torch.empty((rows,), dtype=torch.float32, device=dev())
+    mla.merge_states(stk_o, stk_l, len(shards), rows, mo, ml)
+    torch.cuda.synchronize()
+    o_ref, l_ref = run_oracle(g)
+    compare(mo, ml, o_ref.reshape(rows, 512), l_ref.reshape(rows), what="merged shards vs unsharded")
+
+
+@pytest.mark.parametrize("heads", [128, 20, 100])
+def test_page_boundary_lengths(heads):
+    """seq_lens 1, 63, 64, 65, 129 (and 0): one-token, full and ragged last pages."""
+    say(f"page boundaries heads={heads}")
+    inp = workloads.make_decode_inputs(6, 1, heads, [1, 63, 64, 65, 129, 0], "bf16", seed=21 + heads,
+                                       device=dev())
+    for ns in (0, 1, 2):
+        out, lse = run_hip(inp, num_splits=ns)
+        o_ref, l_ref = run_oracle(inp)
+        compare(out, lse, o_ref, l_ref, what=f"boundaries H={heads} splits={ns}")
+    assert torch.all(out[5] == 0) and torch.all(torch.isneginf(lse[5]))
+
+
+def test_ragged_batch_many_tiles_and_splits():
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1, 2500, size=7).tolist()
+    say(f"ragged lens={lens}")
+    inp = workloads.make_decode_inputs(7, 1, 128, lens, "bf16", seed=22, device=dev())
+    o_ref, l_ref = run_oracle(inp)
+    for ns in (0, 1, 5, 40):
+        out, lse = run_hip(inp, num_splits=ns)
+        compare(out, lse, o_ref, l_ref, what=f"ragged splits={ns}")
+
+
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_qlen2_causal(num_splits):
+    """Speculative q_len 2: query token t sees seq_len - (1 - t) tokens."""
+    say(f"q_len=2 causal splits={num_splits}")
+    inp = workloads.make_decode_inputs(3, 2, 128, [200, 130, 65], "bf16", seed=23, device=dev())
+    assert inp.causal
+    out, lse = run_hip(inp, num_splits=num_splits)
+    o_ref, l_ref = run_oracle(inp)
+    compare(out, lse, o_ref, l_ref, what=f"qlen2 causal splits={num_splits}")
+
+
+def test_qlen2_causal_single_token_sequence():
+    """seq_len 1 with q_len 2: token 0 sees nothing (o = 0, lse = -inf), token 1 sees one."""
+    say("q_len=2 causal seq_len=1")
+    inp = workloads.make_decode_inputs(1, 2, 32, [1], "bf16", seed=24, device=dev())
+    out, lse = run_hip(inp)
+    o_ref, l_ref = run_oracle(inp)
+    compare(out, lse, o_ref, l_ref, what="qlen2 seq1")
+    assert torch.isneginf(lse[0, 0]).all() and torch.all(out[0, 0] == 0)
+
+
+def test_bf16_output():
+    import mla_latent_decode_absorbed_amd as mla
+    say("bf16 output")
+    inp = workloads.make_decode_inputs(3, 1, 128, [300, 64, 1000], "bf16", seed=25, device=dev())
+    o_ref, l_ref = run_oracle(inp)
+    for ns in (1, 4):
+        out, lse = run_hip(inp, num_splits=ns, out_dtype=mla.BF16)
+        assert out.dtype == torch.bfloat16
+        compare(out, lse, o_ref, l_ref, what=f"bf16 out splits={ns}")
+
+
+def test_deterministic():
+    say("determinism")
+    inp = workloads.make_decode_inputs(4, 1, 128, [900, 1300, 40, 2048], "bf16", seed=26, device=dev())
+    a = run_hip(inp)
+    b = run_hip(inp)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("n", [1, 2, 5])
+def test_merge_kernel(n):
+    """mla_merge_states on random partials with -inf (empty) entries, incl. all-empty rows."""
+    import mla_latent_decode_absorbed_amd as mla
+    from oracle import merge_ref
+    say(f"merge n={n}")
+    rows = 300
+    g = torch.Generator().manual_seed(27 + n)
+    outs = torch.randn((n, rows, 512), generator=g)
+    lses = torch.randn((n, rows), generator=g) * 3
+    lses[:, 7] = float("-inf")                       # all-empty row
+    if n > 1:
+        lses[0, 11] = float("-inf")
+        outs[0, 11] = float("nan")                   # an empty partial's output is never read
+    o_ref, l_ref = merge_ref(outs.double().numpy(), lses.double().numpy())
+    for dt in (mla.F32, mla.BF16):
+        mo = torch.empty((rows, 512), dtype=torch.float32 if dt == mla.F32 else torch.bfloat16, device=dev())
+        ml = torch.empty((rows,), dtype=torch.float32, device=dev())
+        mla.merge_states(outs.to(dev()), lses.to(dev()), n, rows, mo, ml, out_dtype=dt)
+        torch.cuda.synchronize()
+        # fp32: rounding only; bf16: one rounding to nearest (half an ulp = 2^-9 relative)
+        tol = 1e-5 if dt == mla.F32 else 2.0 ** -8 * np.abs(o_ref) + 1e-6
+        o = mo.double().cpu().numpy()
+        l = ml.double().cpu().numpy()
+        assert np.array_equal(np.isneginf(l), np.isneginf(l_ref))
+        fin = ~np.isneginf(l_ref)
+        assert np.all(np.abs(o - o_ref) <= tol)
+        assert np.max(np.abs(l[fin] - l_ref[fin])) <= 1e-5

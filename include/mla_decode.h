@@ -115,7 +115,7 @@ int mla_decode_workspace_size(const mla_decode_desc* desc, size_t* bytes);
  *               ceil(seq_len / 64) are never read (may be -1).
  *   seq_lens    device int32 [B]: cache tokens per request in this shard,
  *               including the q_len new ones; 0 is allowed (empty shard).
- *   scale       softmax scale applied to q.k (e.g. 1/sqrt(192)).
+ *   scale       softmax scale applied to q.k (e.g. 1/sqrt(192)); finite and > 0.
  *   out         device, [B][q_len][H][512] of out_dtype, 16-byte aligned.
  *   lse         device float [B][q_len][H]: natural-log LSE of the scaled
  *               logits; -inf (and out = 0) for a row that sees no token.

@@ -68,7 +68,7 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
         return MLA_ERR_INVALID_ARG;
     if (d->kv_dtype == MLA_FP8_E4M3 ? (kv_scale == nullptr) : (kv_scale != nullptr))
         return MLA_ERR_INVALID_ARG;
-    if (!isfinite(scale)) return MLA_ERR_INVALID_ARG;
+    if (!isfinite(scale) || !(scale > 0.f)) return MLA_ERR_INVALID_ARG;
     const WorkspaceLayout L = layout_for(d);
     if (!workspace || !aligned(workspace, kAlign)) return MLA_ERR_WORKSPACE;
     if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;

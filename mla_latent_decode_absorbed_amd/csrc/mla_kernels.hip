@@ -146,87 +146,80 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
 // MFMA N dimension, so every K or V fragment read from LDS feeds 32 rows:
 //   S^T[32 tok][32 rows]  += K[32 tok][16 dims]  . Q^T[16 dims][32 rows]
 //   O^T[32 dims][32 rows] += V^T[32 dims][16 tok] . P^T[16 tok][32 rows]
-// Within a pair, wave h computes S for tokens 32h .. 32h+31 of the page and O
-// for dims 256h .. 256h+255; the two waves exchange their row maxima and their
-// bf16 P^T fragments through LDS.  Each lane owns one query row (lane % 32).
-// Q^T (144 VGPRs) and the wave's half of O^T (128 accumulators) stay in
-// registers for the whole page range; pages stream HBM -> LDS (direct loads)
-// into two buffers so the next page is in flight while this one is used.
+// The cache streams through LDS in half pages of 32 tokens (36,864 bytes)
+// held in a ring of 4 slots: three half pages are in flight while one is used.
+// Within a pair, wave h contracts dims 288h .. 288h+287 of every token of the
+// half page; the pair adds its two partial S^T tiles through LDS (IEEE
+// addition is commutative, so both waves hold bit-identical S), both run the
+// same online softmax, and wave h accumulates O^T for dims 256h .. 256h+255.
+// Each lane owns one query row (lane % 32).  The wave's Q^T half (72 VGPRs)
+// and O^T half (128 accumulators) stay in registers for the whole range.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
+constexpr int kHalfTok = 32;                          // tokens per ring slot
+constexpr int kSlotBytes = kHalfTok * kRowBytes;      // 36,864
+constexpr int kSlots = 4;
+constexpr int kDmaPerHalf = 9;                        // 1 KB direct loads per wave per half page
+constexpr float kRescaleSlack = 8.f;                  // lazy max: rescale when the max grows by > 2^8
+
 // One direct HBM -> LDS load of 16 bytes per lane: lane i writes LDS bytes
 // [lds_addr + 16 i, +16) with the 16 bytes at gbase + voff.  Issued as inline
 // assembly so that the compiler does not track it: the caller waits for it
-// explicitly (page_sync) before the data is read, and the compiler's own LDS
-// waits stay exact instead of draining every pending LDS read.
+// explicitly before the data is read, and the compiler's own LDS waits stay
+// exact instead of draining every pending LDS read.
 __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* gbase, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory");
 }
 
-// Issue the direct HBM -> LDS copy of one 73,728-byte page.  LDS chunk
-// q = 64 * blk + lane of instruction blk holds (token q / 72, position q % 72)
-// = global chunk (position ^ swz(token)) of that token.  Eight tokens are
-// 576 chunks = 9 instructions, so each lane needs the 9 offsets of one
-// 8-token group (cp_off, precomputed) plus a per-group stride of 9216 bytes.
-__device__ __forceinline__ void issue_page_copy(lds_u8* dst, const uint8_t* src, int wave,
+// Copy one half page (32 tokens) into a ring slot.  LDS chunk q = 64 j + lane
+// of instruction j of 8-token group g holds (token q / 72, position q % 72) =
+// global chunk (position ^ swz(token)) of that token; wave w copies group w.
+__device__ __forceinline__ void issue_half_copy(uint32_t slot_addr, const uint8_t* half_src, int wave,
                                                 const int (&cp_off)[9]) {
-    const uint32_t dst_addr = (uint32_t)(uintptr_t)dst;
+    const uint8_t* gsrc = half_src + wave * 8 * kRowBytes;
+    const uint32_t gdst = slot_addr + wave * 9 * 1024;
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-        const int grp = 2 * wave + gi;                       // 8-token group of this wave
-        const uint8_t* gsrc = src + grp * 8 * kRowBytes;
-        const uint32_t gdst = dst_addr + grp * 9 * 1024;
-#pragma unroll
-        for (int j = 0; j < 9; ++j) dma16(gdst + j * 1024, gsrc, (uint32_t)cp_off[j]);
-    }
+    for (int j = 0; j < 9; ++j) dma16(gdst + j * 1024, gsrc, (uint32_t)cp_off[j]);
 }
 
-__device__ __forceinline__ void zero_slack_rows(lds_u8* buf, int t0) {
-    // rows t0..63 of the page are past the sequence end and may hold anything
-    // (NaN): zero them so that a zero softmax weight times V stays zero
-    for (int idx = threadIdx.x; idx < (kPage - t0) * kRowChunks; idx += 256) {
-        const int t = t0 + idx / kRowChunks;
-        const int c = idx % kRowChunks;
-        *(__attribute__((address_space(3))) i32x4*)(buf + t * kRowBytes + c * 16) = (i32x4)0;
-    }
+// Wait until at most `ahead` half pages of this wave's copies are still in flight.
+__device__ __forceinline__ void wait_copies(int ahead) {
+    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
-// not for its outstanding global loads (the next page's copy stays in flight).
+// Workgroup barrier for LDS traffic only (outstanding copies stay in flight).
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Workgroup barrier after this wave's page copy (direct-to-LDS loads) has landed.
-__device__ __forceinline__ void page_sync() {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-constexpr int kXMaxBytes = 2 * 2 * 32 * 4;          // [pair][half][row] floats
-constexpr int kXPBytes = 2 * 2 * 2 * 64 * 16;       // [pair][half][kstep][lane] x 16 B
 
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void decode_bf16_kernel(DecodeParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t kv_a[kPageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t kv_b[kPageBytes];
-    __shared__ __attribute__((aligned(16))) float xmax[kXMaxBytes / 4];
-    __shared__ __attribute__((aligned(16))) uint8_t xp[kXPBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotBytes];
+    __shared__ __attribute__((aligned(16))) f32x4 xs[4 * 4 * 64];     // [wave][quarter][lane]
 
     const WorkItem w = p.work[blockIdx.x];
     if (w.b < 0) return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int pair = wave >> 1;     // which 32 rows of the tile
-    const int h = wave & 1;         // which token half (QK) and dim half (PV)
+    const int h = wave & 1;         // which half of the dims (QK contraction and PV output)
     const int G = lane >> 5;        // MFMA k-group of this lane (0/1)
     const int lr = lane & 31;       // query row of this lane within the pair's 32
     const int b = w.b;
     const int n = min(max(p.seq_lens[b], 0), p.max_pages * kPage);
     const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
     const uint8_t* kvbase = (const uint8_t*)p.kv;
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)(lds_u8*)ring;
 
-    // per-lane page-copy offsets within an 8-token group
+    // half pages of this unit that hold at least one token
+    const int half_begin = 2 * w.page_begin;
+    const int half_end = min(2 * w.page_end, (n + kHalfTok - 1) / kHalfTok);
+
+    // per-lane copy offsets within an 8-token group
     int cp_off[9];
 #pragma unroll
     for (int j = 0; j < 9; ++j) {
@@ -235,174 +228,269 @@ void decode_bf16_kernel(DecodeParams p) {
         const int pc = qc - t * kRowChunks;
         cp_off[j] = t * kRowBytes + ((pc ^ swz(t)) << 4);
     }
-
-    // start the first page while the query loads
-    if (w.page_begin < w.page_end)
-        issue_page_copy((lds_u8*)kv_a, kvbase + (size_t)__builtin_amdgcn_readfirstlane(bt[w.page_begin]) * kPageBytes, wave, cp_off);
+    // Page ids: lane i holds block-table entry page_begin + 64 g + i of the
+    // current group g (bt_cur) and of group g + 1 (bt_nxt, loaded a group
+    // ahead), so a copy never waits for a block-table load.
+    int bt_grp = 0;
+    auto bt_load = [&](int g) {
+        const int pg = w.page_begin + 64 * g + lane;
+        return pg < w.page_end ? bt[pg] : 0;
+    };
+    int bt_cur = bt_load(0);
+    int bt_nxt = bt_load(1);
+    auto half_src = [&](int k) {
+        const int rel = (k >> 1) - w.page_begin;
+        while ((rel >> 6) > bt_grp) {       // entering the next group of 64 pages
+            bt_cur = bt_nxt;
+            ++bt_grp;
+            bt_nxt = bt_load(bt_grp + 1);
+        }
+        const int pid = __builtin_amdgcn_readlane(bt_cur, rel & 63);
+        return kvbase + (size_t)pid * kPageBytes + (k & 1) * kSlotBytes;
+    };
+    // prologue: three half pages in flight before the query loads
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+        if (half_begin + j < half_end)
+            issue_half_copy(ring_addr + j * kSlotBytes, half_src(half_begin + j), wave, cp_off);
 
     // this lane's query row, its visible length, and its Q^T fragments:
-    // k-step ks covers dims 16 ks .. 16 ks + 15, lane holds dims 16 ks + 8 G .. + 7
+    // k-step ks covers dims 288 h + 16 ks .. + 15, lane holds dims + 8 G .. + 7
     const int row = w.mt * kMTile + pair * 32 + lr;
     const bool row_ok = row < p.rows;
     const int tq = row / p.heads;
     const int nvis = p.causal ? max(n - (p.q_len - 1 - tq), 0) : n;
-    bf16x8_t qf[36];
+    // smallest visible length over every row of the workgroup: half pages below
+    // it need no masking (row tiles span at most q_len query tokens)
+    const int nvis_min = p.causal ? max(n - (p.q_len - 1), 0) : n;
+    bf16x8_t qf[18];
     {
-        const __bf16* qr = (const __bf16*)p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * kQK + 8 * G;
+        const __bf16* qr = (const __bf16*)p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * kQK + 288 * h + 8 * G;
 #pragma unroll
-        for (int ks = 0; ks < 36; ++ks) {
+        for (int ks = 0; ks < 18; ++ks) {
             bf16x8_t v = *(const bf16x8_t*)(qr + 16 * ks);
             qf[ks] = row_ok ? v : (bf16x8_t)0;
         }
     }
 
-    // LDS read bases.  QK: token 32 h + lr, chunk (2 ks + G) ^ swz(lr), and
-    // 2 ks + G = 8 (ks / 4) + (2 (ks % 4) + G): four bases, the rest immediate.
-    int qk_base[4];
+    // LDS read offsets within a slot.  QK: token lr, chunk c(ks) = 36 h + 2 ks + G
+    // at position (c & ~7) | ((c ^ swz(lr)) & 7); c(ks + 4) = c(ks) + 8, so four
+    // bases cover all 18 k-steps with immediate offsets 128 (ks / 4).
+    int qk_off[4];
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4)
-        qk_base[k4] = (32 * h + lr) * kRowBytes + (((2 * k4 + G) ^ swz(lr)) << 4);
+    for (int k4 = 0; k4 < 4; ++k4) {
+        const int c = 36 * h + 2 * k4 + G;
+        qk_off[k4] = lr * kRowBytes + (((c & ~7) | ((c ^ swz(lr)) & 7)) << 4);
+    }
     // PV transpose reads.  The 16-lane block bk = lane / 16 covers dims
-    // 16 (bk % 2) .. + 15 of a 32-dim tile and tokens 16 kk + 4 G + e (first
+    // 16 (bk % 2) .. + 15 of a 32-dim tile and tokens 16 k2 + 4 G + e (first
     // read) and + 8 (second read), e = (lane % 16) / 4; the lane supplies dims
     // 4 (lane % 4) .. + 3 of its token.  Dim tile dt of half h starts at dim
-    // 256 h + 32 dt: chunk 32 h + 4 dt + 2 (bk % 2) + (lane % 4) / 2.
-    int tr_base[2];
+    // 256 h + 32 dt: chunk 32 h + 4 dt + 2 (bk % 2) + (lane % 4) / 2, and every
+    // token read has swizzle 2 e + G.
+    int tr_off[2];
     {
         const int li = lane & 15, e = li >> 2, cc = li & 3, dh = (lane >> 4) & 1;
         const int t = 4 * G + e;
-        const int sw = swz(t);          // = swz of t + 16 kk (+ 8) as well
+        const int sw = swz(t);
 #pragma unroll
         for (int d2 = 0; d2 < 2; ++d2)
-            tr_base[d2] = t * kRowBytes + h * 512 + (((4 * d2 + 2 * dh + (cc >> 1)) ^ sw) << 4) + (cc & 1) * 8;
+            tr_off[d2] = t * kRowBytes + h * 512 + (((4 * d2 + 2 * dh + (cc >> 1)) ^ sw) << 4) + (cc & 1) * 8;
     }
-    float* xmax_mine = xmax + (pair * 2 + h) * 32;
-    float* xmax_other = xmax + (pair * 2 + (h ^ 1)) * 32;
-    lds_u8* xp_mine = (lds_u8*)xp + (pair * 2 + h) * 2 * 1024 + lane * 16;
-    lds_u8* xp_other = (lds_u8*)xp + (pair * 2 + (h ^ 1)) * 2 * 1024 + lane * 16;
+    __attribute__((address_space(3))) f32x4* xs_mine = (__attribute__((address_space(3))) f32x4*)xs + wave * 256 + lane;
+    __attribute__((address_space(3))) f32x4* xs_other = (__attribute__((address_space(3))) f32x4*)xs + (wave ^ 1) * 256 + lane;
 
     f32x16 o[8];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = (f32x16)0.f;
+    for (int dt = 0; dt < 8; ++dt) {
+        o[dt] = (f32x16)0.f;
+        asm volatile("" : "+a"(o[dt]));
+    }
     float m = -INFINITY, l = 0.f;
 
-    auto consume = [&](lds_u8* cur, int page) {
-        const int tok0 = page * kPage + 32 * h;
+    auto slot_ptr = [&](int k) { return (lds_u8*)ring + ((k - half_begin) & 3) * kSlotBytes; };
 
-        // ---- S^T = K . Q^T over this wave's 32 tokens; K fragments are read two
-        //      k-steps ahead of their MFMA
-        f32x16 s = (f32x16)0.f;
-        bf16x8_t ka[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            ka[ks] = *(const __attribute__((address_space(3))) bf16x8_t*)(cur + qk_base[ks & 3] + (ks >> 2) * 128);
-#pragma unroll
-        for (int ks = 0; ks < 36; ++ks) {
-            const bf16x8_t a = ka[ks & 1];
-            if (ks + 2 < 36)
-                ka[ks & 1] = *(const __attribute__((address_space(3))) bf16x8_t*)(
-                    cur + qk_base[(ks + 2) & 3] + ((ks + 2) >> 2) * 128);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // two LDS reads ahead
-#pragma unroll
-        for (int ks = 0; ks < 34; ++ks) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-
-        // ---- online softmax (base 2).  Element i is token tok0 + 8 (i / 4) + 4 G + i % 4.
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int j = tok0 + 8 * (i >> 2) + 4 * G + (i & 3);
-            s[i] = j < nvis ? s[i] * p.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, s[i]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (G == 0) xmax_mine[lr] = mx;
+    // Wait until half page k's copy has landed in every wave (and every wave
+    // is past its previous use of the slot that the next refill targets).
+    auto top = [&](int k) {
+        wait_copies(min(2, half_end - 1 - k));
         lds_sync();
-        const float m_new = fmaxf(m, fmaxf(mx, xmax_other[lr]));
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-        float sum = 0.f;
+        const int tok0 = k * kHalfTok;
+        if (tok0 + kHalfTok > n) {
+            // rows past the sequence end may hold anything (NaN): zero them so
+            // that a zero softmax weight times V stays zero
+            lds_u8* cur = slot_ptr(k);
+            const int t0 = n - tok0;
+            for (int idx = threadIdx.x; idx < (kHalfTok - t0) * kRowChunks; idx += 256) {
+                const int t = t0 + idx / kRowChunks;
+                const int c = idx % kRowChunks;
+                *(__attribute__((address_space(3))) i32x4*)(cur + t * kRowBytes + c * 16) = (i32x4)0;
+            }
+            lds_sync();
+        }
+    };
+    // Partial S^T of half page k over this wave's 288 dims (two chains); K
+    // fragments are read four k-steps ahead of their MFMA.
+    auto qk = [&](int k, f32x16& sa, f32x16& sb) {
+        lds_u8* cur = slot_ptr(k);
+        sa = (f32x16)0.f;
+        sb = (f32x16)0.f;
+        auto kfrag = [&](int ks) -> bf16x8_t {
+            return *(const __attribute__((address_space(3))) bf16x8_t*)(cur + qk_off[ks & 3] + (ks >> 2) * 128);
+        };
+        bf16x8_t kf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kf[ks] = kfrag(ks);
+#pragma unroll
+        for (int ks = 0; ks < 18; ++ks) {
+            const bf16x8_t a = kf[ks & 3];
+            if (ks + 4 < 18) kf[ks & 3] = kfrag(ks + 4);
+            if (ks & 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sb, 0, 0, 0);
+            else        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sa, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int ks = 0; ks < 14; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+    // O^T += V^T . P^T over half page k (2 k-steps of 16 tokens x 8 dim tiles).
+    // The MFMAs are inline assembly, which the compiler does not move loads
+    // across, so the V^T fragments are software-pipelined here explicitly:
+    // four fragments (eight transpose reads) are in flight ahead of the MFMA.
+    auto pv = [&](int k, const bf16x8_t (&pf)[2]) {
+        lds_u8* cur = slot_ptr(k);
+        auto vfrag = [&](int i) -> bf16x8_t {      // i = 8 k2 + dt
+            const int k2 = i >> 3, dt = i & 7;
+            const int off = tr_off[dt & 1] + (dt >> 1) * 128 + k2 * 16 * kRowBytes;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off + 8 * kRowBytes));
+            return __builtin_bit_cast(bf16x8_t, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        };
+        bf16x8_t vf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vf[i] = vfrag(i);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            s[i] = s[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[i] - m_new);
-            sum += s[i];
+            // issued as inline assembly with O tied to its accumulation
+            // registers, so the compiler never renames (and copies) O.  The
+            // compiler does not see an MFMA here, so the wait states between a
+            // VALU write of an operand (the P^T fragment, any register move of
+            // the V^T fragment) and the MFMA read are inserted explicitly:
+            // s_nop 3 gives 4.
+            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+a"(o[i & 7]) : "v"(vf[i & 3]), "v"(pf[i >> 3]));
+            if (i + 4 < 16) vf[i & 3] = vfrag(i + 4);
         }
-        l = l * alpha + sum;
-        m = m_new;
-        // P^T fragments of this wave's tokens: k-step k2 (16 tokens) = elements 8 k2 .. + 7
-        bf16x8_t pf[2];
+    };
+    // MFMA results of the inline-assembly PV read by VALU code: the compiler
+    // does not see those MFMAs, so the wait states are inserted here
+    // (more than the 8-pass XDL write -> VALU / accvgpr read requirement).
+    auto pv_drain = [&]() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); };
+    // Pair sum of the partial tiles, masking of invisible tokens; returns the
+    // row max in log2 units (logits stay unscaled: scale is applied in the
+    // exponent, and scale > 0 commutes with the max).
+    auto finish_s = [&](int k, const f32x16& sa, const f32x16& sb, f32x16& s) -> float {
+        s = sa + sb;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            xs_mine[q4 * 64] = (f32x4){s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
+        lds_sync();
+        // every wave is past its reads of half page k - 1: refill its slot
+        if (k + 3 < half_end)
+            issue_half_copy(ring_addr + ((k + 3 - half_begin) & 3) * kSlotBytes, half_src(k + 3), wave, cp_off);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 v = xs_other[q4 * 64];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[4 * q4 + i] += v[i];
+        }
+        // element i is token 32 k + 8 (i / 4) + 4 G + i % 4
+        const int tok0 = k * kHalfTok;
+        if (tok0 + kHalfTok > nvis_min) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int j = tok0 + 8 * (i >> 2) + 4 * G + (i & 3);
+                s[i] = j < nvis ? s[i] : -INFINITY;
+            }
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        return mx * p.scale_log2;
+    };
+    // Weights of half page k against the reference max m (log2 units); adds
+    // the row sums.  exp2(c s - m) with c = scale * log2(e) is one FMA and one
+    // exp; masked logits are -inf and give 0.
+    auto weights = [&](f32x16& s, bf16x8_t (&pf)[2]) {
+        const float c = p.scale_log2;
+        const float mneg = m == -INFINITY ? 0.f : -m;
+        float sum0 = 0.f, sum1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, mneg));
+            if (i & 1) sum1 += s[i]; else sum0 += s[i];
+        }
+        l += sum0 + sum1;
+        // P^T fragments: k-step k2 (16 tokens) = accumulator elements 8 k2 .. + 7
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             pf[0][e] = (__bf16)s[e];
             pf[1][e] = (__bf16)s[8 + e];
         }
-        *(__attribute__((address_space(3))) bf16x8_t*)(xp_mine) = pf[0];
-        *(__attribute__((address_space(3))) bf16x8_t*)(xp_mine + 1024) = pf[1];
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-        }
-        lds_sync();
-        bf16x8_t pq[2];
-        pq[0] = *(const __attribute__((address_space(3))) bf16x8_t*)(xp_other);
-        pq[1] = *(const __attribute__((address_space(3))) bf16x8_t*)(xp_other + 1024);
-
-        // ---- O^T += V^T . P^T: 4 k-steps of 16 tokens (two per half) x 8 dim tiles
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8_t pk = ((kk >> 1) == h) ? pf[kk & 1] : pq[kk & 1];
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const int off = tr_base[dt & 1] + (dt >> 1) * 128 + kk * 16 * kRowBytes;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off + 8 * kRowBytes));
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, (i16x8){lo[0], lo[1], lo[2], lo[3],
-                                                                        hi[0], hi[1], hi[2], hi[3]});
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk, o[dt], 0, 0, 0);
-            }
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);       // four fragments ahead
-#pragma unroll
-        for (int i = 0; i < 28; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);   // two transpose reads
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
     };
 
-    for (int page = w.page_begin; page < w.page_end; page += 2) {
-        // page is in kv_a, page + 1 (if any) goes to kv_b
-        page_sync();                     // kv_a landed; kv_b and xp are free
-        if (page + 1 < w.page_end)
-            issue_page_copy((lds_u8*)kv_b, kvbase + (size_t)__builtin_amdgcn_readfirstlane(bt[page + 1]) * kPageBytes, wave, cp_off);
-        if (page * kPage + kPage > n) {
-            zero_slack_rows((lds_u8*)kv_a, n - page * kPage);
-            lds_sync();
-        }
-        consume((lds_u8*)kv_a, page);
-        if (page + 1 < w.page_end) {
-            page_sync();                 // kv_b landed; kv_a and xp are free
-            if (page + 2 < w.page_end)
-                issue_page_copy((lds_u8*)kv_a, kvbase + (size_t)__builtin_amdgcn_readfirstlane(bt[page + 2]) * kPageBytes, wave, cp_off);
-            if ((page + 1) * kPage + kPage > n) {
-                zero_slack_rows((lds_u8*)kv_b, n - (page + 1) * kPage);
-                lds_sync();
+    // Software pipeline: the QK^T of half page k + 1 is issued together with
+    // the PV of half page k.  The reference max m only moves when a row max
+    // exceeds it by more than 2^8 (weights stay <= 2^8); that rescale of O
+    // runs outside the inner loop, which never touches O with VALU work.
+    if (half_begin < half_end) {
+        int k = half_begin;
+        f32x16 s, sa, sb;
+        top(k);
+        qk(k, sa, sb);
+        float mx = finish_s(k, sa, sb, s);
+        bool grow = mx > m + kRescaleSlack;
+        for (;;) {
+            if (__any(grow)) {
+                pv_drain();
+                const float m_new = grow ? mx : m;
+                const float alpha = grow ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new)) : 1.f;
+                l *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+                m = m_new;
             }
-            consume((lds_u8*)kv_b, page + 1);
+            bool done = false;
+            for (;;) {
+                bf16x8_t pf[2];
+                const bool more = k + 1 < half_end;
+                if (more) {
+                    top(k + 1);
+                    qk(k + 1, sa, sb);        // MFMAs run while the weights of k are computed
+                }
+                weights(s, pf);
+                pv(k, pf);                    // PV MFMAs run through the pair exchange of k + 1
+                if (!more) {
+                    done = true;
+                    break;
+                }
+                ++k;
+                mx = finish_s(k, sa, sb, s);
+                grow = mx > m + kRescaleSlack;
+                if (__any(grow)) break;
+            }
+            if (done) break;
         }
     }
 
-    // ---- epilogue: o = O / l, lse = ln(sum exp).  l is split between the pair.
-    // (the cross-lane sum is taken with all 64 lanes active, outside the branch)
-    const float l_wave = l + __shfl_xor(l, 32);
-    lds_sync();
-    if (G == 0) xmax_mine[lr] = l_wave;
-    lds_sync();
-    const float lt = l_wave + xmax_other[lr];
+    pv_drain();
+    // ---- epilogue: o = O / l, lse = ln(sum exp).  Both waves of a pair hold
+    //      the full row sum; the lane pair (G = 0, 1) splits its tokens.
+    const float lt = l + __shfl_xor(l, 32);
     if (!row_ok) return;
     const bool empty = m == -INFINITY;
     const float inv = empty ? 0.f : 1.f / lt;

@@ -96,6 +96,8 @@ def test_null_and_misaligned_pointers_rejected():
     assert _call(d, out=4096 + 4) == mla.ERR_INVALID_ARG
     assert _call(d, bt=4096 + 2) == mla.ERR_INVALID_ARG
     assert _call(d, scale=float("nan")) == mla.ERR_INVALID_ARG
+    assert _call(d, scale=0.0) == mla.ERR_INVALID_ARG
+    assert _call(d, scale=-0.1) == mla.ERR_INVALID_ARG
     assert _call(d, kv_scale=4096) == mla.ERR_INVALID_ARG          # bf16 takes no kv_scale
 
 

@@ -140,29 +140,40 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
 // ---------------------------------------------------------------------------
 // split-KV decode, bf16 cache
 //
-// Workgroup = 4 waves (one per SIMD) = 2 pairs; a pair owns 32 query rows, so
-// kMTile = 64.  One work item (request, M-tile, page range) per workgroup.
-// Both contractions use v_mfma_f32_32x32x16_bf16 with the query rows as the
-// MFMA N dimension, so every K or V fragment read from LDS feeds 32 rows:
+// Workgroup = 4 waves (one per SIMD), kMTile = 128 query rows, one work item
+// (request, 128-row tile, page range) per workgroup, so every cache page is
+// ingested once per 128 rows.  Both contractions run on
+// v_mfma_f32_32x32x16_bf16 with the query rows as the MFMA N dimension:
 //   S^T[32 tok][32 rows]  += K[32 tok][16 dims]  . Q^T[16 dims][32 rows]
 //   O^T[32 dims][32 rows] += V^T[32 dims][16 tok] . P^T[16 tok][32 rows]
+// Wave w owns query rows 32 w .. 32 w + 31: it contracts all 576 dims of
+// every token against them (its Q^T stays in 144 VGPRs), runs their online
+// softmax and owns their max and row sum.  Waves 2j and 2j + 1 form a pair
+// for the PV product: each accumulates O^T for BOTH tiles of the pair (64
+// rows) over one half of the 512 output dims, so every V^T fragment read from
+// LDS feeds two MFMAs.  The pair trades its bf16 P^T tiles (and, when a row
+// max moves, the rescale factor) through LDS once per half page.
+//
 // The cache streams through LDS in half pages of 32 tokens (36,864 bytes)
-// held in a ring of 4 slots: three half pages are in flight while one is used.
-// Within a pair, wave h contracts dims 288h .. 288h+287 of every token of the
-// half page; the pair adds its two partial S^T tiles through LDS (IEEE
-// addition is commutative, so both waves hold bit-identical S), both run the
-// same online softmax, and wave h accumulates O^T for dims 256h .. 256h+255.
-// Each lane owns one query row (lane % 32).  The wave's Q^T half (72 VGPRs)
-// and O^T half (128 accumulators) stay in registers for the whole range.
+// held in a ring of 4 slots with direct HBM -> LDS loads; the copy of half
+// page k + 3 is issued while half page k + 1 is contracted.  One loop
+// iteration k (all in one basic block in the common case) contracts
+// QK^T of half page k + 1, then issues the PV of half page k interleaved with
+// the softmax of half page k + 1.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
+typedef __attribute__((address_space(3))) float lds_f32;
 
 constexpr int kHalfTok = 32;                          // tokens per ring slot
 constexpr int kSlotBytes = kHalfTok * kRowBytes;      // 36,864
 constexpr int kSlots = 4;
-constexpr int kDmaPerHalf = 9;                        // 1 KB direct loads per wave per half page
+constexpr int kRingBytes = kSlots * kSlotBytes;       // 147,456
+constexpr int kPBufOff = kRingBytes;                  // [wave][k2][lane] 16 B: P^T fragments
+constexpr int kABufOff = kPBufOff + 4 * 2 * 64 * 16;  // [wave][lane] float: rescale factor / row sum
+constexpr int kLdsBytes = kABufOff + 4 * 64 * 4;      // 156,672
 constexpr float kRescaleSlack = 8.f;                  // lazy max: rescale when the max grows by > 2^8
 
 // One direct HBM -> LDS load of 16 bytes per lane: lane i writes LDS bytes
@@ -175,17 +186,6 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* gbase, uint
                  :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory");
 }
 
-// Copy one half page (32 tokens) into a ring slot.  LDS chunk q = 64 j + lane
-// of instruction j of 8-token group g holds (token q / 72, position q % 72) =
-// global chunk (position ^ swz(token)) of that token; wave w copies group w.
-__device__ __forceinline__ void issue_half_copy(uint32_t slot_addr, const uint8_t* half_src, int wave,
-                                                const int (&cp_off)[9]) {
-    const uint8_t* gsrc = half_src + wave * 8 * kRowBytes;
-    const uint32_t gdst = slot_addr + wave * 9 * 1024;
-#pragma unroll
-    for (int j = 0; j < 9; ++j) dma16(gdst + j * 1024, gsrc, (uint32_t)cp_off[j]);
-}
-
 // Wait until at most `ahead` half pages of this wave's copies are still in flight.
 __device__ __forceinline__ void wait_copies(int ahead) {
     if (ahead >= 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
@@ -196,30 +196,46 @@ __device__ __forceinline__ void wait_copies(int ahead) {
 // Workgroup barrier for LDS traffic only (outstanding copies stay in flight).
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// max over the lane pair (l, l ^ 32) without LDS: the swap leaves both values of
+// the pair in (r[0], r[1]) on both lanes.
+__device__ __forceinline__ float pair_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void decode_bf16_kernel(DecodeParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[kSlots * kSlotBytes];
-    __shared__ __attribute__((aligned(16))) f32x4 xs[4 * 4 * 64];     // [wave][quarter][lane]
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
     const WorkItem w = p.work[blockIdx.x];
     if (w.b < 0) return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int pair = wave >> 1;     // which 32 rows of the tile
-    const int h = wave & 1;         // which half of the dims (QK contraction and PV output)
+    const int h = wave & 1;         // PV: which half of the 512 output dims
     const int G = lane >> 5;        // MFMA k-group of this lane (0/1)
-    const int lr = lane & 31;       // query row of this lane within the pair's 32
+    const int lr = lane & 31;       // query row of this lane within its 32-row tile
     const int b = w.b;
     const int n = min(max(p.seq_lens[b], 0), p.max_pages * kPage);
     const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
     const uint8_t* kvbase = (const uint8_t*)p.kv;
-    const uint32_t ring_addr = (uint32_t)(uintptr_t)(lds_u8*)ring;
+    lds_u8* const ring = (lds_u8*)lds;
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+    lds_u8* const pbuf_mine = (lds_u8*)lds + kPBufOff + wave * 2048 + lane * 16;
+    lds_u8* const pbuf_other = (lds_u8*)lds + kPBufOff + (wave ^ 1) * 2048 + lane * 16;
+    lds_f32* const abuf_mine = (lds_f32*)(lds + kABufOff) + wave * 64 + lane;
+    lds_f32* const abuf_other = (lds_f32*)(lds + kABufOff) + (wave ^ 1) * 64 + lane;
 
     // half pages of this unit that hold at least one token
     const int half_begin = 2 * w.page_begin;
     const int half_end = min(2 * w.page_end, (n + kHalfTok - 1) / kHalfTok);
 
-    // per-lane copy offsets within an 8-token group
+    // per-lane copy offsets within an 8-token group: LDS chunk q = 64 j + lane
+    // of copy j holds (token q / 72, position q % 72) = global chunk
+    // (position ^ swz(token)) of that token; wave w copies tokens 8w .. 8w + 7
     int cp_off[9];
 #pragma unroll
     for (int j = 0; j < 9; ++j) {
@@ -248,39 +264,49 @@ void decode_bf16_kernel(DecodeParams p) {
         const int pid = __builtin_amdgcn_readlane(bt_cur, rel & 63);
         return kvbase + (size_t)pid * kPageBytes + (k & 1) * kSlotBytes;
     };
+    auto slot_addr = [&](int k) { return ring_addr + ((k - half_begin) & 3) * kSlotBytes; };
+    auto slot_ptr = [&](int k) { return ring + ((k - half_begin) & 3) * kSlotBytes; };
+    auto issue_copy = [&](int k, int j, const uint8_t* src) {
+        dma16(slot_addr(k) + wave * 9 * 1024 + j * 1024, src + wave * 8 * kRowBytes, (uint32_t)cp_off[j]);
+    };
     // prologue: three half pages in flight before the query loads
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-        if (half_begin + j < half_end)
-            issue_half_copy(ring_addr + j * kSlotBytes, half_src(half_begin + j), wave, cp_off);
+    for (int j3 = 0; j3 < 3; ++j3)
+        if (half_begin + j3 < half_end) {
+            const uint8_t* src = half_src(half_begin + j3);
+#pragma unroll
+            for (int j = 0; j < 9; ++j) issue_copy(half_begin + j3, j, src);
+        }
 
     // this lane's query row, its visible length, and its Q^T fragments:
-    // k-step ks covers dims 288 h + 16 ks .. + 15, lane holds dims + 8 G .. + 7
-    const int row = w.mt * kMTile + pair * 32 + lr;
+    // k-step ks covers dims 16 ks .. + 15, lane holds dims 16 ks + 8 G .. + 7
+    const int row = w.mt * kMTile + wave * 32 + lr;
     const bool row_ok = row < p.rows;
     const int tq = row / p.heads;
-    const int nvis = p.causal ? max(n - (p.q_len - 1 - tq), 0) : n;
-    // smallest visible length over every row of the workgroup: half pages below
-    // it need no masking (row tiles span at most q_len query tokens)
-    const int nvis_min = p.causal ? max(n - (p.q_len - 1), 0) : n;
-    bf16x8_t qf[18];
+    // (capped at the end of this unit's token range, so that the dummy half
+    // page past the range is masked completely)
+    const int unit_end = half_end * kHalfTok;
+    const int nvis = min(p.causal ? max(n - (p.q_len - 1 - tq), 0) : n, unit_end);
+    // smallest visible length over every row of the workgroup: half pages
+    // entirely below it need no masking
+    const int nvis_min = min(p.causal ? max(n - (p.q_len - 1), 0) : n, unit_end);
+    // (a row past the end of the tile reads the last row instead; its
+    // results are never stored)
+    bf16x8_t qf[36];
     {
-        const __bf16* qr = (const __bf16*)p.q + ((size_t)b * p.rows + (row_ok ? row : 0)) * kQK + 288 * h + 8 * G;
+        const __bf16* qr = (const __bf16*)p.q + ((size_t)b * p.rows + min(row, p.rows - 1)) * kQK + 8 * G;
 #pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-            bf16x8_t v = *(const bf16x8_t*)(qr + 16 * ks);
-            qf[ks] = row_ok ? v : (bf16x8_t)0;
-        }
+        for (int ks = 0; ks < 36; ++ks) qf[ks] = *(const bf16x8_t*)(qr + 16 * ks);
     }
 
-    // LDS read offsets within a slot.  QK: token lr, chunk c(ks) = 36 h + 2 ks + G
-    // at position (c & ~7) | ((c ^ swz(lr)) & 7); c(ks + 4) = c(ks) + 8, so four
-    // bases cover all 18 k-steps with immediate offsets 128 (ks / 4).
+    // LDS read offsets within a slot.  QK: token lr, chunk c(ks) = 2 ks + G at
+    // position (c & ~7) | ((c ^ swz(lr)) & 7); c(ks + 4) = c(ks) + 8, so four
+    // bases cover all 36 k-steps with immediate offsets 128 (ks / 4).
     int qk_off[4];
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
-        const int c = 36 * h + 2 * k4 + G;
-        qk_off[k4] = lr * kRowBytes + (((c & ~7) | ((c ^ swz(lr)) & 7)) << 4);
+        const int c = 2 * k4 + G;
+        qk_off[k4] = lr * kRowBytes + (((c ^ swz(lr)) & 7) << 4);
     }
     // PV transpose reads.  The 16-lane block bk = lane / 16 covers dims
     // 16 (bk % 2) .. + 15 of a 32-dim tile and tokens 16 k2 + 4 G + e (first
@@ -297,135 +323,99 @@ void decode_bf16_kernel(DecodeParams p) {
         for (int d2 = 0; d2 < 2; ++d2)
             tr_off[d2] = t * kRowBytes + h * 512 + (((4 * d2 + 2 * dh + (cc >> 1)) ^ sw) << 4) + (cc & 1) * 8;
     }
-    __attribute__((address_space(3))) f32x4* xs_mine = (__attribute__((address_space(3))) f32x4*)xs + wave * 256 + lane;
-    __attribute__((address_space(3))) f32x4* xs_other = (__attribute__((address_space(3))) f32x4*)xs + (wave ^ 1) * 256 + lane;
 
-    f32x16 o[8];
+    // O^T accumulators: o0 = this wave's own 32 rows, o1 = the partner's 32
+    // rows, each over dims 256 h .. 256 h + 255 (8 tiles of 32 dims).
+    f32x16 o0[8], o1[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-        o[dt] = (f32x16)0.f;
-        asm volatile("" : "+a"(o[dt]));
+        o0[dt] = (f32x16)0.f;
+        o1[dt] = (f32x16)0.f;
+        asm volatile("" : "+a"(o0[dt]));
+        asm volatile("" : "+a"(o1[dt]));
     }
-    float m = -INFINITY, l = 0.f;
-
-    auto slot_ptr = [&](int k) { return (lds_u8*)ring + ((k - half_begin) & 3) * kSlotBytes; };
-
-    // Wait until half page k's copy has landed in every wave (and every wave
-    // is past its previous use of the slot that the next refill targets).
-    auto top = [&](int k) {
-        wait_copies(min(2, half_end - 1 - k));
-        lds_sync();
-        const int tok0 = k * kHalfTok;
-        if (tok0 + kHalfTok > n) {
-            // rows past the sequence end may hold anything (NaN): zero them so
-            // that a zero softmax weight times V stays zero
-            lds_u8* cur = slot_ptr(k);
-            const int t0 = n - tok0;
-            for (int idx = threadIdx.x; idx < (kHalfTok - t0) * kRowChunks; idx += 256) {
-                const int t = t0 + idx / kRowChunks;
-                const int c = idx % kRowChunks;
-                *(__attribute__((address_space(3))) i32x4*)(cur + t * kRowBytes + c * 16) = (i32x4)0;
-            }
-            lds_sync();
-        }
-    };
-    // Partial S^T of half page k over this wave's 288 dims (two chains); K
-    // fragments are read four k-steps ahead of their MFMA.
-    auto qk = [&](int k, f32x16& sa, f32x16& sb) {
-        lds_u8* cur = slot_ptr(k);
-        sa = (f32x16)0.f;
-        sb = (f32x16)0.f;
-        auto kfrag = [&](int ks) -> bf16x8_t {
-            return *(const __attribute__((address_space(3))) bf16x8_t*)(cur + qk_off[ks & 3] + (ks >> 2) * 128);
-        };
-        bf16x8_t kf[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kf[ks] = kfrag(ks);
-#pragma unroll
-        for (int ks = 0; ks < 18; ++ks) {
-            const bf16x8_t a = kf[ks & 3];
-            if (ks + 4 < 18) kf[ks & 3] = kfrag(ks + 4);
-            if (ks & 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sb, 0, 0, 0);
-            else        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sa, 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int ks = 0; ks < 14; ++ks) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    };
-    // O^T += V^T . P^T over half page k (2 k-steps of 16 tokens x 8 dim tiles).
-    // The MFMAs are inline assembly, which the compiler does not move loads
-    // across, so the V^T fragments are software-pipelined here explicitly:
-    // four fragments (eight transpose reads) are in flight ahead of the MFMA.
-    auto pv = [&](int k, const bf16x8_t (&pf)[2]) {
-        lds_u8* cur = slot_ptr(k);
-        auto vfrag = [&](int i) -> bf16x8_t {      // i = 8 k2 + dt
-            const int k2 = i >> 3, dt = i & 7;
-            const int off = tr_off[dt & 1] + (dt >> 1) * 128 + k2 * 16 * kRowBytes;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off + 8 * kRowBytes));
-            return __builtin_bit_cast(bf16x8_t, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        };
-        bf16x8_t vf[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vf[i] = vfrag(i);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            // issued as inline assembly with O tied to its accumulation
-            // registers, so the compiler never renames (and copies) O.  The
-            // compiler does not see an MFMA here, so the wait states between a
-            // VALU write of an operand (the P^T fragment, any register move of
-            // the V^T fragment) and the MFMA read are inserted explicitly:
-            // s_nop 3 gives 4.
-            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                         : "+a"(o[i & 7]) : "v"(vf[i & 3]), "v"(pf[i >> 3]));
-            if (i + 4 < 16) vf[i & 3] = vfrag(i + 4);
-        }
-    };
     // MFMA results of the inline-assembly PV read by VALU code: the compiler
-    // does not see those MFMAs, so the wait states are inserted here
-    // (more than the 8-pass XDL write -> VALU / accvgpr read requirement).
+    // does not see those MFMAs, so their wait states are inserted here (more
+    // than an XDL write -> VALU read of a 16-pass MFMA needs).
     auto pv_drain = [&]() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); };
-    // Pair sum of the partial tiles, masking of invisible tokens; returns the
-    // row max in log2 units (logits stay unscaled: scale is applied in the
-    // exponent, and scale > 0 commutes with the max).
-    auto finish_s = [&](int k, const f32x16& sa, const f32x16& sb, f32x16& s) -> float {
-        s = sa + sb;
+    // o *= a for one set of accumulators, one register at a time through a
+    // single VGPR (the accumulators never leave the AGPRs).
+    auto scale_acc = [&](f32x16 (&o)[8], float a) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            xs_mine[q4 * 64] = (f32x4){s[4 * q4], s[4 * q4 + 1], s[4 * q4 + 2], s[4 * q4 + 3]};
-        lds_sync();
-        // every wave is past its reads of half page k - 1: refill its slot
-        if (k + 3 < half_end)
-            issue_half_copy(ring_addr + ((k + 3 - half_begin) & 3) * kSlotBytes, half_src(k + 3), wave, cp_off);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 v = xs_other[q4 * 64];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[4 * q4 + i] += v[i];
-        }
-        // element i is token 32 k + 8 (i / 4) + 4 G + i % 4
-        const int tok0 = k * kHalfTok;
-        if (tok0 + kHalfTok > nvis_min) {
+        for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int j = tok0 + 8 * (i >> 2) + 4 * G + (i & 3);
-                s[i] = j < nvis ? s[i] : -INFINITY;
+                float e = o[dt][i];
+                float t;
+                asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                             : "+a"(e), "=&v"(t) : "v"(a));
+                o[dt][i] = e;
             }
+    };
+    float m = -INFINITY, l = 0.f;   // reference max (log2 units) and this lane's part of the row sum
+
+    auto kfrag = [&](lds_u8* cur, int ks) -> bf16x8_t {
+        return *(const lds_bf16x8*)(cur + qk_off[ks & 3] + (ks >> 2) * 128);
+    };
+    auto vfrag = [&](lds_u8* cur, int i) -> bf16x8_t {      // i = 8 k2 + dt
+        const int k2 = i >> 3, dt = i & 7;
+        const int off = tr_off[dt & 1] + (dt >> 1) * 128 + k2 * 16 * kRowBytes;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off + 8 * kRowBytes));
+        return __builtin_bit_cast(bf16x8_t, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
+
+    // S^T of half page k: all 36 k-steps in one accumulation chain, K
+    // fragments read four k-steps ahead; `between(q)` runs after MFMA 4 q + 3
+    // (the copies of a later half page are issued there).
+    // The MFMAs are inline assembly with S tied to VGPRs, so that the compiler
+    // keeps every AGPR for O.  It does not see these MFMAs, so the wait states
+    // before VALU code reads S are inserted at the end.  The first MFMA of the chain
+    // takes the constant 0 as its accumulator (no VALU write precedes it);
+    // the others accumulate back to back into the same registers.
+    auto qk = [&](int k, f32x16& s, auto&& between) {
+        lds_u8* cur = slot_ptr(k);
+        bf16x8_t kf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kf[ks] = kfrag(cur, ks);
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) {
+            const bf16x8_t a = kf[ks & 3];
+            if (ks + 4 < 36) kf[ks & 3] = kfrag(cur, ks + 4);
+            if (ks == 0)
+                asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                             : "=&v"(s) : "v"(a), "v"(qf[ks]));
+            else
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                             : "+v"(s) : "v"(a), "v"(qf[ks]));
+            if ((ks & 3) == 3) between(ks >> 2);
         }
+        // wait states before VALU code reads the last MFMA's result
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
+    };
+
+    // Online softmax of half page k for this lane's row: masks invisible
+    // tokens (element i is token 32 k + 8 (i / 4) + 4 G + i % 4), moves the
+    // reference max when the row max exceeds it by more than kRescaleSlack
+    // (log2 units), and returns
+    // the rescale factor of everything accumulated so far (1 when unchanged).
+    // Weights are exp2(c s - m) with c = scale * log2(e): one FMA and one exp.
+    auto mask_s = [&](int k, f32x16& s) {
+        const int lim = nvis - k * kHalfTok - 4 * G;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = (8 * (i >> 2) + (i & 3)) < lim ? s[i] : -INFINITY;
+    };
+    auto softmax = [&](int k, f32x16& s, bf16x8_t (&pf)[2], bool masked) -> float {
+        if (masked) mask_s(k, s);
         float mx = s[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        return mx * p.scale_log2;
-    };
-    // Weights of half page k against the reference max m (log2 units); adds
-    // the row sums.  exp2(c s - m) with c = scale * log2(e) is one FMA and one
-    // exp; masked logits are -inf and give 0.
-    auto weights = [&](f32x16& s, bf16x8_t (&pf)[2]) {
+        mx = pair_max(mx) * p.scale_log2;
+        const bool grow = mx > m + kRescaleSlack;
+        const float m_new = grow ? mx : m;
+        // (nothing has been accumulated while m is still -inf: no rescale)
+        const float alpha = grow && m != -INFINITY ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+        m = m_new;
         const float c = p.scale_log2;
         const float mneg = m == -INFINITY ? 0.f : -m;
         float sum0 = 0.f, sum1 = 0.f;
@@ -434,85 +424,207 @@ void decode_bf16_kernel(DecodeParams p) {
             s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, mneg));
             if (i & 1) sum1 += s[i]; else sum0 += s[i];
         }
-        l += sum0 + sum1;
-        // P^T fragments: k-step k2 (16 tokens) = accumulator elements 8 k2 .. + 7
+        l = l * alpha + (sum0 + sum1);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             pf[0][e] = (__bf16)s[e];
             pf[1][e] = (__bf16)s[8 + e];
         }
+        return alpha;
+    };
+    auto publish = [&](const bf16x8_t (&pf)[2], float alpha) {
+        *(lds_bf16x8*)pbuf_mine = pf[0];
+        *(lds_bf16x8*)(pbuf_mine + 1024) = pf[1];
+        *abuf_mine = alpha;
     };
 
-    // Software pipeline: the QK^T of half page k + 1 is issued together with
-    // the PV of half page k.  The reference max m only moves when a row max
-    // exceeds it by more than 2^8 (weights stay <= 2^8); that rescale of O
-    // runs outside the inner loop, which never touches O with VALU work.
-    if (half_begin < half_end) {
-        int k = half_begin;
-        f32x16 s, sa, sb;
-        top(k);
-        qk(k, sa, sb);
-        float mx = finish_s(k, sa, sb, s);
-        bool grow = mx > m + kRescaleSlack;
-        for (;;) {
-            if (__any(grow)) {
-                pv_drain();
-                const float m_new = grow ? mx : m;
-                const float alpha = grow ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new)) : 1.f;
-                l *= alpha;
+    // O^T += V^T . P^T over half page k for both tiles of the pair, with the
+    // softmax of half page k + 1 spread between its MFMAs so that the
+    // exp/max/convert work runs while the matrix cores are busy
+    // (sched_barrier(0) pins the order of the groups).  V^T fragments are read
+    // four ahead and each feeds two MFMAs.  The MFMAs are inline assembly with
+    // O tied to its accumulation registers, so the compiler never moves O out
+    // of the AGPRs; it does not see them, so s_nop 3 gives the wait states a
+    // VALU write of an operand needs before an MFMA reads it.
+    auto pv_softmax = [&](int k, const bf16x8_t (&pf_own)[2], const bf16x8_t (&pf_oth_)[2], f32x16& s,
+                          bf16x8_t (&pf)[2], float& alpha_out) {
+        lds_u8* cur = slot_ptr(k);
+        bf16x8_t vf[4];
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+        for (int i = 0; i < 4; ++i) vf[i] = vfrag(cur, i);
+        float mx, mneg, sum0 = 0.f, sum1 = 0.f;
+        const float c = p.scale_log2;
+        auto chunk = [&](int g) {
+            if (g == 0) {
+                mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+#pragma unroll
+                for (int i = 4; i < 16; ++i) mx = fmaxf(mx, s[i]);
+            } else if (g == 1) {
+                mx = pair_max(mx) * c;
+                const bool grow = mx > m + kRescaleSlack;
+                const float m_new = grow ? mx : m;
+                // (nothing has been accumulated while m is still -inf: no rescale)
+                alpha_out = grow && m != -INFINITY ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
                 m = m_new;
+                mneg = m == -INFINITY ? 0.f : -m;
+                l *= alpha_out;
+            } else if (g >= 2 && g < 10) {
+                const int i = 2 * (g - 2);
+                s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, mneg));
+                s[i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, mneg));
+                sum0 += s[i];
+                sum1 += s[i + 1];
+            } else if (g == 10) {
+                l += sum0 + sum1;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pf[0][e] = (__bf16)s[e];
+            } else if (g == 11) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pf[1][e] = (__bf16)s[8 + e];
+            } else if (g == 12) {
+                *(lds_bf16x8*)pbuf_mine = pf[0];
+                *(lds_bf16x8*)(pbuf_mine + 1024) = pf[1];
+                *abuf_mine = alpha_out;
             }
-            bool done = false;
+        };
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const bf16x8_t a = vf[i & 3];
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+a"(o0[i & 7]) : "v"(a), "v"(pf_own[i >> 3]));
+            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+a"(o1[i & 7]) : "v"(a), "v"(pf_oth_[i >> 3]));
+            if (i + 4 < 16) vf[i & 3] = vfrag(cur, i + 4);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < 13) chunk(i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Zero the rows of half page k past the sequence end (they may hold
+    // anything, NaN included), so that a zero weight times V stays zero.
+    auto zero_tail = [&](int k) {
+        const int t0 = n - k * kHalfTok;     // callers pass half pages holding >= 1 token
+        if (t0 >= kHalfTok) return;
+        lds_u8* cur = slot_ptr(k);
+        for (int idx = threadIdx.x; idx < (kHalfTok - t0) * kRowChunks; idx += 256) {
+            const int t = t0 + idx / kRowChunks;
+            const int c = idx % kRowChunks;
+            *(__attribute__((address_space(3))) i32x4*)(cur + t * kRowBytes + c * 16) = (i32x4)0;
+        }
+        lds_sync();
+    };
+    auto needs_mask = [&](int k) { return k * kHalfTok + kHalfTok > nvis_min; };
+
+    if (half_begin < half_end) {
+        bf16x8_t pf_cur[2], pf_nxt[2], pf_oth[2];
+        float a_cur, a_oth;
+        // ---- prologue: S, softmax and P of the first half page
+        {
+            const int k = half_begin;
+            wait_copies(min(2, half_end - 1 - k));
+            lds_sync();
+            zero_tail(k);
+            f32x16 s;
+            qk(k, s, [&](int) {});
+            a_cur = softmax(k, s, pf_cur, needs_mask(k));
+            publish(pf_cur, a_cur);
+        }
+        // Top of iteration k: the copies of half page k + 1 have landed, P(k)
+        // of both waves is visible, and every wave is past its reads of half
+        // page k - 1 (whose slot the next copy refills).
+        auto enter = [&](int k) {
+            wait_copies(k + 2 < half_end ? 1 : 0);
+            lds_sync();
+            if (k + 1 < half_end) zero_tail(k + 1);
+            pf_oth[0] = *(const lds_bf16x8*)pbuf_other;
+            pf_oth[1] = *(const lds_bf16x8*)(pbuf_other + 1024);
+            a_oth = *abuf_other;
+        };
+        int k = half_begin;
+        enter(k);
+        bool done = false;
+        while (!done) {
+            if (__any(a_cur != 1.f || a_oth != 1.f)) {
+                // a row max moved: rescale what both tiles have accumulated so far
+                pv_drain();
+                scale_acc(o0, a_cur);
+                scale_acc(o1, a_oth);
+                a_cur = a_oth = 1.f;
+            }
+            // Iteration k: QK^T of half page k + 1 (past the last half page a
+            // dummy, fully masked) while the copy of half page k + 3 is issued,
+            // then the PV of half page k interleaved with the softmax of k + 1.
             for (;;) {
-                bf16x8_t pf[2];
-                const bool more = k + 1 < half_end;
-                if (more) {
-                    top(k + 1);
-                    qk(k + 1, sa, sb);        // MFMAs run while the weights of k are computed
-                }
-                weights(s, pf);
-                pv(k, pf);                    // PV MFMAs run through the pair exchange of k + 1
-                if (!more) {
+                f32x16 s;
+                // copy of half page k + 3 into the slot of k - 1; past the end
+                // of the range that slot is dead and receives half page k again
+                // (a cache hit that keeps this block free of branches)
+                const int kc = k + 3 < half_end ? k + 3 : k;
+                const uint8_t* csrc_w = half_src(kc) + wave * 8 * kRowBytes;
+                const uint32_t cdst = slot_addr(k + 3) + wave * 9 * 1024;
+                qk(k + 1, s, [&](int j) { dma16(cdst + j * 1024, csrc_w, (uint32_t)cp_off[j]); });
+                lds_sync();   // the partner has read P(k): it may be overwritten
+                if (needs_mask(k + 1)) mask_s(k + 1, s);
+                float a_nxt;
+                pv_softmax(k, pf_cur, pf_oth, s, pf_nxt, a_nxt);
+                if (k + 1 >= half_end) {
                     done = true;
                     break;
                 }
                 ++k;
-                mx = finish_s(k, sa, sb, s);
-                grow = mx > m + kRescaleSlack;
-                if (__any(grow)) break;
+                pf_cur[0] = pf_nxt[0];
+                pf_cur[1] = pf_nxt[1];
+                a_cur = a_nxt;
+                enter(k);
+                if (__any(a_cur != 1.f || a_oth != 1.f)) break;
             }
-            if (done) break;
         }
     }
 
+    // ---- epilogue: o = O / l and lse = ln(sum exp) for both tiles of the pair.
+    // No copy may still be writing this workgroup's LDS when it exits.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     pv_drain();
-    // ---- epilogue: o = O / l, lse = ln(sum exp).  Both waves of a pair hold
-    //      the full row sum; the lane pair (G = 0, 1) splits its tokens.
-    const float lt = l + __shfl_xor(l, 32);
-    if (!row_ok) return;
-    const bool empty = m == -INFINITY;
-    const float inv = empty ? 0.f : 1.f / lt;
-    const float lse = empty ? -INFINITY : (m + __log2f(lt)) * kLn2;
-    const int rit = row - w.mt * kMTile;
+    const float l_own = pair_sum(l);
+    __syncthreads();                      // every wave is done reading the exchange buffers
+    *abuf_mine = l_own;
+    __syncthreads();
+    const float l_oth = *abuf_other;
+    const int tile_oth = wave ^ 1;
+    const int row_oth = w.mt * kMTile + tile_oth * 32 + lr;
+    const float inv_own = l_own > 0.f ? 1.f / l_own : 0.f;
+    const float inv_oth = l_oth > 0.f ? 1.f / l_oth : 0.f;
     // element i of dim tile dt is dim 256 h + 32 dt + 8 (i / 4) + 4 G + i % 4
     const int dim0 = 256 * h + 4 * G;
-    if (w.nsplit == 1) {
-        const size_t orow = (size_t)b * p.rows + row;
-        if (p.out_bf16) {
-            __bf16* dst = (__bf16*)p.out + orow * kV + dim0;
+    auto store_tile = [&](const f32x16 (&o)[8], int r, float inv) {
+        if (r >= p.rows) return;
+        const int rit = r - w.mt * kMTile;
+        if (w.nsplit == 1) {
+            const size_t orow = (size_t)b * p.rows + r;
+            if (p.out_bf16) {
+                __bf16* dst = (__bf16*)p.out + orow * kV + dim0;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
+                for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    __bf16 __attribute__((ext_vector_type(4))) v;
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        __bf16 __attribute__((ext_vector_type(4))) v;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[dt][4 * q4 + i] * inv);
-                    *(__bf16 __attribute__((ext_vector_type(4)))*)(dst + 32 * dt + 8 * q4) = v;
-                }
+                        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[dt][4 * q4 + i] * inv);
+                        *(__bf16 __attribute__((ext_vector_type(4)))*)(dst + 32 * dt + 8 * q4) = v;
+                    }
+            } else {
+                float* dst = (float*)p.out + orow * kV + dim0;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        *(f32x4*)(dst + 32 * dt + 8 * q4) =
+                            (f32x4){o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]} * inv;
+            }
         } else {
-            float* dst = (float*)p.out + orow * kV + dim0;
+            float* dst = p.ws_o + ((size_t)blockIdx.x * kMTile + rit) * kV + dim0;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -520,16 +632,13 @@ void decode_bf16_kernel(DecodeParams p) {
                     *(f32x4*)(dst + 32 * dt + 8 * q4) =
                         (f32x4){o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]} * inv;
         }
-        if (G == 0 && h == 0) p.lse[orow] = lse;
-    } else {
-        float* dst = p.ws_o + ((size_t)blockIdx.x * kMTile + rit) * kV + dim0;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                *(f32x4*)(dst + 32 * dt + 8 * q4) =
-                    (f32x4){o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]} * inv;
-        if (G == 0 && h == 0) p.ws_lse[(size_t)blockIdx.x * kMTile + rit] = lse;
+    };
+    store_tile(o0, row, inv_own);
+    store_tile(o1, row_oth, inv_oth);
+    if (row_ok && G == 0) {
+        const float lse = l_own > 0.f ? (m + __log2f(l_own)) * kLn2 : -INFINITY;
+        if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
+        else p.ws_lse[(size_t)blockIdx.x * kMTile + (row - w.mt * kMTile)] = lse;
     }
 }
 

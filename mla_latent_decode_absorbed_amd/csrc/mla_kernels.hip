@@ -533,7 +533,8 @@ void decode_bf16_kernel(DecodeParams p) {
         }
         // Top of iteration k: the copies of half page k + 1 have landed, P(k)
         // of both waves is visible, and every wave is past its reads of half
-        // page k - 1 (whose slot the next copy refills).
+        // page k - 1 (whose slot the next copy refills).  The partner's P(k)
+        // and rescale factor are read here and first used after the QK^T.
         auto enter = [&](int k) {
             wait_copies(k + 2 < half_end ? 1 : 0);
             lds_sync();
@@ -544,42 +545,34 @@ void decode_bf16_kernel(DecodeParams p) {
         };
         int k = half_begin;
         enter(k);
-        bool done = false;
-        while (!done) {
-            if (__any(a_cur != 1.f || a_oth != 1.f)) {
+        // Iteration k: QK^T of half page k + 1 (past the last half page a
+        // dummy, fully masked) while the copy of half page k + 3 is issued,
+        // then the PV of half page k interleaved with the softmax of k + 1.
+        for (;;) {
+            f32x16 s;
+            // copy of half page k + 3 into the slot of k - 1; past the end of
+            // the range that slot is dead and receives half page k again (a
+            // cache hit that keeps this block free of branches)
+            const int kc = k + 3 < half_end ? k + 3 : k;
+            const uint8_t* csrc_w = half_src(kc) + wave * 8 * kRowBytes;
+            const uint32_t cdst = slot_addr(k + 3) + wave * 9 * 1024;
+            qk(k + 1, s, [&](int j) { dma16(cdst + j * 1024, csrc_w, (uint32_t)cp_off[j]); });
+            lds_sync();   // the partner has read P(k): it may be overwritten
+            if (__builtin_expect(__any(a_cur != 1.f || a_oth != 1.f), 0)) {
                 // a row max moved: rescale what both tiles have accumulated so far
                 pv_drain();
                 scale_acc(o0, a_cur);
                 scale_acc(o1, a_oth);
-                a_cur = a_oth = 1.f;
             }
-            // Iteration k: QK^T of half page k + 1 (past the last half page a
-            // dummy, fully masked) while the copy of half page k + 3 is issued,
-            // then the PV of half page k interleaved with the softmax of k + 1.
-            for (;;) {
-                f32x16 s;
-                // copy of half page k + 3 into the slot of k - 1; past the end
-                // of the range that slot is dead and receives half page k again
-                // (a cache hit that keeps this block free of branches)
-                const int kc = k + 3 < half_end ? k + 3 : k;
-                const uint8_t* csrc_w = half_src(kc) + wave * 8 * kRowBytes;
-                const uint32_t cdst = slot_addr(k + 3) + wave * 9 * 1024;
-                qk(k + 1, s, [&](int j) { dma16(cdst + j * 1024, csrc_w, (uint32_t)cp_off[j]); });
-                lds_sync();   // the partner has read P(k): it may be overwritten
-                if (needs_mask(k + 1)) mask_s(k + 1, s);
-                float a_nxt;
-                pv_softmax(k, pf_cur, pf_oth, s, pf_nxt, a_nxt);
-                if (k + 1 >= half_end) {
-                    done = true;
-                    break;
-                }
-                ++k;
-                pf_cur[0] = pf_nxt[0];
-                pf_cur[1] = pf_nxt[1];
-                a_cur = a_nxt;
-                enter(k);
-                if (__any(a_cur != 1.f || a_oth != 1.f)) break;
-            }
+            if (needs_mask(k + 1)) mask_s(k + 1, s);
+            float a_nxt;
+            pv_softmax(k, pf_cur, pf_oth, s, pf_nxt, a_nxt);
+            if (k + 1 >= half_end) break;
+            ++k;
+            pf_cur[0] = pf_nxt[0];
+            pf_cur[1] = pf_nxt[1];
+            a_cur = a_nxt;
+            enter(k);
         }
     }
 

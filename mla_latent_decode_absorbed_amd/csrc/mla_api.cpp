@@ -29,7 +29,6 @@ int check_desc(const mla_decode_desc* d) {
     if (d->out_dtype != MLA_F32 && d->out_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
     if (d->page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
     if (d->q_len > 16) return MLA_ERR_UNSUPPORTED;
-    if (d->kv_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
     const int64_t rows = (int64_t)d->q_len * d->num_heads;
     if (rows > (1 << 20)) return MLA_ERR_UNSUPPORTED;
     if ((int64_t)d->max_pages_per_seq * MLA_PAGE_SIZE > INT32_MAX / 2) return MLA_ERR_UNSUPPORTED;
@@ -109,8 +108,10 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     dp.causal = d->q_len > 1 ? d->causal : 0;
     dp.max_pages = d->max_pages_per_seq;
     dp.out_bf16 = d->out_dtype == MLA_BF16;
-    if (mla::launch_decode_bf16(dp, (int)L.units_max, s, (hipEvent_t)ev0, (hipEvent_t)ev1) != hipSuccess)
-        return MLA_ERR_HIP;
+    const hipError_t de = d->kv_dtype == MLA_FP8_E4M3
+                              ? mla::launch_decode_fp8(dp, (int)L.units_max, s, (hipEvent_t)ev0, (hipEvent_t)ev1)
+                              : mla::launch_decode_bf16(dp, (int)L.units_max, s, (hipEvent_t)ev0, (hipEvent_t)ev1);
+    if (de != hipSuccess) return MLA_ERR_HIP;
 
     mla::CombineParams cp;
     cp.req_info = req_info;

@@ -27,7 +27,7 @@ struct PlanParams {
 struct DecodeParams {
     const void* q;              // [B][M][576]
     const void* kv;             // [P][64][576]
-    const float* kv_scale;      // fp8 only
+    const float* kv_scale;      // fp8 only: device float, the per-tensor cache scale
     const int32_t* block_table; // [B][max_pages]
     const int32_t* seq_lens;    // [B]
     const WorkItem* work;       // [units_max]
@@ -87,6 +87,8 @@ hipError_t launch_plan(const PlanParams& p, const int32_t* seq_lens, int32_t* re
                        WorkItem* work, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, int units, hipStream_t stream,
                               hipEvent_t ev_before, hipEvent_t ev_after);
+hipError_t launch_decode_fp8(const DecodeParams& p, int units, hipStream_t stream,
+                             hipEvent_t ev_before, hipEvent_t ev_after);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 

@@ -15,6 +15,7 @@
 // Kernels:
 //   plan_kernel     - reads seq_lens on the device, chooses splits, writes the work list
 //   decode_bf16     - one workgroup per work item: streams pages HBM -> LDS, QK^T, softmax, PV
+//   decode_fp8      - the same for an OCP fp8 e4m3 cache and query (fp8 MFMA for both products)
 //   combine_kernel  - LSE-merges the split partials of each row into the shard result
 //   merge_kernel    - LSE-merges n stacked partial results (DCP shards)
 
@@ -636,6 +637,475 @@ void decode_bf16_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// split-KV decode, OCP fp8 e4m3 cache and query
+//
+// Same schedule as the bf16 kernel (128 query rows per workgroup, wave w owns
+// rows 32 w .. 32 w + 31 for QK^T and the softmax, wave pairs share their
+// P^T tiles so that every V^T fragment feeds two MFMAs, a 4-slot LDS ring
+// filled by direct HBM -> LDS loads), with these differences:
+//  - one ring slot holds a whole 64-token page (64 x 576 bytes = 36,864);
+//  - both contractions run on v_mfma_f32_32x32x64_f8f6f4 (fp8 x fp8 ->
+//    fp32, K = 64 per instruction):
+//      S^T[32 tok][32 rows]  += K[32 tok][64 dims] . Q^T[64 dims][32 rows]
+//      O^T[32 dims][32 rows] += V^T[32 dims][64 tok] . P^T[64 tok][32 rows]
+//    so a page is 2 token tiles x 9 k-steps of QK^T and one PV MFMA per
+//    32-dim tile and row tile;
+//  - the weights enter the PV product as two e4m3 terms, hi = e4m3(w) and
+//    lo = e4m3(w - hi), one MFMA each, so that their error is about 2^-8 of
+//    w instead of the 2^-4 of a single e4m3 rounding (which alone exceeds a
+//    few 1e-2 on short, peaked rows).  Weights are offset by 2^4 so that they
+//    span (0, 2^8]; the reference max takes integer values (log2 units) and
+//    moves once the row max exceeds it by 2^4, so every rescale factor is an
+//    exact power of two 2^-d.  The pair exchanges hi and lo through LDS; d
+//    (8 bits) rides in the sign bits of hi bytes 0-7, which are free because
+//    the weights are non-negative;
+//  - the per-tensor cache scale multiplies the logits (folded into the exp2
+//    factor) and the output (in the epilogue); the query scale arrives folded
+//    into `scale`.
+// Operand layouts of the 32x32x64 fp8 MFMA: lane L supplies row (A) or
+// column (B) L % 32 and 32 consecutive k values 32 (L / 32) .. + 31 of it,
+// one byte each; the result layout is the one of every 32x32 f32 MFMA.
+//
+// LDS row layout: token t of the page occupies 576 bytes = 36 chunks of 16;
+// chunk c sits at position c ^ swz8(t), swz8(t) = (t / 4) % 4 (a permutation
+// inside aligned groups of 4 chunks), which puts 16 consecutive tokens, and
+// the 8 tokens of a V^T transpose read, on distinct banks.
+// ---------------------------------------------------------------------------
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+constexpr int kRowBytes8 = kQK;                    // 576 bytes per fp8 cache row
+constexpr int kPageBytes8 = kPage * kRowBytes8;    // 36,864 = one ring slot
+constexpr int kRowChunks8 = kRowBytes8 / 16;       // 36
+constexpr float kRescaleSlack8 = 4.f;              // reference max moves when the max grows by > 2^4
+constexpr float kWeightOffset8 = 4.f;              // weights are exp2(s c - m + 4) <= 2^8 < 448
+constexpr int kPLoOff8 = kRingBytes + 4 * 2048;    // [wave][half][lane] 16 B: lo P^T terms (hi at kPBufOff)
+constexpr int kLdsBytes8 = kPLoOff8 + 4 * 2048;    // 163,840 (the whole LDS)
+static_assert(kPageBytes8 == kSlotBytes, "an fp8 page fills exactly one ring slot");
+static_assert(kLdsBytes8 <= 163840, "LDS budget");
+
+// d (0..255) into the sign bits of the bytes of two dwords (bits 8 i + 7),
+// and back: each is a multiply that spreads / gathers one nibble without carries.
+__device__ __forceinline__ int spread_nibble(int x) { return (int)(((uint32_t)(x & 15) * 0x10204080u) & 0x80808080u); }
+__device__ __forceinline__ int gather_nibble(int w) {
+    return (int)(((((uint32_t)w >> 7) & 0x01010101u) * 0x01020408u) >> 24) & 15;
+}
+
+__device__ __forceinline__ int swz8(int t) { return (t >> 2) & 3; }
+
+__device__ __forceinline__ i32x8 cat8(i32x4 a, i32x4 b) {
+    return (i32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Four e4m3 codes (round to nearest even, saturating) of v[0..3] in one dword.
+__device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void decode_fp8_kernel(DecodeParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes8];
+
+    const WorkItem w = p.work[blockIdx.x];
+    if (w.b < 0) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = wave & 1;         // PV: which half of the 512 output dims
+    const int G = lane >> 5;        // MFMA k-half of this lane (0/1)
+    const int lr = lane & 31;       // query row (QK B operand) / token (QK A operand) of this lane
+    const int b = w.b;
+    const int n = min(max(p.seq_lens[b], 0), p.max_pages * kPage);
+    const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
+    const uint8_t* kvbase = (const uint8_t*)p.kv;
+    lds_u8* const ring = (lds_u8*)lds;
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+    lds_u8* const pbuf_mine = (lds_u8*)lds + kPBufOff + wave * 2048 + lane * 16;
+    lds_u8* const pbuf_other = (lds_u8*)lds + kPBufOff + (wave ^ 1) * 2048 + lane * 16;
+    lds_u8* const plo_mine = (lds_u8*)lds + kPLoOff8 + wave * 2048 + lane * 16;
+    lds_u8* const plo_other = (lds_u8*)lds + kPLoOff8 + (wave ^ 1) * 2048 + lane * 16;
+    // after the loop the hi buffer carries the row sums
+    lds_f32* const lsum_mine = (lds_f32*)(lds + kPBufOff) + wave * 64 + lane;
+    lds_f32* const lsum_other = (lds_f32*)(lds + kPBufOff) + (wave ^ 1) * 64 + lane;
+    const float kv_scale = *p.kv_scale;
+    const float c_exp = p.scale_log2 * kv_scale;   // logits in log2 units per unit of q.k
+
+    // pages of this unit that hold at least one token
+    const int pg_begin = w.page_begin;
+    const int pg_end = min(w.page_end, (n + kPage - 1) / kPage);
+
+    // copy offsets: wave w copies tokens 16 w .. 16 w + 15 of a page; LDS chunk
+    // q = 64 j + lane of copy j holds (token q / 36, position q % 36) = global
+    // chunk (position ^ swz8(token)) of that token
+    int cp_off[9];
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+        const int qc = j * 64 + lane;
+        const int t = qc / kRowChunks8;
+        const int pc = qc - t * kRowChunks8;
+        cp_off[j] = t * kRowBytes8 + ((pc ^ swz8(t)) << 4);
+    }
+    int bt_grp = 0;
+    auto bt_load = [&](int g) {
+        const int pg = w.page_begin + 64 * g + lane;
+        return pg < w.page_end ? bt[pg] : 0;
+    };
+    int bt_cur = bt_load(0);
+    int bt_nxt = bt_load(1);
+    auto page_src = [&](int k) {
+        const int rel = k - w.page_begin;
+        while ((rel >> 6) > bt_grp) {
+            bt_cur = bt_nxt;
+            ++bt_grp;
+            bt_nxt = bt_load(bt_grp + 1);
+        }
+        const int pid = __builtin_amdgcn_readlane(bt_cur, rel & 63);
+        return kvbase + (size_t)pid * kPageBytes8;
+    };
+    auto slot_addr = [&](int k) { return ring_addr + ((k - pg_begin) & 3) * kSlotBytes; };
+    auto slot_ptr = [&](int k) { return ring + ((k - pg_begin) & 3) * kSlotBytes; };
+#pragma unroll
+    for (int j3 = 0; j3 < 3; ++j3)
+        if (pg_begin + j3 < pg_end) {
+            const uint8_t* src = page_src(pg_begin + j3) + wave * 16 * kRowBytes8;
+            const uint32_t dst = slot_addr(pg_begin + j3) + wave * 9 * 1024;
+#pragma unroll
+            for (int j = 0; j < 9; ++j) dma16(dst + j * 1024, src, (uint32_t)cp_off[j]);
+        }
+
+    const int row = w.mt * kMTile + wave * 32 + lr;
+    const bool row_ok = row < p.rows;
+    const int tq = row / p.heads;
+    const int unit_end = pg_end * kPage;
+    const int nvis = min(p.causal ? max(n - (p.q_len - 1 - tq), 0) : n, unit_end);
+    const int nvis_min = min(p.causal ? max(n - (p.q_len - 1), 0) : n, unit_end);
+    // Q^T fragments: k-step ks covers dims 64 ks .. + 63; lane holds dims 64 ks + 32 G .. + 31
+    i32x8 qf[9];
+    {
+        const uint8_t* qr = (const uint8_t*)p.q + ((size_t)b * p.rows + min(row, p.rows - 1)) * kQK + 32 * G;
+#pragma unroll
+        for (int ks = 0; ks < 9; ++ks) {
+            const i32x4 lo = *(const i32x4*)(qr + 64 * ks);
+            const i32x4 hi = *(const i32x4*)(qr + 64 * ks + 16);
+            qf[ks] = cat8(lo, hi);
+        }
+    }
+    // QK A fragments: token 32 tau + lr, chunks 4 ks + 2 G + e (e = 0, 1) at
+    // positions 4 ks + ((2 G + e) ^ swz8(lr)): two bases, immediates 64 ks and
+    // 32 rows (18,432 bytes) per token tile
+    int qk_off[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) qk_off[e] = lr * kRowBytes8 + (((2 * G + e) ^ swz8(lr)) << 4);
+    // PV A fragments (V^T, 32 dims x 64 tokens) by transpose reads: in each
+    // 16-lane group gl = lane / 16, source lane s = lane % 16 reads 8 bytes =
+    // dims D0 + 8 (s % 2) .. + 7 of token 16 r + 4 (gl / 2) + 8 (s / 8) + (s / 2) % 4
+    // (read r = 0..3), D0 = 256 h + 32 dt + 16 (gl % 2); the group then holds
+    // dims D0 .. D0 + 15 (one per lane) over those 8 tokens.  The token of byte
+    // j of k-half kh is then 32 (j / 16) + 8 ((j / 4) % 4) + 4 kh + j % 4, the
+    // same token the S^T accumulator element (j % 16) of token tile j / 16
+    // holds in lane (row, kh): the P^T operand is the accumulators in order.
+    int tr_off[2];
+    {
+        const int gl = lane >> 4, s = lane & 15, kh = gl >> 1;
+        const int t0 = 4 * kh + 8 * (s >> 3) + ((s >> 1) & 3);
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) {
+            const int c = 16 * h + 2 * d2 + (gl & 1);
+            tr_off[d2] = t0 * kRowBytes8 + ((c ^ swz8(t0)) << 4) + 8 * (s & 1);
+        }
+    }
+
+    f32x16 o0[8], o1[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        o0[dt] = (f32x16)0.f;
+        o1[dt] = (f32x16)0.f;
+        asm volatile("" : "+a"(o0[dt]));
+        asm volatile("" : "+a"(o1[dt]));
+    }
+    float m = -INFINITY, l = 0.f;
+
+    auto kfrag = [&](lds_u8* cur, int tau, int ks) -> i32x8 {
+        const i32x4 lo = *(const lds_i32x4*)(cur + qk_off[0] + tau * 32 * kRowBytes8 + 64 * ks);
+        const i32x4 hi = *(const lds_i32x4*)(cur + qk_off[1] + tau * 32 * kRowBytes8 + 64 * ks);
+        return cat8(lo, hi);
+    };
+    auto vfrag = [&](lds_u8* cur, int dt) -> i32x8 {
+        const int off = tr_off[dt & 1] + (dt >> 1) * 64;
+        const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + off));
+        const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + off + 16 * kRowBytes8));
+        const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + off + 32 * kRowBytes8));
+        const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + off + 48 * kRowBytes8));
+        return (i32x8){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+    };
+    auto pv_drain = [&]() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); };
+    auto scale_acc = [&](f32x16 (&o)[8], float a) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float e = o[dt][i];
+                float t;
+                asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                             : "+a"(e), "=&v"(t) : "v"(a));
+                o[dt][i] = e;
+            }
+    };
+
+    // S^T of page k: two token tiles, 9 k-steps each, as two interleaved
+    // accumulation chains (inline assembly, S in VGPRs; the wait states before
+    // VALU code reads S are inserted at the end); K fragments are read two
+    // k-steps ahead; `between(q)` runs after MFMA pair q (copies go there).
+    auto qk = [&](int k, f32x16& s0, f32x16& s1, auto&& between) {
+        lds_u8* cur = slot_ptr(k);
+        i32x8 kf0[2], kf1[2];
+        kf0[0] = kfrag(cur, 0, 0);
+        kf1[0] = kfrag(cur, 1, 0);
+        kf0[1] = kfrag(cur, 0, 1);
+        kf1[1] = kfrag(cur, 1, 1);
+#pragma unroll
+        for (int ks = 0; ks < 9; ++ks) {
+            const i32x8 a0 = kf0[ks & 1], a1 = kf1[ks & 1];
+            if (ks + 2 < 9) {
+                kf0[ks & 1] = kfrag(cur, 0, ks + 2);
+                kf1[ks & 1] = kfrag(cur, 1, ks + 2);
+            }
+            if (ks == 0) {
+                asm volatile("s_nop 3\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0"
+                             : "=&v"(s0) : "v"(a0), "v"(qf[ks]));
+                asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0"
+                             : "=&v"(s1) : "v"(a1), "v"(qf[ks]));
+            } else {
+                asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+                             : "+v"(s0) : "v"(a0), "v"(qf[ks]));
+                asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+                             : "+v"(s1) : "v"(a1), "v"(qf[ks]));
+            }
+            between(ks);
+        }
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+    };
+
+    // element i of token tile tau is token 64 k + 32 tau + 8 (i / 4) + 4 G + i % 4
+    auto mask_s = [&](int k, f32x16& s0, f32x16& s1) {
+        const int lim = nvis - k * kPage - 4 * G;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = 8 * (i >> 2) + (i & 3);
+            s0[i] = t < lim ? s0[i] : -INFINITY;
+            s1[i] = t + 32 < lim ? s1[i] : -INFINITY;
+        }
+    };
+    auto needs_mask = [&](int k) { return k * kPage + kPage > nvis_min; };
+
+    // Online softmax of one page for this lane's row (64 tokens, 32 per lane),
+    // in groups that are spread between MFMAs.  Produces the weights as hi/lo
+    // e4m3 operands (bytes 0-15 from tile 0, 16-31 from tile 1) and d_out, the
+    // rescale shift of everything accumulated so far (0 when unchanged).
+    auto softmax_steps = [&](f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out, int g) {
+        if (g == 0) {
+            float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+            mx = pair_max(mx) * c_exp;
+            const bool grow = mx > m + kRescaleSlack8;
+            const float m_new = grow ? __builtin_ceilf(mx) : m;
+            // (nothing has been accumulated while m is still -inf: no rescale)
+            d_out = grow && m != -INFINITY ? (int)fminf(m_new - m, 255.f) : 0;
+            m = m_new;
+            l *= __builtin_ldexpf(1.f, -d_out);
+        } else if (g >= 1 && g <= 4) {
+            const float mneg = m == -INFINITY ? 0.f : kWeightOffset8 - m;
+            f32x16& s = g <= 2 ? s0 : s1;
+            const int i0 = ((g - 1) & 1) * 8;
+            float sum = 0.f;
+#pragma unroll
+            for (int i = i0; i < i0 + 8; ++i) {
+                s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_exp, mneg));
+                sum += s[i];
+            }
+            l += sum;
+            const int r0 = (g - 1) * 2;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int i = i0 + 4 * q;
+                const int hw = pack_e4m3(s[i], s[i + 1], s[i + 2], s[i + 3]);
+                const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+                const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+                ph[r0 + q] = hw;
+                pl[r0 + q] = pack_e4m3(s[i] - h01[0], s[i + 1] - h01[1], s[i + 2] - h23[0], s[i + 3] - h23[1]);
+            }
+        } else if (g == 5) {
+            // publish (d in the sign bits of hi bytes 0-7; the own operand stays clean)
+            const int e0 = ph[0] | spread_nibble(d_out), e1 = ph[1] | spread_nibble(d_out >> 4);
+            *(lds_i32x4*)pbuf_mine = (i32x4){e0, e1, ph[2], ph[3]};
+            *(lds_i32x4*)(pbuf_mine + 1024) = (i32x4){ph[4], ph[5], ph[6], ph[7]};
+            *(lds_i32x4*)plo_mine = (i32x4){pl[0], pl[1], pl[2], pl[3]};
+            *(lds_i32x4*)(plo_mine + 1024) = (i32x4){pl[4], pl[5], pl[6], pl[7]};
+        }
+    };
+
+    // O^T += V^T . (P_hi + P_lo)^T over page k for both tiles of the pair (8
+    // dim tiles x 2 row tiles x 2 terms), with the softmax of page k + 1
+    // spread between the MFMA groups.  V^T fragments are read two ahead and
+    // each feeds four MFMAs.  MFMAs as inline assembly with O tied to its
+    // AGPRs; s_nop 3 covers a VALU write of an operand.
+    auto pv_softmax = [&](int k, const i32x8& ph_own, const i32x8& pl_own, const i32x8& ph_oth,
+                          const i32x8& pl_oth, f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out) {
+        lds_u8* cur = slot_ptr(k);
+        i32x8 vf[2];
+        vf[0] = vfrag(cur, 0);
+        vf[1] = vfrag(cur, 1);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const i32x8 a = vf[dt & 1];
+            __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+                         : "+a"(o0[dt]) : "v"(a), "v"(ph_own));
+            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+                         : "+a"(o1[dt]) : "v"(a), "v"(ph_oth));
+            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+                         : "+a"(o0[dt]) : "v"(a), "v"(pl_own));
+            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+                         : "+a"(o1[dt]) : "v"(a), "v"(pl_oth));
+            if (dt + 2 < 8) vf[dt & 1] = vfrag(cur, dt + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            if (dt < 6) softmax_steps(s0, s1, ph, pl, d_out, dt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Zero the rows of page k past the sequence end (they may hold anything,
+    // NaN included), so that a zero weight times V stays zero.
+    auto zero_tail = [&](int k) {
+        const int t0 = n - k * kPage;     // callers pass pages holding >= 1 token
+        if (t0 >= kPage) return;
+        lds_u8* cur = slot_ptr(k);
+        for (int idx = threadIdx.x; idx < (kPage - t0) * kRowChunks8; idx += 256) {
+            const int t = t0 + idx / kRowChunks8;
+            const int c = idx % kRowChunks8;
+            *(lds_i32x4*)(cur + t * kRowBytes8 + c * 16) = (i32x4)0;
+        }
+        lds_sync();
+    };
+
+    if (pg_begin < pg_end) {
+        i32x8 ph_cur, pl_cur, ph_nxt, pl_nxt, ph_oth, pl_oth;
+        int d_cur, d_oth;
+        {
+            const int k = pg_begin;
+            wait_copies(min(2, pg_end - 1 - k));
+            lds_sync();
+            zero_tail(k);
+            f32x16 s0, s1;
+            qk(k, s0, s1, [&](int) {});
+            if (needs_mask(k)) mask_s(k, s0, s1);
+#pragma unroll
+            for (int g = 0; g < 6; ++g) softmax_steps(s0, s1, ph_cur, pl_cur, d_cur, g);
+        }
+        // top of iteration k: page k + 1 landed, P(k) of both waves visible,
+        // every wave past its reads of page k - 1; the partner's P(k) terms and
+        // rescale shift are read here and first used after the QK^T
+        auto enter = [&](int k) {
+            wait_copies(k + 2 < pg_end ? 1 : 0);
+            lds_sync();
+            if (k + 1 < pg_end) zero_tail(k + 1);
+            const i32x4 h0 = *(const lds_i32x4*)pbuf_other;
+            const i32x4 h1 = *(const lds_i32x4*)(pbuf_other + 1024);
+            const i32x4 l0 = *(const lds_i32x4*)plo_other;
+            const i32x4 l1 = *(const lds_i32x4*)(plo_other + 1024);
+            d_oth = gather_nibble(h0[0]) | (gather_nibble(h0[1]) << 4);
+            ph_oth = (i32x8){h0[0] & 0x7f7f7f7f, h0[1] & 0x7f7f7f7f, h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+            pl_oth = cat8(l0, l1);
+        };
+        int k = pg_begin;
+        enter(k);
+        for (;;) {
+            f32x16 s0, s1;
+            // copy of page k + 3 into the slot of k - 1 (past the end of the
+            // range: page k again into that dead slot)
+            const int kc = k + 3 < pg_end ? k + 3 : k;
+            const uint8_t* csrc_w = page_src(kc) + wave * 16 * kRowBytes8;
+            const uint32_t cdst = slot_addr(k + 3) + wave * 9 * 1024;
+            qk(k + 1, s0, s1, [&](int j) { dma16(cdst + j * 1024, csrc_w, (uint32_t)cp_off[j]); });
+            lds_sync();   // the partner has read P(k): it may be overwritten
+            if (__builtin_expect(__any(d_cur != 0 || d_oth != 0), 0)) {
+                pv_drain();
+                scale_acc(o0, __builtin_ldexpf(1.f, -d_cur));
+                scale_acc(o1, __builtin_ldexpf(1.f, -d_oth));
+            }
+            if (needs_mask(k + 1)) mask_s(k + 1, s0, s1);
+            int d_nxt;
+            pv_softmax(k, ph_cur, pl_cur, ph_oth, pl_oth, s0, s1, ph_nxt, pl_nxt, d_nxt);
+            if (k + 1 >= pg_end) break;
+            ++k;
+            ph_cur = ph_nxt;
+            pl_cur = pl_nxt;
+            d_cur = d_nxt;
+            enter(k);
+        }
+    }
+
+    // ---- epilogue: o = kv_scale O / l, lse = ln(sum exp(s)) for both tiles of the pair.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    pv_drain();
+    const float l_own = pair_sum(l);
+    __syncthreads();
+    *lsum_mine = l_own;
+    __syncthreads();
+    const float l_oth = *lsum_other;
+    const int row_oth = w.mt * kMTile + (wave ^ 1) * 32 + lr;
+    const float inv_own = l_own > 0.f ? kv_scale / l_own : 0.f;
+    const float inv_oth = l_oth > 0.f ? kv_scale / l_oth : 0.f;
+    const int dim0 = 256 * h + 4 * G;
+    auto store_tile = [&](const f32x16 (&o)[8], int r, float inv) {
+        if (r >= p.rows) return;
+        const int rit = r - w.mt * kMTile;
+        if (w.nsplit == 1) {
+            const size_t orow = (size_t)b * p.rows + r;
+            if (p.out_bf16) {
+                __bf16* dst = (__bf16*)p.out + orow * kV + dim0;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        __bf16 __attribute__((ext_vector_type(4))) v;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[dt][4 * q4 + i] * inv);
+                        *(__bf16 __attribute__((ext_vector_type(4)))*)(dst + 32 * dt + 8 * q4) = v;
+                    }
+            } else {
+                float* dst = (float*)p.out + orow * kV + dim0;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        *(f32x4*)(dst + 32 * dt + 8 * q4) =
+                            (f32x4){o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]} * inv;
+            }
+        } else {
+            float* dst = p.ws_o + ((size_t)blockIdx.x * kMTile + rit) * kV + dim0;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    *(f32x4*)(dst + 32 * dt + 8 * q4) =
+                        (f32x4){o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]} * inv;
+        }
+    };
+    store_tile(o0, row, inv_own);
+    store_tile(o1, row_oth, inv_oth);
+    if (row_ok && G == 0) {
+        // l sums exp2(s c - m + 4): ln sum exp = (m - 4 + log2 l) ln 2
+        const float lse = l_own > 0.f ? (m - kWeightOffset8 + __log2f(l_own)) * kLn2 : -INFINITY;
+        if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
+        else p.ws_lse[(size_t)blockIdx.x * kMTile + (row - w.mt * kMTile)] = lse;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // LSE merge of one row from n partials: one wave, 8 output dims per lane
 // ---------------------------------------------------------------------------
 template <typename PartialAt>
@@ -735,6 +1205,20 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int units, hipStream_t stre
     }
     clear_stale_error();
     hipLaunchKernelGGL(decode_bf16_kernel, dim3(units), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ev_after) return hipEventRecord(ev_after, stream);
+    return hipSuccess;
+}
+
+hipError_t launch_decode_fp8(const DecodeParams& p, int units, hipStream_t stream,
+                             hipEvent_t ev_before, hipEvent_t ev_after) {
+    if (ev_before) {
+        hipError_t e = hipEventRecord(ev_before, stream);
+        if (e != hipSuccess) return e;
+    }
+    clear_stale_error();
+    hipLaunchKernelGGL(decode_fp8_kernel, dim3(units), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_after) return hipEventRecord(ev_after, stream);

@@ -78,6 +78,15 @@ def test_dcp_rank_share_and_four_shard_merge():
     compare(mo[sel], ml[sel], o_ref, l_ref, what="4-shard merge sampled")
 
 
+def test_fp8_cache_sampled():
+    """batch 128, 128 heads, ragged seq_lens uniform in [1024, 16384], e4m3 cache and
+    query with per-tensor scales, automatic splits."""
+    say("full-size fp8 batch128 H128 ragged 1024..16384 auto splits")
+    inp = workloads.make_config("c4", device=dev(), poison=True, extra_pages=4)
+    out, lse = run_hip(inp)
+    check_sampled(inp, out, lse, sample(inp.batch, 8, 404), "fp8 batch128 sampled")
+
+
 @pytest.fixture(scope="module")
 def long_context():
     say("full-size long context inputs + oracle: batch4 qlen2 seq131072")

@@ -149,3 +149,62 @@ def test_merge_kernel(n):
         fin = ~np.isneginf(l_ref)
         assert np.all(np.abs(o - o_ref) <= tol)
         assert np.max(np.abs(l[fin] - l_ref[fin])) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# OCP fp8 e4m3 cache and query (per-tensor scales: amax / 448; the query scale
+# is folded into the softmax scale, the cache scale is a device float)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 3])
+def test_fp8_tiny_all_elements(num_splits):
+    say(f"fp8 tiny num_splits={num_splits}")
+    inp = workloads.make_decode_inputs(2, 1, 16, [37, 100], "fp8", seed=31, device=dev())
+    out, lse = run_hip(inp, num_splits=num_splits)
+    o_ref, l_ref = run_oracle(inp)
+    compare(out, lse, o_ref, l_ref, dtype="fp8", what=f"fp8 tiny splits={num_splits}")
+
+
+@pytest.mark.parametrize("heads", [128, 20])
+def test_fp8_page_boundary_lengths(heads):
+    say(f"fp8 page boundaries heads={heads}")
+    inp = workloads.make_decode_inputs(6, 1, heads, [1, 63, 64, 65, 129, 0], "fp8", seed=32 + heads,
+                                       device=dev())
+    o_ref, l_ref = run_oracle(inp)
+    for ns in (0, 1, 2):
+        out, lse = run_hip(inp, num_splits=ns)
+        compare(out, lse, o_ref, l_ref, dtype="fp8", what=f"fp8 boundaries H={heads} splits={ns}")
+    assert torch.all(out[5] == 0) and torch.all(torch.isneginf(lse[5]))
+
+
+def test_fp8_ragged_many_pages_and_splits():
+    rng = np.random.default_rng(33)
+    lens = rng.integers(1, 3000, size=6).tolist()
+    say(f"fp8 ragged lens={lens}")
+    inp = workloads.make_decode_inputs(6, 1, 128, lens, "fp8", seed=33, device=dev())
+    o_ref, l_ref = run_oracle(inp)
+    for ns in (0, 1, 5, 30):
+        out, lse = run_hip(inp, num_splits=ns)
+        compare(out, lse, o_ref, l_ref, dtype="fp8", what=f"fp8 ragged splits={ns}")
+
+
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_fp8_qlen2_causal(num_splits):
+    say(f"fp8 q_len=2 causal splits={num_splits}")
+    inp = workloads.make_decode_inputs(3, 2, 128, [200, 130, 65], "fp8", seed=34, device=dev())
+    out, lse = run_hip(inp, num_splits=num_splits)
+    o_ref, l_ref = run_oracle(inp)
+    compare(out, lse, o_ref, l_ref, dtype="fp8", what=f"fp8 qlen2 causal splits={num_splits}")
+
+
+def test_fp8_bf16_output_and_determinism():
+    import mla_latent_decode_absorbed_amd as mla
+    say("fp8 bf16 output + determinism")
+    inp = workloads.make_decode_inputs(3, 1, 128, [300, 64, 1000], "fp8", seed=35, device=dev())
+    o_ref, l_ref = run_oracle(inp)
+    out, lse = run_hip(inp, num_splits=2, out_dtype=mla.BF16)
+    assert out.dtype == torch.bfloat16
+    compare(out, lse, o_ref, l_ref, dtype="fp8", what="fp8 bf16 out")
+    a = run_hip(inp)
+    b = run_hip(inp)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

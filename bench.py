@@ -137,6 +137,8 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="minimum wall time of the untimed warm-up (clocks settle)")
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over the steps")
@@ -179,8 +181,14 @@ def main(argv=None) -> int:
         dec(inp.q, copies[i % len(copies)], inp.block_table, inp.seq_lens, inp.scale,
             kv_scale=inp.kv_scale, out=out, lse=lse, stream=stream, events=events)
 
-    for i in range(args.warmup):
+    # warm-up: at least W steps and at least --warmup-seconds of back-to-back
+    # work, so that the clocks have settled before the timed region
+    i, t_w = 0, time.perf_counter()
+    while i < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
         step(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -226,6 +234,7 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": i,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -28,8 +28,31 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the gfx950 library cannot be built")
 
 
+def check_wait_states(verbose: bool = False) -> None:
+    """Compile the kernels to gfx950 assembly and verify the wait states around
+    the inline-assembly MFMAs (see isa_check.py); raises on a violation."""
+    from mla_latent_decode_absorbed_amd import isa_check  # noqa: WPS433 (import inside: plain module)
+    asm = os.path.join(PKG, "_kernels_gfx950.s")
+    flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
+    cmd = [hipcc(), *flags, "--cuda-device-only", "-S", "-I", INCLUDE, "-I", CSRC, "-o", asm, SOURCES[0]]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc -S failed with status {res.returncode}")
+    try:
+        problems = isa_check.check_asm(open(asm).read())
+    finally:
+        os.remove(asm)
+    if problems:
+        raise RuntimeError("gfx950 wait-state check failed:\n  " + "\n  ".join(problems[:20]))
+    if verbose:
+        print("wait-state check: ok", flush=True)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 into the package's libmla_decode.so (always rebuilds)."""
+    """Compile every source for gfx950 into the package's libmla_decode.so (always
+    rebuilds), after checking the wait states of the generated kernel code."""
+    check_wait_states(verbose)
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *SOURCES]
     if verbose:

@@ -3,9 +3,26 @@
 #include "mla_decode.h"
 #include "mla_internal.h"
 
+#include <atomic>
 #include <math.h>
 
 namespace {
+
+// Compute units of the current device (cached per device; the only state the
+// library keeps).  The automatic split targets one workgroup per CU, capped at
+// kTargetUnits, which also bounds the workspace.
+int target_units_for_current_device() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return mla::kTargetUnits;
+    int cus = cached[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return mla::kTargetUnits;
+        cached[dev].store(cus, std::memory_order_relaxed);
+    }
+    return cus < mla::kTargetUnits ? cus : mla::kTargetUnits;
+}
 
 constexpr size_t kAlign = 256;
 
@@ -85,7 +102,7 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     pp.m_tiles = L.m_tiles;
     pp.max_pages = d->max_pages_per_seq;
     pp.num_splits = d->num_splits;
-    pp.target_units = mla::kTargetUnits;
+    pp.target_units = target_units_for_current_device();
     pp.min_chunk = mla::kMinChunkPages;
     pp.units_max = (int32_t)L.units_max;
     if (mla::launch_plan(pp, seq_lens, req_info, work, s) != hipSuccess) return MLA_ERR_HIP;

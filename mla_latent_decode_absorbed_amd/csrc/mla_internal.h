@@ -11,7 +11,7 @@ constexpr int kQK = 576;          // latent 512 + rope 64
 constexpr int kV = 512;           // V = the latent part of the same cache row
 constexpr int kPage = 64;         // tokens per cache page
 constexpr int kMTile = 128;       // query rows per decode workgroup (heads x query tokens)
-constexpr int kTargetUnits = 256; // automatic split target: one workgroup per CU (256 CUs)
+constexpr int kTargetUnits = 256; // automatic split: at most this many workgroups (one per CU)
 constexpr int kMinChunkPages = 2; // smallest automatic split, in pages
 
 // One unit of split-KV work: rows [mt*kMTile, +kMTile) of request b over the

@@ -54,87 +54,139 @@ __device__ __forceinline__ int lds_off(int t, int c) { return t * kRowBytes + ((
 // ---------------------------------------------------------------------------
 // plan: per-request split counts and the work list (one workgroup, no host sync)
 // ---------------------------------------------------------------------------
+// Sum (or max) of one value per thread over the 1024-thread block: a
+// wavefront reduction, then the 16 wave results through LDS.  `buf` alternates
+// between two halves so that back-to-back calls need one barrier each.
+__device__ __forceinline__ long long block_reduce(long long v, bool is_max, long long* buf, int& parity) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const long long o = __shfl_xor(v, off);
+        v = is_max ? (o > v ? o : v) : v + o;
+    }
+    long long* half = buf + 16 * parity;
+    parity ^= 1;
+    if ((threadIdx.x & 63) == 0) half[threadIdx.x >> 6] = v;
+    __syncthreads();
+    long long r = half[0];
+    for (int i = 1; i < 16; ++i) r = is_max ? (half[i] > r ? half[i] : r) : r + half[i];
+    return r;
+}
+
 __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t* __restrict__ seq_lens,
                                                     int32_t* __restrict__ req_info,
                                                     WorkItem* __restrict__ work) {
-    __shared__ long long s_red[1024];
+    constexpr int kCached = 8192;            // page counts of up to this many requests stay in LDS
+    __shared__ long long s_part[32];
     __shared__ int s_scan[1024];
+    __shared__ int s_pages[kCached];
+    int parity = 0;
     const int tid = threadIdx.x;
     const int per = (p.batch + 1023) / 1024;
     const int b0 = min(p.batch, tid * per), b1 = min(p.batch, b0 + per);
     const int cap = p.max_pages * kPage;
-
-    long long my_pages = 0;
-    for (int b = b0; b < b1; ++b) {
-        int n = min(max(seq_lens[b], 0), cap);
-        my_pages += (n + kPage - 1) / kPage;
-    }
-    s_red[tid] = my_pages;
+    auto pages_global = [&](int b) {
+        const int n = min(max(seq_lens[b], 0), cap);
+        return (n + kPage - 1) / kPage;
+    };
+    for (int b = tid; b < p.batch && b < kCached; b += 1024) s_pages[b] = pages_global(b);
     __syncthreads();
-    for (int s = 512; s > 0; s >>= 1) {
-        if (tid < s) s_red[tid] += s_red[tid + s];
-        __syncthreads();
+    auto pages_of = [&](int b) { return b < kCached ? s_pages[b] : pages_global(b); };
+
+    long long my_pages = 0, my_max = 0;
+    for (int b = b0; b < b1; ++b) {
+        const int pg = pages_of(b);
+        my_pages += pg;
+        my_max = pg > my_max ? pg : my_max;
     }
-    const long long total_pages = s_red[0];
+    const long long total_pages = block_reduce(my_pages, false, s_part, parity);
     long long chunk = 1;
     if (p.num_splits <= 0) {
-        long long want = (total_pages * p.m_tiles + p.target_units - 1) / p.target_units;
-        chunk = want > p.min_chunk ? want : p.min_chunk;
+        // The smallest chunk (in pages) for which every request's splits, times
+        // the row tiles, fit in one round of target_units workgroups: the
+        // longest unit, and so the kernel, is then as short as this policy
+        // allows.  Binary search between the averaging bound and the longest
+        // request (a batch too large to split keeps one split per request).
+        const long long max_pages = block_reduce(my_max, true, s_part, parity);
+        const long long units_cap = p.target_units / p.m_tiles > 0 ? p.target_units / p.m_tiles : 1;
+        long long lo = (total_pages + units_cap - 1) / units_cap;
+        lo = lo > p.min_chunk ? lo : p.min_chunk;
+        long long hi = max_pages > lo ? max_pages : lo;
+        while (lo < hi) {
+            const long long mid = (lo + hi) / 2;
+            long long cnt = 0;
+            for (int b = b0; b < b1; ++b) {
+                const long long pg = pages_of(b);
+                cnt += pg > mid ? (pg + mid - 1) / mid : 1;
+            }
+            if (block_reduce(cnt, false, s_part, parity) <= units_cap) hi = mid;
+            else lo = mid + 1;
+        }
+        chunk = lo;
     }
 
+    // splits per request, and the first kv-unit of each request (exclusive
+    // scan: a wavefront scan, then the 16 wave totals through LDS)
     int my_k = 0;
     for (int b = b0; b < b1; ++b) {
-        int n = min(max(seq_lens[b], 0), cap);
-        int pages = (n + kPage - 1) / kPage;
-        int S = p.num_splits > 0 ? min(p.num_splits, pages) : (int)((pages + chunk - 1) / chunk);
+        const int pages = pages_of(b);
+        const int S = p.num_splits > 0 ? min(p.num_splits, pages) : (int)((pages + chunk - 1) / chunk);
         my_k += max(S, 1);
     }
-    s_scan[tid] = my_k;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {   // inclusive Hillis-Steele scan
-        int v = tid >= off ? s_scan[tid - off] : 0;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
+    const int lane = tid & 63, wv = tid >> 6;
+    int incl = my_k;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
     }
-    const int k_total = s_scan[1023];
-    int base = s_scan[tid] - my_k;
-
+    if (lane == 63) s_scan[wv] = incl;
+    __syncthreads();
+    int wave_base = 0, k_total = 0;
+    for (int i = 0; i < 16; ++i) {
+        const int t = s_scan[i];
+        wave_base += i < wv ? t : 0;
+        k_total += t;
+    }
+    int base = wave_base + incl - my_k;
     for (int b = b0; b < b1; ++b) {
-        int n = min(max(seq_lens[b], 0), cap);
-        int pages = (n + kPage - 1) / kPage;
-        int S, cb;
-        if (p.num_splits > 0) {
-            S = max(1, min(p.num_splits, pages));
-            cb = (pages + S - 1) / S;
-        } else {
-            S = max(1, (int)((pages + chunk - 1) / chunk));
-            cb = (int)chunk;
-        }
+        const int pages = pages_of(b);
+        const int S = p.num_splits > 0 ? max(1, min(p.num_splits, pages))
+                                       : max(1, (int)((pages + chunk - 1) / chunk));
         req_info[2 * b] = S;
         req_info[2 * b + 1] = base;
-        for (int s = 0; s < S; ++s) {
-            const int k = base + s;
-            const int pb = min(pages, s * cb), pe = min(pages, (s + 1) * cb);
-            for (int mt = 0; mt < p.m_tiles; ++mt) {
-                WorkItem w;
-                w.b = b; w.mt = mt; w.split = s; w.page_begin = pb; w.page_end = pe;
-                w.nsplit = S; w.pad0 = 0; w.pad1 = 0;
-                work[unit_index(k, mt, p.m_tiles)] = w;
-            }
-        }
         base += S;
     }
-    // slots past the last kv-unit are empty
+    __syncthreads();   // req_info of every request written (and visible to the block)
+
+    // Work items, one thread per (kv-unit, row tile) slot.  Slot u holds kv-unit
+    // k = 8 (u / (8 m_tiles)) + u % 8 and row tile (u / 8) % m_tiles; its
+    // request is found by binary search over the first kv-unit of each request.
     for (int u = tid; u < p.units_max; u += 1024) {
         const int grp = u / (8 * p.m_tiles);
         const int k = grp * 8 + (u & 7);
+        const int mt = (u >> 3) % p.m_tiles;
+        WorkItem w;
+        w.pad0 = 0;
+        w.pad1 = 0;
         if (k >= k_total) {
-            WorkItem w;
-            w.b = -1; w.mt = 0; w.split = 0; w.page_begin = 0; w.page_end = 0;
-            w.nsplit = 0; w.pad0 = 0; w.pad1 = 0;
-            work[u] = w;
+            w.b = -1; w.mt = 0; w.split = 0; w.page_begin = 0; w.page_end = 0; w.nsplit = 0;
+        } else {
+            int lo = 0, hi = p.batch - 1;     // last request whose first kv-unit is <= k
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (req_info[2 * mid + 1] <= k) lo = mid; else hi = mid - 1;
+            }
+            const int b = lo;
+            const int S = req_info[2 * b];
+            const int s = k - req_info[2 * b + 1];
+            const int pages = pages_of(b);
+            const int cb = p.num_splits > 0 ? (pages + S - 1) / S : (int)chunk;
+            w.b = b; w.mt = mt; w.split = s;
+            w.page_begin = min(pages, s * cb);
+            w.page_end = min(pages, (s + 1) * cb);
+            w.nsplit = S;
         }
+        work[u] = w;
     }
 }
 
@@ -149,11 +201,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
 //   O^T[32 dims][32 rows] += V^T[32 dims][16 tok] . P^T[16 tok][32 rows]
 // Wave w owns query rows 32 w .. 32 w + 31: it contracts all 576 dims of
 // every token against them (its Q^T stays in 144 VGPRs), runs their online
-// softmax and owns their max and row sum.  Waves 2j and 2j + 1 form a pair
-// for the PV product: each accumulates O^T for BOTH tiles of the pair (64
-// rows) over one half of the 512 output dims, so every V^T fragment read from
-// LDS feeds two MFMAs.  The pair trades its bf16 P^T tiles (and, when a row
-// max moves, the rescale factor) through LDS once per half page.
+// softmax and owns their max and row sum.  For the PV product every wave
+// accumulates O^T for ALL four row tiles (128 rows) over one quarter of the
+// 512 output dims (128 w .. 128 w + 127), so every V^T fragment read from LDS
+// feeds four MFMAs: the LDS transpose reads, the slowest LDS access a single
+// wave per SIMD can issue, are a quarter of the cache bytes per wave.  The
+// waves trade their bf16 P^T tiles (and, when a row max moves, the rescale
+// factor) through LDS once per half page.
 //
 // The cache streams through LDS in half pages of 32 tokens (36,864 bytes)
 // held in a ring of 4 slots with direct HBM -> LDS loads; the copy of half
@@ -187,11 +241,19 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* gbase, uint
                  :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory");
 }
 
-// Wait until at most `ahead` half pages of this wave's copies are still in flight.
+// s_waitcnt immediates (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8) that wait for vector memory only.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Wait until at most `ahead` groups of 9 copies (one ring slot per wave) are
+// still in flight.  Issued through the builtin (not inline assembly) so that
+// the compiler's own wait tracking sees it: a value it loaded earlier (a
+// block-table entry) is then known to have arrived, and it does not add a
+// vmcnt(0) of its own that would drain the copies in flight.
 __device__ __forceinline__ void wait_copies(int ahead) {
-    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 }
 
 // Workgroup barrier for LDS traffic only (outstanding copies stay in flight).
@@ -216,7 +278,6 @@ void decode_bf16_kernel(DecodeParams p) {
     if (w.b < 0) return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int h = wave & 1;         // PV: which half of the 512 output dims
     const int G = lane >> 5;        // MFMA k-group of this lane (0/1)
     const int lr = lane & 31;       // query row of this lane within its 32-row tile
     const int b = w.b;
@@ -225,10 +286,12 @@ void decode_bf16_kernel(DecodeParams p) {
     const uint8_t* kvbase = (const uint8_t*)p.kv;
     lds_u8* const ring = (lds_u8*)lds;
     const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
-    lds_u8* const pbuf_mine = (lds_u8*)lds + kPBufOff + wave * 2048 + lane * 16;
-    lds_u8* const pbuf_other = (lds_u8*)lds + kPBufOff + (wave ^ 1) * 2048 + lane * 16;
-    lds_f32* const abuf_mine = (lds_f32*)(lds + kABufOff) + wave * 64 + lane;
-    lds_f32* const abuf_other = (lds_f32*)(lds + kABufOff) + (wave ^ 1) * 64 + lane;
+    // exchange buffers: P^T fragments of tile t at pbuf + 2048 t (k-step k2 at
+    // + 1024 k2), rescale factor / row sum of tile t at abuf + 64 t
+    lds_u8* const pbuf = (lds_u8*)lds + kPBufOff + lane * 16;
+    lds_f32* const abuf = (lds_f32*)(lds + kABufOff) + lane;
+    lds_u8* const pbuf_mine = pbuf + wave * 2048;
+    lds_f32* const abuf_mine = abuf + wave * 64;
 
     // half pages of this unit that hold at least one token
     const int half_begin = 2 * w.page_begin;
@@ -312,9 +375,10 @@ void decode_bf16_kernel(DecodeParams p) {
     // PV transpose reads.  The 16-lane block bk = lane / 16 covers dims
     // 16 (bk % 2) .. + 15 of a 32-dim tile and tokens 16 k2 + 4 G + e (first
     // read) and + 8 (second read), e = (lane % 16) / 4; the lane supplies dims
-    // 4 (lane % 4) .. + 3 of its token.  Dim tile dt of half h starts at dim
-    // 256 h + 32 dt: chunk 32 h + 4 dt + 2 (bk % 2) + (lane % 4) / 2, and every
-    // token read has swizzle 2 e + G.
+    // 4 (lane % 4) .. + 3 of its token.  Dim tile dq of quarter w starts at dim
+    // 128 w + 32 dq: chunk 16 w + 4 dq + 2 (bk % 2) + (lane % 4) / 2, and every
+    // token read has swizzle 2 e + G (the XOR touches the 3 low chunk bits
+    // only, so 16 w and 4 (dq / 2) stay outside it).
     int tr_off[2];
     {
         const int li = lane & 15, e = li >> 2, cc = li & 3, dh = (lane >> 4) & 1;
@@ -322,45 +386,45 @@ void decode_bf16_kernel(DecodeParams p) {
         const int sw = swz(t);
 #pragma unroll
         for (int d2 = 0; d2 < 2; ++d2)
-            tr_off[d2] = t * kRowBytes + h * 512 + (((4 * d2 + 2 * dh + (cc >> 1)) ^ sw) << 4) + (cc & 1) * 8;
+            tr_off[d2] = t * kRowBytes + wave * 256 + (((4 * d2 + 2 * dh + (cc >> 1)) ^ sw) << 4) + (cc & 1) * 8;
     }
 
-    // O^T accumulators: o0 = this wave's own 32 rows, o1 = the partner's 32
-    // rows, each over dims 256 h .. 256 h + 255 (8 tiles of 32 dims).
-    f32x16 o0[8], o1[8];
+    // O^T accumulators: o[t][dq] = rows of tile t (32 t .. 32 t + 31) over dims
+    // 128 w + 32 dq .. + 31 (element i is dim + 8 (i / 4) + 4 G + i % 4).
+    f32x16 o[4][4];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        o0[dt] = (f32x16)0.f;
-        o1[dt] = (f32x16)0.f;
-        asm volatile("" : "+a"(o0[dt]));
-        asm volatile("" : "+a"(o1[dt]));
-    }
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int dq = 0; dq < 4; ++dq) {
+            o[t][dq] = (f32x16)0.f;
+            asm volatile("" : "+a"(o[t][dq]));
+        }
+    float m = -INFINITY, l = 0.f;   // reference max (log2 units) and this lane's part of the row sum
     // MFMA results of the inline-assembly PV read by VALU code: the compiler
     // does not see those MFMAs, so their wait states are inserted here (more
     // than an XDL write -> VALU read of a 16-pass MFMA needs).
     auto pv_drain = [&]() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); };
-    // o *= a for one set of accumulators, one register at a time through a
-    // single VGPR (the accumulators never leave the AGPRs).
-    auto scale_acc = [&](f32x16 (&o)[8], float a) {
+    // o *= a for the accumulators of one row tile, one register at a time
+    // through a single VGPR (the accumulators never leave the AGPRs).
+    auto scale_acc = [&](f32x16 (&ot)[4], float a) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
+        for (int dq = 0; dq < 4; ++dq)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float e = o[dt][i];
+                float e = ot[dq][i];
                 float t;
                 asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
                              : "+a"(e), "=&v"(t) : "v"(a));
-                o[dt][i] = e;
+                ot[dq][i] = e;
             }
     };
-    float m = -INFINITY, l = 0.f;   // reference max (log2 units) and this lane's part of the row sum
 
     auto kfrag = [&](lds_u8* cur, int ks) -> bf16x8_t {
         return *(const lds_bf16x8*)(cur + qk_off[ks & 3] + (ks >> 2) * 128);
     };
-    auto vfrag = [&](lds_u8* cur, int i) -> bf16x8_t {      // i = 8 k2 + dt
-        const int k2 = i >> 3, dt = i & 7;
-        const int off = tr_off[dt & 1] + (dt >> 1) * 128 + k2 * 16 * kRowBytes;
+    auto vfrag = [&](lds_u8* cur, int i) -> bf16x8_t {      // i = 4 k2 + dq
+        const int k2 = i >> 2, dq = i & 3;
+        const int off = tr_off[dq & 1] + (dq >> 1) * 128 + k2 * 16 * kRowBytes;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off + 8 * kRowBytes));
         return __builtin_bit_cast(bf16x8_t, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
@@ -376,13 +440,14 @@ void decode_bf16_kernel(DecodeParams p) {
     // the others accumulate back to back into the same registers.
     auto qk = [&](int k, f32x16& s, auto&& between) {
         lds_u8* cur = slot_ptr(k);
-        bf16x8_t kf[4];
+        constexpr int kKAhead = 6;
+        bf16x8_t kf[kKAhead];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kf[ks] = kfrag(cur, ks);
+        for (int ks = 0; ks < kKAhead; ++ks) kf[ks] = kfrag(cur, ks);
 #pragma unroll
         for (int ks = 0; ks < 36; ++ks) {
-            const bf16x8_t a = kf[ks & 3];
-            if (ks + 4 < 36) kf[ks & 3] = kfrag(cur, ks + 4);
+            const bf16x8_t a = kf[ks % kKAhead];
+            if (ks + kKAhead < 36) kf[ks % kKAhead] = kfrag(cur, ks + kKAhead);
             if (ks == 0)
                 asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
                              : "=&v"(s) : "v"(a), "v"(qf[ks]));
@@ -439,20 +504,22 @@ void decode_bf16_kernel(DecodeParams p) {
         *abuf_mine = alpha;
     };
 
-    // O^T += V^T . P^T over half page k for both tiles of the pair, with the
-    // softmax of half page k + 1 spread between its MFMAs so that the
+    // O^T += V^T . P^T over half page k for all four row tiles, with the
+    // softmax of half page k + 1 spread between its MFMA groups so that the
     // exp/max/convert work runs while the matrix cores are busy
-    // (sched_barrier(0) pins the order of the groups).  V^T fragments are read
-    // four ahead and each feeds two MFMAs.  The MFMAs are inline assembly with
-    // O tied to its accumulation registers, so the compiler never moves O out
-    // of the AGPRs; it does not see them, so s_nop 3 gives the wait states a
-    // VALU write of an operand needs before an MFMA reads it.
-    auto pv_softmax = [&](int k, const bf16x8_t (&pf_own)[2], const bf16x8_t (&pf_oth_)[2], f32x16& s,
-                          bf16x8_t (&pf)[2], float& alpha_out) {
+    // (sched_barrier(0) pins the order of the groups).  Each of the 8 V^T
+    // fragments (2 k-steps x 4 dim tiles) feeds four MFMAs; fragments are read
+    // four ahead.  The MFMAs are inline assembly with O tied to its
+    // accumulation registers, so the compiler never moves O out of the AGPRs.
+    // Their operands come straight from LDS reads (no VALU write precedes an
+    // MFMA read, which would need 2 wait states the compiler does not know to
+    // insert); the build scans the generated code for such a pair.
+    auto pv_softmax = [&](int k, const bf16x8_t (&pa)[4][2], f32x16& s, bf16x8_t (&pf)[2], float& alpha_out) {
         lds_u8* cur = slot_ptr(k);
-        bf16x8_t vf[4];
+        constexpr int kVAhead = 4;
+        bf16x8_t vf[kVAhead];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vf[i] = vfrag(cur, i);
+        for (int i = 0; i < kVAhead; ++i) vf[i] = vfrag(cur, i);
         float mx, mneg, sum0 = 0.f, sum1 = 0.f;
         const float c = p.scale_log2;
         auto chunk = [&](int g) {
@@ -469,36 +536,40 @@ void decode_bf16_kernel(DecodeParams p) {
                 m = m_new;
                 mneg = m == -INFINITY ? 0.f : -m;
                 l *= alpha_out;
-            } else if (g >= 2 && g < 10) {
-                const int i = 2 * (g - 2);
-                s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, mneg));
-                s[i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, mneg));
-                sum0 += s[i];
-                sum1 += s[i + 1];
-            } else if (g == 10) {
+            } else if (g >= 2 && g < 6) {
+                const int i = 4 * (g - 2);
+#pragma unroll
+                for (int u = 0; u < 4; u += 2) {
+                    s[i + u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + u], c, mneg));
+                    s[i + u + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + u + 1], c, mneg));
+                    sum0 += s[i + u];
+                    sum1 += s[i + u + 1];
+                }
+            } else if (g == 6) {
                 l += sum0 + sum1;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pf[0][e] = (__bf16)s[e];
-            } else if (g == 11) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pf[1][e] = (__bf16)s[8 + e];
-            } else if (g == 12) {
+                for (int e = 0; e < 8; ++e) {
+                    pf[0][e] = (__bf16)s[e];
+                    pf[1][e] = (__bf16)s[8 + e];
+                }
+            } else if (g == 7) {
                 *(lds_bf16x8*)pbuf_mine = pf[0];
                 *(lds_bf16x8*)(pbuf_mine + 1024) = pf[1];
                 *abuf_mine = alpha_out;
             }
         };
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const bf16x8_t a = vf[i & 3];
+        for (int i = 0; i < 8; ++i) {
+            const bf16x8_t a = vf[i % kVAhead];
+            const int k2 = i >> 2, dq = i & 3;
             __builtin_amdgcn_sched_barrier(0);
-            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                         : "+a"(o0[i & 7]) : "v"(a), "v"(pf_own[i >> 3]));
-            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                         : "+a"(o1[i & 7]) : "v"(a), "v"(pf_oth_[i >> 3]));
-            if (i + 4 < 16) vf[i & 3] = vfrag(cur, i + 4);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                             : "+a"(o[t][dq]) : "v"(a), "v"(pa[t][k2]));
+            if (i + kVAhead < 8) vf[i % kVAhead] = vfrag(cur, i + kVAhead);
             __builtin_amdgcn_sched_barrier(0);
-            if (i < 13) chunk(i);
+            chunk(i);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -519,8 +590,8 @@ void decode_bf16_kernel(DecodeParams p) {
     auto needs_mask = [&](int k) { return k * kHalfTok + kHalfTok > nvis_min; };
 
     if (half_begin < half_end) {
-        bf16x8_t pf_cur[2], pf_nxt[2], pf_oth[2];
-        float a_cur, a_oth;
+        bf16x8_t pa[4][2], pf_nxt[2];
+        float av[4];
         // ---- prologue: S, softmax and P of the first half page
         {
             const int k = half_begin;
@@ -529,20 +600,26 @@ void decode_bf16_kernel(DecodeParams p) {
             zero_tail(k);
             f32x16 s;
             qk(k, s, [&](int) {});
-            a_cur = softmax(k, s, pf_cur, needs_mask(k));
-            publish(pf_cur, a_cur);
+            const float a0 = softmax(k, s, pf_nxt, needs_mask(k));
+            publish(pf_nxt, a0);
         }
         // Top of iteration k: the copies of half page k + 1 have landed, P(k)
-        // of both waves is visible, and every wave is past its reads of half
-        // page k - 1 (whose slot the next copy refills).  The partner's P(k)
-        // and rescale factor are read here and first used after the QK^T.
+        // of every wave is visible, and every wave is past its reads of half
+        // page k - 1 (whose slot the next copy refills).
         auto enter = [&](int k) {
             wait_copies(k + 2 < half_end ? 1 : 0);
             lds_sync();
             if (k + 1 < half_end) zero_tail(k + 1);
-            pf_oth[0] = *(const lds_bf16x8*)pbuf_other;
-            pf_oth[1] = *(const lds_bf16x8*)(pbuf_other + 1024);
-            a_oth = *abuf_other;
+        };
+        // P(k) of all four tiles and their rescale factors, read late in the
+        // QK^T of half page k + 1 (after its last K fragment reads)
+        auto read_p = [&]() {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                pa[t][0] = *(const lds_bf16x8*)(pbuf + t * 2048);
+                pa[t][1] = *(const lds_bf16x8*)(pbuf + t * 2048 + 1024);
+                av[t] = abuf[t * 64];
+            }
         };
         int k = half_begin;
         enter(k);
@@ -557,78 +634,75 @@ void decode_bf16_kernel(DecodeParams p) {
             const int kc = k + 3 < half_end ? k + 3 : k;
             const uint8_t* csrc_w = half_src(kc) + wave * 8 * kRowBytes;
             const uint32_t cdst = slot_addr(k + 3) + wave * 9 * 1024;
-            qk(k + 1, s, [&](int j) { dma16(cdst + j * 1024, csrc_w, (uint32_t)cp_off[j]); });
-            lds_sync();   // the partner has read P(k): it may be overwritten
-            if (__builtin_expect(__any(a_cur != 1.f || a_oth != 1.f), 0)) {
-                // a row max moved: rescale what both tiles have accumulated so far
+            qk(k + 1, s, [&](int j) {
+                dma16(cdst + j * 1024, csrc_w, (uint32_t)cp_off[j]);
+                if (j == 7) read_p();
+            });
+            lds_sync();   // every wave has read P(k): it may be overwritten
+            if (__builtin_expect(__any(av[0] != 1.f || av[1] != 1.f || av[2] != 1.f || av[3] != 1.f), 0)) {
+                // a row max moved: rescale what the tile has accumulated so far
                 pv_drain();
-                scale_acc(o0, a_cur);
-                scale_acc(o1, a_oth);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) scale_acc(o[t], av[t]);
             }
             if (needs_mask(k + 1)) mask_s(k + 1, s);
             float a_nxt;
-            pv_softmax(k, pf_cur, pf_oth, s, pf_nxt, a_nxt);
+            pv_softmax(k, pa, s, pf_nxt, a_nxt);
             if (k + 1 >= half_end) break;
             ++k;
-            pf_cur[0] = pf_nxt[0];
-            pf_cur[1] = pf_nxt[1];
-            a_cur = a_nxt;
             enter(k);
         }
     }
 
-    // ---- epilogue: o = O / l and lse = ln(sum exp) for both tiles of the pair.
+    // ---- epilogue: o = O / l for all four row tiles over this wave's dims, and
+    //      lse = ln(sum exp) for this wave's own rows.
     // No copy may still be writing this workgroup's LDS when it exits.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     pv_drain();
     const float l_own = pair_sum(l);
     __syncthreads();                      // every wave is done reading the exchange buffers
     *abuf_mine = l_own;
     __syncthreads();
-    const float l_oth = *abuf_other;
-    const int tile_oth = wave ^ 1;
-    const int row_oth = w.mt * kMTile + tile_oth * 32 + lr;
-    const float inv_own = l_own > 0.f ? 1.f / l_own : 0.f;
-    const float inv_oth = l_oth > 0.f ? 1.f / l_oth : 0.f;
-    // element i of dim tile dt is dim 256 h + 32 dt + 8 (i / 4) + 4 G + i % 4
-    const int dim0 = 256 * h + 4 * G;
-    auto store_tile = [&](const f32x16 (&o)[8], int r, float inv) {
+    // element i of dim tile dq is dim 128 w + 32 dq + 8 (i / 4) + 4 G + i % 4
+    const int dim0 = 128 * wave + 4 * G;
+    auto store_tile = [&](const f32x16 (&ot)[4], int r, float lt) {
         if (r >= p.rows) return;
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
         const int rit = r - w.mt * kMTile;
         if (w.nsplit == 1) {
             const size_t orow = (size_t)b * p.rows + r;
             if (p.out_bf16) {
                 __bf16* dst = (__bf16*)p.out + orow * kV + dim0;
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
+                for (int dq = 0; dq < 4; ++dq)
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
                         __bf16 __attribute__((ext_vector_type(4))) v;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[dt][4 * q4 + i] * inv);
-                        *(__bf16 __attribute__((ext_vector_type(4)))*)(dst + 32 * dt + 8 * q4) = v;
+                        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(ot[dq][4 * q4 + i] * inv);
+                        *(__bf16 __attribute__((ext_vector_type(4)))*)(dst + 32 * dq + 8 * q4) = v;
                     }
             } else {
                 float* dst = (float*)p.out + orow * kV + dim0;
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
+                for (int dq = 0; dq < 4; ++dq)
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4)
-                        *(f32x4*)(dst + 32 * dt + 8 * q4) =
-                            (f32x4){o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]} * inv;
+                        *(f32x4*)(dst + 32 * dq + 8 * q4) =
+                            (f32x4){ot[dq][4 * q4], ot[dq][4 * q4 + 1], ot[dq][4 * q4 + 2], ot[dq][4 * q4 + 3]} * inv;
             }
         } else {
             float* dst = p.ws_o + ((size_t)blockIdx.x * kMTile + rit) * kV + dim0;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
+            for (int dq = 0; dq < 4; ++dq)
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
-                    *(f32x4*)(dst + 32 * dt + 8 * q4) =
-                        (f32x4){o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]} * inv;
+                    *(f32x4*)(dst + 32 * dq + 8 * q4) =
+                        (f32x4){ot[dq][4 * q4], ot[dq][4 * q4 + 1], ot[dq][4 * q4 + 2], ot[dq][4 * q4 + 3]} * inv;
         }
     };
-    store_tile(o0, row, inv_own);
-    store_tile(o1, row_oth, inv_oth);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) store_tile(o[t], w.mt * kMTile + 32 * t + lr, abuf[t * 64]);
     if (row_ok && G == 0) {
         const float lse = l_own > 0.f ? (m + __log2f(l_own)) * kLn2 : -INFINITY;
         if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
@@ -951,7 +1025,8 @@ void decode_fp8_kernel(DecodeParams p) {
     // dim tiles x 2 row tiles x 2 terms), with the softmax of page k + 1
     // spread between the MFMA groups.  V^T fragments are read two ahead and
     // each feeds four MFMAs.  MFMAs as inline assembly with O tied to its
-    // AGPRs; s_nop 3 covers a VALU write of an operand.
+    // AGPRs; their operands come from LDS reads and registers no VALU
+    // instruction writes right before them (the build checks the wait states).
     auto pv_softmax = [&](int k, const i32x8& ph_own, const i32x8& pl_own, const i32x8& ph_oth,
                           const i32x8& pl_oth, f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out) {
         lds_u8* cur = slot_ptr(k);
@@ -962,13 +1037,13 @@ void decode_fp8_kernel(DecodeParams p) {
         for (int dt = 0; dt < 8; ++dt) {
             const i32x8 a = vf[dt & 1];
             __builtin_amdgcn_sched_barrier(0);
-            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+            asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
                          : "+a"(o0[dt]) : "v"(a), "v"(ph_own));
-            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+            asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
                          : "+a"(o1[dt]) : "v"(a), "v"(ph_oth));
-            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+            asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
                          : "+a"(o0[dt]) : "v"(a), "v"(pl_own));
-            asm volatile("s_nop 3\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+            asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
                          : "+a"(o1[dt]) : "v"(a), "v"(pl_oth));
             if (dt + 2 < 8) vf[dt & 1] = vfrag(cur, dt + 2);
             __builtin_amdgcn_sched_barrier(0);
@@ -1049,7 +1124,7 @@ void decode_fp8_kernel(DecodeParams p) {
     }
 
     // ---- epilogue: o = kv_scale O / l, lse = ln(sum exp(s)) for both tiles of the pair.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     pv_drain();
     const float l_own = pair_sum(l);
     __syncthreads();
@@ -1119,7 +1194,30 @@ __device__ __forceinline__ void merge_row(int n, PartialAt at, void* out, float*
     f32x4 acc0 = (f32x4)0.f, acc1 = (f32x4)0.f;
     float wsum = 0.f;
     if (mx != -INFINITY) {
-        for (int i = 0; i < n; ++i) {
+        // eight partials per step, so that 16 KB of loads per wave are in flight
+        int i = 0;
+        for (; i + 8 <= n; i += 8) {
+            float li[8];
+            f32x4 v0[8], v1[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                li[u] = *at.lse(i + u);
+                const f32x4* src = (const f32x4*)at.out(i + u) + 2 * lane;
+                v0[u] = src[0];
+                v1[u] = src[1];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                // an empty partial (lse -inf) has weight 0 and its output is never used
+                const float wgt = li[u] == -INFINITY ? 0.f : __expf(li[u] - mx);
+                wsum += wgt;
+                if (wgt != 0.f) {
+                    acc0 += wgt * v0[u];
+                    acc1 += wgt * v1[u];
+                }
+            }
+        }
+        for (; i < n; ++i) {
             const float li = *at.lse(i);
             if (li == -INFINITY) continue;
             const float wgt = __expf(li - mx);

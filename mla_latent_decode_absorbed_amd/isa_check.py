@@ -1,0 +1,116 @@
+"""Wait-state check of the generated gfx950 code.
+
+Several MFMAs in the decode kernels are issued as inline assembly (to keep
+the accumulators pinned in their registers).  The compiler does not see
+those MFMAs, so it cannot insert the wait states the matrix cores require
+around them; the kernels insert what they know they need, and this check
+verifies the final instruction stream instead of trusting that:
+
+  * VALU write of a VGPR/AGPR -> MFMA read of it: at least 2 wait states;
+  * MFMA write -> VALU (or v_accvgpr_read) read of the result: at least 18
+    wait states (a 16-pass XDL instruction), and no MFMA result is read by a
+    VALU instruction before that;
+
+where `s_nop N` counts N + 1 wait states and every other instruction one.
+Used by build.py on the device assembly of the kernels source.
+"""
+from __future__ import annotations
+
+import re
+import sys
+
+VALU_TO_MFMA = 2
+MFMA_TO_VALU = 18
+
+
+def _regs(tok: str):
+    tok = tok.strip()
+    m = re.match(r"^([va])\[(\d+):(\d+)\]$", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"^([va])(\d+)$", tok)
+    if m:
+        return {(m.group(1), int(m.group(2)))}
+    return set()
+
+
+def _instructions(lines):
+    out = []
+    for raw in lines:
+        line = raw.split(";")[0].strip()
+        if not line or line.endswith(":") or line.startswith("."):
+            continue
+        out.append(line)
+    return out
+
+
+def _operands(line: str):
+    parts = line.split(None, 1)
+    if len(parts) < 2:
+        return parts[0], []
+    return parts[0], [o.strip() for o in parts[1].split(",")]
+
+
+def _ws(line: str) -> int:
+    op, ops = _operands(line)
+    if op == "s_nop":
+        return int(ops[0], 0) + 1
+    return 1
+
+
+def check_function(lines, name=""):
+    """Return a list of violation strings for one function body."""
+    ins = _instructions(lines)
+    bad = []
+    for i, line in enumerate(ins):
+        op, ops = _operands(line)
+        if op.startswith("v_mfma"):
+            srcs = set().union(*[_regs(o) for o in ops[1:4]]) if len(ops) >= 4 else set()
+            ws, j = 0, i - 1
+            while j >= 0 and ws < VALU_TO_MFMA:
+                pop, pops = _operands(ins[j])
+                if pop.startswith("v_") and not pop.startswith("v_mfma") and pops:
+                    if _regs(pops[0]) & srcs:
+                        bad.append(f"{name}: VALU write {ins[j]!r} -> {line!r} after {ws} wait states")
+                ws += _ws(ins[j])
+                j -= 1
+        elif op.startswith("v_") and ops:
+            reads = set().union(*[_regs(o) for o in ops[1:]])
+            if op.startswith("v_accvgpr_read"):
+                reads = _regs(ops[1])
+            if not reads:
+                continue
+            ws, j = 0, i - 1
+            while j >= 0 and ws < MFMA_TO_VALU:
+                pop, pops = _operands(ins[j])
+                if pop.startswith("v_mfma") and pops and (_regs(pops[0]) & reads):
+                    bad.append(f"{name}: MFMA {ins[j]!r} -> VALU {line!r} after {ws} wait states")
+                    break
+                ws += _ws(ins[j])
+                j -= 1
+    return bad
+
+
+def check_asm(text: str, kernels=("decode_bf16_kernel", "decode_fp8_kernel")):
+    """Check the named kernels in a device assembly listing; returns violations."""
+    lines = text.splitlines()
+    bad = []
+    for kname in kernels:
+        start = None
+        for i, l in enumerate(lines):
+            head = l.split(";")[0].rstrip()
+            if kname in head and head.endswith(":") and not head.startswith("."):
+                start = i
+                break
+        if start is None:
+            bad.append(f"kernel {kname} not found in the assembly")
+            continue
+        end = next(i for i in range(start, len(lines)) if "s_endpgm" in lines[i])
+        bad += check_function(lines[start:end + 1], kname)
+    return bad
+
+
+if __name__ == "__main__":
+    problems = check_asm(open(sys.argv[1]).read())
+    print("\n".join(problems) if problems else "no wait-state violations")
+    sys.exit(1 if problems else 0)

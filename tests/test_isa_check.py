@@ -1,0 +1,59 @@
+"""The wait-state checker used by the build flags the hazards it is meant to
+catch around MFMAs the compiler cannot see, and accepts correctly spaced code."""
+import pytest
+
+from mla_latent_decode_absorbed_amd.isa_check import check_function
+
+pytestmark = pytest.mark.cpu
+
+
+def run(src: str):
+    return check_function(src.strip().splitlines(), "k")
+
+
+def test_valu_write_then_mfma_read_needs_two_wait_states():
+    bad = run("""
+        v_mov_b32_e32 v3, v40
+        v_mfma_f32_32x32x16_bf16 a[0:15], v[2:5], v[6:9], a[0:15]
+    """)
+    assert len(bad) == 1 and "VALU write" in bad[0]
+    assert run("""
+        v_mov_b32_e32 v3, v40
+        s_nop 1
+        v_mfma_f32_32x32x16_bf16 a[0:15], v[2:5], v[6:9], a[0:15]
+    """) == []
+    # an unrelated VALU write right before the MFMA is fine
+    assert run("""
+        v_mov_b32_e32 v30, v40
+        v_mfma_f32_32x32x16_bf16 a[0:15], v[2:5], v[6:9], a[0:15]
+    """) == []
+
+
+def test_accvgpr_write_then_mfma_accumulator_read():
+    bad = run("""
+        v_accvgpr_write_b32 a7, v1
+        v_mfma_f32_32x32x16_bf16 a[0:15], v[2:5], v[6:9], a[0:15]
+    """)
+    assert len(bad) == 1
+
+
+def test_mfma_result_read_by_valu_needs_eighteen_wait_states():
+    bad = run("""
+        v_mfma_f32_32x32x16_bf16 v[10:25], v[2:5], v[6:9], 0
+        s_nop 7
+        v_add_f32_e32 v1, v10, v11
+    """)
+    assert len(bad) == 1 and "MFMA" in bad[0]
+    bad = run("""
+        v_mfma_f32_32x32x16_bf16 a[0:15], v[2:5], v[6:9], a[0:15]
+        s_nop 7
+        v_accvgpr_read_b32 v1, a3
+    """)
+    assert len(bad) == 1
+    assert run("""
+        v_mfma_f32_32x32x16_bf16 v[10:25], v[2:5], v[6:9], 0
+        s_nop 7
+        s_nop 7
+        s_nop 7
+        v_add_f32_e32 v1, v10, v11
+    """) == []

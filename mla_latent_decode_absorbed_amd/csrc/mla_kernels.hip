@@ -79,6 +79,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
     __shared__ long long s_part[32];
     __shared__ int s_scan[1024];
     __shared__ int s_pages[kCached];
+    __shared__ int s_first[kCached];           // first kv-unit of each request (when cached)
     int parity = 0;
     const int tid = threadIdx.x;
     const int per = (p.batch + 1023) / 1024;
@@ -154,9 +155,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
                                        : max(1, (int)((pages + chunk - 1) / chunk));
         req_info[2 * b] = S;
         req_info[2 * b + 1] = base;
+        if (b < kCached) s_first[b] = base;
         base += S;
     }
     __syncthreads();   // req_info of every request written (and visible to the block)
+    auto first_of = [&](int b) { return b < kCached ? s_first[b] : req_info[2 * b + 1]; };
 
     // Work items, one thread per (kv-unit, row tile) slot.  Slot u holds kv-unit
     // k = 8 (u / (8 m_tiles)) + u % 8 and row tile (u / 8) % m_tiles; its
@@ -174,11 +177,11 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
             int lo = 0, hi = p.batch - 1;     // last request whose first kv-unit is <= k
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
-                if (req_info[2 * mid + 1] <= k) lo = mid; else hi = mid - 1;
+                if (first_of(mid) <= k) lo = mid; else hi = mid - 1;
             }
             const int b = lo;
-            const int S = req_info[2 * b];
-            const int s = k - req_info[2 * b + 1];
+            const int s = k - first_of(b);
+            const int S = (b + 1 < p.batch ? first_of(b + 1) : k_total) - first_of(b);
             const int pages = pages_of(b);
             const int cb = p.num_splits > 0 ? (pages + S - 1) / S : (int)chunk;
             w.b = b; w.mt = mt; w.split = s;

@@ -190,11 +190,11 @@ def main(argv=None) -> int:
     # work, so that the clocks have settled before the timed region
     step(0)                      # first call: module load and first-touch costs
     torch.cuda.synchronize()
-    i, t_w = 1, time.perf_counter()
-    while i < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
-        step(i)
-        i += 1
-        if i % 64 == 0:
+    n_warm, t_w = 1, time.perf_counter()
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
+        step(n_warm)
+        n_warm += 1
+        if n_warm % 64 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -241,7 +241,7 @@ def main(argv=None) -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warmup_steps_run": i,
+        "warmup_steps_run": n_warm,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

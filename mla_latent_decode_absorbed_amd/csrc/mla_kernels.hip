@@ -54,34 +54,19 @@ __device__ __forceinline__ int lds_off(int t, int c) { return t * kRowBytes + ((
 // ---------------------------------------------------------------------------
 // plan: per-request split counts and the work list (one workgroup, no host sync)
 // ---------------------------------------------------------------------------
-// Sum (or max) of one value per thread over the 1024-thread block: a
-// wavefront reduction, then the 16 wave results through LDS.  `buf` alternates
-// between two halves so that back-to-back calls need one barrier each.
-__device__ __forceinline__ long long block_reduce(long long v, bool is_max, long long* buf, int& parity) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const long long o = __shfl_xor(v, off);
-        v = is_max ? (o > v ? o : v) : v + o;
-    }
-    long long* half = buf + 16 * parity;
-    parity ^= 1;
-    if ((threadIdx.x & 63) == 0) half[threadIdx.x >> 6] = v;
-    __syncthreads();
-    long long r = half[0];
-    for (int i = 1; i < 16; ++i) r = is_max ? (half[i] > r ? half[i] : r) : r + half[i];
-    return r;
-}
-
 __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t* __restrict__ seq_lens,
                                                     int32_t* __restrict__ req_info,
                                                     WorkItem* __restrict__ work) {
     constexpr int kCached = 8192;            // page counts of up to this many requests stay in LDS
-    __shared__ long long s_part[32];
+    constexpr int kCand = 16;                // chunk sizes counted per round, one per wave
     __shared__ int s_scan[1024];
     __shared__ int s_pages[kCached];
-    __shared__ int s_first[kCached];           // first kv-unit of each request (when cached)
-    int parity = 0;
+    __shared__ int s_first[kCached];         // first kv-unit of each request (when cached)
+    __shared__ unsigned long long s_total[16];   // per-wave partial sums of pages
+    __shared__ int s_longest[16];                // per-wave longest request (pages)
+    __shared__ unsigned int s_cnt[2][kCand];     // kv-units per candidate chunk, two rounds in turn
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
     const int per = (p.batch + 1023) / 1024;
     const int b0 = min(p.batch, tid * per), b1 = min(p.batch, b0 + per);
     const int cap = p.max_pages * kPage;
@@ -89,40 +74,91 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
         const int n = min(max(seq_lens[b], 0), cap);
         return (n + kPage - 1) / kPage;
     };
-    for (int b = tid; b < p.batch && b < kCached; b += 1024) s_pages[b] = pages_global(b);
+    // page counts into LDS, with the total and the longest request on the way
+    // (reduced within each wave by shuffles, then over the 16 wave partials)
+    unsigned long long my_total = 0;
+    int my_longest = 0;
+    for (int b = tid; b < p.batch; b += 1024) {
+        const int pg = pages_global(b);
+        if (b < kCached) s_pages[b] = pg;
+        my_total += (unsigned long long)pg;
+        my_longest = max(my_longest, pg);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        my_total += __shfl_xor(my_total, off);
+        my_longest = max(my_longest, __shfl_xor(my_longest, off));
+    }
+    if (lane == 0) {
+        s_total[wv] = my_total;
+        s_longest[wv] = my_longest;
+    }
     __syncthreads();
     auto pages_of = [&](int b) { return b < kCached ? s_pages[b] : pages_global(b); };
-
-    long long my_pages = 0, my_max = 0;
-    for (int b = b0; b < b1; ++b) {
-        const int pg = pages_of(b);
-        my_pages += pg;
-        my_max = pg > my_max ? pg : my_max;
+    unsigned long long total_pages = 0;
+    int longest = 0;
+    for (int i = 0; i < 16; ++i) {
+        total_pages += s_total[i];
+        longest = max(longest, s_longest[i]);
     }
-    const long long total_pages = block_reduce(my_pages, false, s_part, parity);
-    long long chunk = 1;
+
+    int chunk = 1;
     if (p.num_splits <= 0) {
         // The smallest chunk (in pages) for which every request's splits, times
         // the row tiles, fit in one round of target_units workgroups: the
         // longest unit, and so the kernel, is then as short as this policy
-        // allows.  Binary search between the averaging bound and the longest
-        // request (a batch too large to split keeps one split per request).
-        const long long max_pages = block_reduce(my_max, true, s_part, parity);
+        // allows.  It lies between the averaging bound and the longest request
+        // (any chunk at or past the longest request gives every request one
+        // split, the same work list); when even that does not fit, the longest
+        // request is the chunk.  Each round counts 16 chunk sizes at once, wave
+        // w the w-th: first the 16 sizes from the averaging bound up (the answer
+        // is almost always among them), then 16 sizes spread evenly over what
+        // is left of the range, which shrinks it 16-fold per round.
         const long long units_cap = p.target_units / p.m_tiles > 0 ? p.target_units / p.m_tiles : 1;
-        long long lo = (total_pages + units_cap - 1) / units_cap;
-        lo = lo > p.min_chunk ? lo : p.min_chunk;
-        long long hi = max_pages > lo ? max_pages : lo;
-        while (lo < hi) {
-            const long long mid = (lo + hi) / 2;
-            long long cnt = 0;
-            for (int b = b0; b < b1; ++b) {
-                const long long pg = pages_of(b);
-                cnt += pg > mid ? (pg + mid - 1) / mid : 1;
+        const long long avg = (long long)((total_pages + units_cap - 1) / units_cap);
+        const int hi0 = max(longest, 1);
+        int lo = (int)(avg < hi0 ? avg : hi0);
+        lo = lo > p.min_chunk ? lo : min(p.min_chunk, hi0);
+        int hi = hi0;
+        // kv-units at chunk c >= avg: at most units_cap + batch, so 32 bits hold them
+        auto count = [&](int c) {
+            unsigned int cnt = 0;
+            for (int b = lane; b < p.batch; b += 64) {
+                const unsigned int pg = (unsigned int)pages_of(b);
+                cnt += pg > (unsigned int)c ? (pg + c - 1) / (unsigned int)c : 1u;
             }
-            if (block_reduce(cnt, false, s_part, parity) <= units_cap) hi = mid;
-            else lo = mid + 1;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+            return cnt;
+        };
+        // invariant: the answer is the smallest fitting chunk in [lo, hi], or hi if none fits
+        for (int round = 0;; ++round) {
+            const bool dense = round == 0 || hi - lo < kCand;
+            auto cand = [&](int j) {
+                return dense ? min(lo + j, hi) : lo + (int)((long long)(hi - lo) * (j + 1) / kCand);
+            };
+            unsigned int* cnt = s_cnt[round & 1];
+            const unsigned int mine = count(cand(wv));
+            if (lane == 0) cnt[wv] = mine;
+            __syncthreads();
+            int first = -1;   // first candidate that fits
+            for (int j = kCand - 1; j >= 0; --j)
+                if ((long long)cnt[j] <= units_cap) first = j;
+            if (dense && (hi - lo < kCand || first >= 0)) {
+                chunk = first >= 0 ? cand(first) : hi;
+                break;
+            }
+            if (first < 0) {
+                if (dense) {
+                    lo += kCand;          // lo .. lo + 15 do not fit; go on above them
+                    continue;
+                }
+                chunk = hi;               // hi itself was counted and does not fit
+                break;
+            }
+            lo = first > 0 ? cand(first - 1) + 1 : lo;
+            hi = cand(first);
         }
-        chunk = lo;
     }
 
     // splits per request, and the first kv-unit of each request (exclusive
@@ -130,10 +166,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
     int my_k = 0;
     for (int b = b0; b < b1; ++b) {
         const int pages = pages_of(b);
-        const int S = p.num_splits > 0 ? min(p.num_splits, pages) : (int)((pages + chunk - 1) / chunk);
+        const int S = p.num_splits > 0 ? min(p.num_splits, pages) : (pages + chunk - 1) / chunk;
         my_k += max(S, 1);
     }
-    const int lane = tid & 63, wv = tid >> 6;
     int incl = my_k;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -152,7 +187,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
     for (int b = b0; b < b1; ++b) {
         const int pages = pages_of(b);
         const int S = p.num_splits > 0 ? max(1, min(p.num_splits, pages))
-                                       : max(1, (int)((pages + chunk - 1) / chunk));
+                                       : max(1, (pages + chunk - 1) / chunk);
         req_info[2 * b] = S;
         req_info[2 * b + 1] = base;
         if (b < kCached) s_first[b] = base;
@@ -183,7 +218,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
             const int s = k - first_of(b);
             const int S = (b + 1 < p.batch ? first_of(b + 1) : k_total) - first_of(b);
             const int pages = pages_of(b);
-            const int cb = p.num_splits > 0 ? (pages + S - 1) / S : (int)chunk;
+            const int cb = p.num_splits > 0 ? (pages + S - 1) / S : chunk;
             w.b = b; w.mt = mt; w.split = s;
             w.page_begin = min(pages, s * cb);
             w.page_end = min(pages, (s + 1) * cb);

@@ -61,11 +61,14 @@ struct MergeParams {
     int32_t n, rows, out_bf16;
 };
 
-// Unit index of kv-unit k (one request x split) for M-tile mt: kv-units are
-// dealt to the 8 XCDs round-robin and the m_tiles M-tiles of one kv-unit land
-// on the same XCD in consecutive dispatch slots, so they share its L2.
-__host__ __device__ inline int unit_index(int k, int mt, int m_tiles) {
-    return ((k >> 3) * m_tiles + mt) * 8 + (k & 7);
+// Unit (workgroup) index of kv-unit k (one request x split) for M-tile mt,
+// with per_xcd = ceil(kv-units / 8): dispatch deals workgroups to the 8 XCDs
+// round-robin, and XCD x runs the contiguous kv-units x per_xcd .. + per_xcd - 1
+// with all their M-tiles, so the splits of one request (same query rows) and
+// the M-tiles of one kv-unit (same pages) share that XCD's L2.
+__host__ __device__ inline int unit_index(int k, int mt, int m_tiles, int per_xcd) {
+    const int x = k / per_xcd;
+    return ((k - x * per_xcd) * m_tiles + mt) * 8 + x;
 }
 
 // Upper bound on kv-units (request x split) for a descriptor.

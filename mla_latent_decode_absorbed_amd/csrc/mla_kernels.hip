@@ -196,17 +196,24 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
     __syncthreads();   // req_info of every request written (and visible to the block)
     auto first_of = [&](int b) { return b < kCached ? s_first[b] : req_info[2 * b + 1]; };
 
-    // Work items, one thread per (kv-unit, row tile) slot.  Slot u holds kv-unit
-    // k = 8 (u / (8 m_tiles)) + u % 8 and row tile (u / 8) % m_tiles; its
-    // request is found by binary search over the first kv-unit of each request.
+    // Work items, one thread per (kv-unit, row tile) slot.  Dispatch deals
+    // workgroups to the 8 XCDs round-robin, so slot u runs on XCD u % 8 as its
+    // (u / 8)-th workgroup there.  Each XCD takes a contiguous run of
+    // C = ceil(kv-units / 8) kv-units with all their row tiles: slot u holds
+    // kv-unit k = C (u % 8) + (u / 8) / m_tiles and row tile (u / 8) % m_tiles.
+    // The splits of one request (which read the same query rows) and the row
+    // tiles of one kv-unit (which read the same pages) then share one L2.  The
+    // request of kv-unit k is found by binary search over the first kv-units.
+    const int per_xcd = (k_total + 7) / 8;   // the same value the combine derives from req_info
     for (int u = tid; u < p.units_max; u += 1024) {
-        const int grp = u / (8 * p.m_tiles);
-        const int k = grp * 8 + (u & 7);
-        const int mt = (u >> 3) % p.m_tiles;
+        const int pos = u >> 3;
+        const int kx = pos / p.m_tiles;
+        const int k = per_xcd * (u & 7) + kx;
+        const int mt = pos - kx * p.m_tiles;
         WorkItem w;
         w.pad0 = 0;
         w.pad1 = 0;
-        if (k >= k_total) {
+        if (kx >= per_xcd || k >= k_total) {
             w.b = -1; w.mt = 0; w.split = 0; w.page_begin = 0; w.page_end = 0; w.nsplit = 0;
         } else {
             int lo = 0, hi = p.batch - 1;     // last request whose first kv-unit is <= k
@@ -1285,12 +1292,12 @@ __device__ __forceinline__ void merge_row(int n, PartialAt at, void* out, float*
 struct SplitPartials {
     const float* ws_o;
     const float* ws_lse;
-    int base, mt, m_tiles, rit;
+    int base, mt, m_tiles, per_xcd, rit;
     __device__ const float* lse(int s) const {
-        return ws_lse + (size_t)unit_index(base + s, mt, m_tiles) * kMTile + rit;
+        return ws_lse + (size_t)unit_index(base + s, mt, m_tiles, per_xcd) * kMTile + rit;
     }
     __device__ const float* out(int s) const {
-        return ws_o + ((size_t)unit_index(base + s, mt, m_tiles) * kMTile + rit) * kV;
+        return ws_o + ((size_t)unit_index(base + s, mt, m_tiles, per_xcd) * kMTile + rit) * kV;
     }
 };
 
@@ -1301,7 +1308,9 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     const int r = (int)(grow - (long long)b * p.rows);
     const int S = p.req_info[2 * b];
     if (S <= 1) return;   // a single split wrote the result directly
-    SplitPartials at{p.ws_o, p.ws_lse, p.req_info[2 * b + 1], r / kMTile, p.m_tiles, r % kMTile};
+    const int k_total = p.req_info[2 * (p.batch - 1)] + p.req_info[2 * (p.batch - 1) + 1];
+    SplitPartials at{p.ws_o, p.ws_lse, p.req_info[2 * b + 1], r / kMTile, p.m_tiles, (k_total + 7) / 8,
+                     r % kMTile};
     merge_row(S, at, p.out, p.lse, (size_t)grow, p.out_bf16);
 }
 

@@ -14,9 +14,10 @@ restated below in plain Python:
   and target = min(compute units, 256); if no chunk up to the longest request
   fits, every request gets one split;
 * split s of request b covers pages [min(P, s c), min(P, (s + 1) c));
-* work slot u holds kv-unit k = 8 (u // (8 m_tiles)) + u % 8 (kv-units numbered
-  request by request, split by split) and row tile (u // 8) % m_tiles, or is
-  empty when k is past the last kv-unit.
+* kv-units are numbered request by request, split by split (K in all); with
+  C = ceil(K / 8), work slot u holds kv-unit k = C (u % 8) + (u // 8) // m_tiles
+  and row tile (u // 8) % m_tiles, or is empty when (u // 8) // m_tiles >= C or
+  k >= K (the XCD-contiguous order: slot u runs on XCD u % 8).
 
 The workspace layout read here is the library's internal one: int32 [B][2]
 (splits, first kv-unit) at offset 0, then 32-byte work items (b, mt, split,
@@ -110,16 +111,20 @@ def check(seq_lens, heads, q_len, max_pages, num_splits, what):
     np.testing.assert_array_equal(req[:, 1], first, err_msg=f"{what}: first kv-unit")
     K = len(units)
     assert work.shape[0] >= ((K + 7) // 8) * 8 * m_tiles, f"{what}: work list too short"
+    C = (K + 7) // 8
+    seen = set()
     for u in range(work.shape[0]):
-        k = 8 * (u // (8 * m_tiles)) + u % 8
-        mt = (u // 8) % m_tiles
+        kx, mt = divmod(u // 8, m_tiles)
+        k = C * (u % 8) + kx
         w = work[u]
-        if k >= K:
+        if kx >= C or k >= K:
             assert w[0] == -1, f"{what}: slot {u} should be empty, holds {w.tolist()}"
             continue
         b, s, pb, pe, ns = units[k]
+        seen.add((k, mt))
         assert w.tolist() == [b, mt, s, pb, pe, ns, 0, 0], \
             f"{what}: slot {u} (kv-unit {k}, tile {mt}) = {w.tolist()}, expected {[b, mt, s, pb, pe, ns, 0, 0]}"
+    assert len(seen) == K * m_tiles, f"{what}: {K * m_tiles - len(seen)} (kv-unit, tile) pairs have no slot"
     return S
 
 
@@ -143,7 +148,7 @@ def test_plan_ragged_two_tiles():
 
 def test_plan_one_long_request_bisects():
     """One long request among short ones: the first 16 candidates do not fit, so
-    the planner bisects the rest of the range."""
+    the planner searches the rest of the range (16 spread candidates a round)."""
     S = check([64] * 199 + [100000], 16, 1, 1563, 0, "one long request")
     assert S[-1] > 1 and (S[:-1] == 1).all()
 

@@ -772,9 +772,9 @@ void decode_bf16_kernel(DecodeParams p) {
 //  - the weights enter the PV product as two e4m3 terms, hi = e4m3(w) and
 //    lo = e4m3(w - hi), one MFMA each, so that their error is about 2^-8 of
 //    w instead of the 2^-4 of a single e4m3 rounding (which alone exceeds a
-//    few 1e-2 on short, peaked rows).  Weights are offset by 2^4 so that they
+//    few 1e-2 on short, peaked rows).  Weights are offset by 2^3 so that they
 //    span (0, 2^8]; the reference max takes integer values (log2 units) and
-//    moves once the row max exceeds it by 2^4, so every rescale factor is an
+//    moves once the row max exceeds it by 5, so every rescale factor is an
 //    exact power of two 2^-d.  The pair exchanges hi and lo through LDS; d
 //    (8 bits) rides in the sign bits of hi bytes 0-7, which are free because
 //    the weights are non-negative;
@@ -798,8 +798,8 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 constexpr int kRowBytes8 = kQK;                    // 576 bytes per fp8 cache row
 constexpr int kPageBytes8 = kPage * kRowBytes8;    // 36,864 = one ring slot
 constexpr int kRowChunks8 = kRowBytes8 / 16;       // 36
-constexpr float kRescaleSlack8 = 4.f;              // reference max moves when the max grows by > 2^4
-constexpr float kWeightOffset8 = 4.f;              // weights are exp2(s c - m + 4) <= 2^8 < 448
+constexpr float kRescaleSlack8 = 5.f;              // reference max moves when the max grows by > 2^5
+constexpr float kWeightOffset8 = 3.f;              // weights are exp2(s c - m + 3) <= 2^8 < 448
 constexpr int kPLoOff8 = kRingBytes + 4 * 2048;    // [wave][half][lane] 16 B: lo P^T terms (hi at kPBufOff)
 constexpr int kLdsBytes8 = kPLoOff8 + 4 * 2048;    // 163,840 (the whole LDS)
 static_assert(kPageBytes8 == kSlotBytes, "an fp8 page fills exactly one ring slot");
@@ -1019,44 +1019,66 @@ void decode_fp8_kernel(DecodeParams p) {
     };
     auto needs_mask = [&](int k) { return k * kPage + kPage > nvis_min; };
 
-    // Online softmax of one page for this lane's row (64 tokens, 32 per lane),
-    // in groups that are spread between MFMAs.  Produces the weights as hi/lo
-    // e4m3 operands (bytes 0-15 from tile 0, 16-31 from tile 1) and d_out, the
-    // rescale shift of everything accumulated so far (0 when unchanged).
-    auto softmax_steps = [&](f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out, int g) {
-        if (g == 0) {
-            float mx = fmaxf(s0[0], s1[0]);
+    // Online softmax of one page for this lane's row (64 tokens, 32 per lane)
+    // as 30 small pieces, one after each PV MFMA (a 64-clock MFMA hides about
+    // a dozen VALU instructions; a larger block would leave the matrix core
+    // idle).  Produces the weights as hi/lo e4m3 operands (bytes 0-15 from
+    // tile 0, 16-31 from tile 1) and d_out, the rescale shift of everything
+    // accumulated so far (0 when unchanged).
+    //   j = 0..3   running max over 8 logits each
+    //   j = 4      row max of the pair, reference max, shift, row sum rescale
+    //   j = 5..28  4 groups of 8 logits (s0[0..7], s0[8..15], s1[0..7], s1[8..15]),
+    //              6 pieces each: exp2 of 4 + 4, then per 4 weights the hi
+    //              code (and its value), then the lo code
+    //   j = 29     row sum, publish
+    struct SoftmaxState {
+        float mx, mneg, sum;
+        int hw;
+        float h0, h1, h2, h3;
+    };
+    auto softmax_piece = [&](f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out, SoftmaxState& st,
+                             int j) {
+        if (j < 4) {
+            f32x16& s = j < 2 ? s0 : s1;
+            const int i0 = (j & 1) * 8;
+            float mx = j == 0 ? s[0] : fmaxf(st.mx, s[i0]);
 #pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-            mx = pair_max(mx) * c_exp;
+            for (int i = i0 + 1; i < i0 + 8; ++i) mx = fmaxf(mx, s[i]);
+            st.mx = mx;
+        } else if (j == 4) {
+            const float mx = pair_max(st.mx) * c_exp;
             const bool grow = mx > m + kRescaleSlack8;
             const float m_new = grow ? __builtin_ceilf(mx) : m;
             // (nothing has been accumulated while m is still -inf: no rescale)
             d_out = grow && m != -INFINITY ? (int)fminf(m_new - m, 255.f) : 0;
             m = m_new;
             l *= __builtin_ldexpf(1.f, -d_out);
-        } else if (g >= 1 && g <= 4) {
-            const float mneg = m == -INFINITY ? 0.f : kWeightOffset8 - m;
-            f32x16& s = g <= 2 ? s0 : s1;
-            const int i0 = ((g - 1) & 1) * 8;
-            float sum = 0.f;
+            st.mneg = m == -INFINITY ? 0.f : kWeightOffset8 - m;
+            st.sum = 0.f;
+        } else if (j < 29) {
+            const int g = (j - 5) / 6, part = (j - 5) % 6;
+            f32x16& s = g < 2 ? s0 : s1;
+            const int i0 = (g & 1) * 8;
+            if (part < 2) {
 #pragma unroll
-            for (int i = i0; i < i0 + 8; ++i) {
-                s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_exp, mneg));
-                sum += s[i];
+                for (int i = i0 + 4 * part; i < i0 + 4 * part + 4; ++i) {
+                    s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_exp, st.mneg));
+                    st.sum += s[i];
+                }
+            } else {
+                const int q = (part - 2) >> 1, i = i0 + 4 * q, r = 2 * g + q;
+                if (((part - 2) & 1) == 0) {
+                    st.hw = pack_e4m3(s[i], s[i + 1], s[i + 2], s[i + 3]);
+                    const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(st.hw, false);
+                    const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(st.hw, true);
+                    st.h0 = h01[0]; st.h1 = h01[1]; st.h2 = h23[0]; st.h3 = h23[1];
+                    ph[r] = st.hw;
+                } else {
+                    pl[r] = pack_e4m3(s[i] - st.h0, s[i + 1] - st.h1, s[i + 2] - st.h2, s[i + 3] - st.h3);
+                }
             }
-            l += sum;
-            const int r0 = (g - 1) * 2;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int i = i0 + 4 * q;
-                const int hw = pack_e4m3(s[i], s[i + 1], s[i + 2], s[i + 3]);
-                const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
-                const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
-                ph[r0 + q] = hw;
-                pl[r0 + q] = pack_e4m3(s[i] - h01[0], s[i + 1] - h01[1], s[i + 2] - h23[0], s[i + 3] - h23[1]);
-            }
-        } else if (g == 5) {
+        } else if (j == 29) {
+            l += st.sum;
             // publish (d in the sign bits of hi bytes 0-7; the own operand stays clean)
             const int e0 = ph[0] | spread_nibble(d_out), e1 = ph[1] | spread_nibble(d_out >> 4);
             *(lds_i32x4*)pbuf_mine = (i32x4){e0, e1, ph[2], ph[3]};
@@ -1067,32 +1089,36 @@ void decode_fp8_kernel(DecodeParams p) {
     };
 
     // O^T += V^T . (P_hi + P_lo)^T over page k for both tiles of the pair (8
-    // dim tiles x 2 row tiles x 2 terms), with the softmax of page k + 1
-    // spread between the MFMA groups.  V^T fragments are read two ahead and
-    // each feeds four MFMAs.  MFMAs as inline assembly with O tied to its
-    // AGPRs; their operands come from LDS reads and registers no VALU
-    // instruction writes right before them (the build checks the wait states).
+    // dim tiles x 2 row tiles x 2 terms), with the softmax of page k + 1 in
+    // pieces between the MFMAs.  V^T fragments are read two ahead and each
+    // feeds four MFMAs.  MFMAs as inline assembly with O tied to its AGPRs;
+    // their operands come from LDS reads and registers no VALU instruction
+    // writes right before them (the build checks the wait states).
     auto pv_softmax = [&](int k, const i32x8& ph_own, const i32x8& pl_own, const i32x8& ph_oth,
                           const i32x8& pl_oth, f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out) {
         lds_u8* cur = slot_ptr(k);
         i32x8 vf[2];
         vf[0] = vfrag(cur, 0);
         vf[1] = vfrag(cur, 1);
+        SoftmaxState st;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             const i32x8 a = vf[dt & 1];
-            __builtin_amdgcn_sched_barrier(0);
-            asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
-                         : "+a"(o0[dt]) : "v"(a), "v"(ph_own));
-            asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
-                         : "+a"(o1[dt]) : "v"(a), "v"(ph_oth));
-            asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
-                         : "+a"(o0[dt]) : "v"(a), "v"(pl_own));
-            asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
-                         : "+a"(o1[dt]) : "v"(a), "v"(pl_oth));
-            if (dt + 2 < 8) vf[dt & 1] = vfrag(cur, dt + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            if (dt < 6) softmax_steps(s0, s1, ph, pl, d_out, dt);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (q == 0)
+                    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(o0[dt]) : "v"(a), "v"(ph_own));
+                else if (q == 1)
+                    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(o1[dt]) : "v"(a), "v"(ph_oth));
+                else if (q == 2)
+                    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(o0[dt]) : "v"(a), "v"(pl_own));
+                else
+                    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(o1[dt]) : "v"(a), "v"(pl_oth));
+                if (q == 3 && dt + 2 < 8) vf[dt & 1] = vfrag(cur, dt + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                softmax_piece(s0, s1, ph, pl, d_out, st, 4 * dt + q);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -1122,8 +1148,9 @@ void decode_fp8_kernel(DecodeParams p) {
             f32x16 s0, s1;
             qk(k, s0, s1, [&](int) {});
             if (needs_mask(k)) mask_s(k, s0, s1);
+            SoftmaxState st;
 #pragma unroll
-            for (int g = 0; g < 6; ++g) softmax_steps(s0, s1, ph_cur, pl_cur, d_cur, g);
+            for (int j = 0; j < 30; ++j) softmax_piece(s0, s1, ph_cur, pl_cur, d_cur, st, j);
         }
         // top of iteration k: page k + 1 landed, P(k) of both waves visible,
         // every wave past its reads of page k - 1; the partner's P(k) terms and

@@ -353,26 +353,15 @@ void decode_bf16_kernel(DecodeParams p) {
         const int pc = qc - t * kRowChunks;
         cp_off[j] = t * kRowBytes + ((pc ^ swz(t)) << 4);
     }
-    // Page ids: lane i holds block-table entry page_begin + 64 g + i of the
-    // current group g (bt_cur) and of group g + 1 (bt_nxt, loaded a group
-    // ahead), so a copy never waits for a block-table load.
-    int bt_grp = 0;
-    auto bt_load = [&](int g) {
-        const int pg = w.page_begin + 64 * g + lane;
-        return pg < w.page_end ? bt[pg] : 0;
-    };
-    int bt_cur = bt_load(0);
-    int bt_nxt = bt_load(1);
-    auto half_src = [&](int k) {
-        const int rel = (k >> 1) - w.page_begin;
-        while ((rel >> 6) > bt_grp) {       // entering the next group of 64 pages
-            bt_cur = bt_nxt;
-            ++bt_grp;
-            bt_nxt = bt_load(bt_grp + 1);
-        }
-        const int pid = __builtin_amdgcn_readlane(bt_cur, rel & 63);
-        return kvbase + (size_t)pid * kPageBytes + (k & 1) * kSlotBytes;
-    };
+    // Page ids come through the scalar unit (the block table is read-only
+    // while the kernel runs, and a page id is the same for the whole wave):
+    // scalar loads are counted by lgkmcnt, so waiting for a page id never
+    // waits for the HBM -> LDS copies in flight, which vmcnt counts.  Callers
+    // pass half pages inside [half_begin, half_end).
+    const __attribute__((address_space(4))) int32_t* bt_s = (const __attribute__((address_space(4))) int32_t*)bt;
+    auto page_id = [&](int k) { return bt_s[k >> 1]; };
+    auto half_src_of = [&](int pid, int k) { return kvbase + (size_t)pid * kPageBytes + (k & 1) * kSlotBytes; };
+    auto half_src = [&](int k) { return half_src_of(page_id(k), k); };
     auto slot_addr = [&](int k) { return ring_addr + ((k - half_begin) & 3) * kSlotBytes; };
     auto slot_ptr = [&](int k) { return ring + ((k - half_begin) & 3) * kSlotBytes; };
     auto issue_copy = [&](int k, int j, const uint8_t* src) {
@@ -550,30 +539,38 @@ void decode_bf16_kernel(DecodeParams p) {
     };
 
     // O^T += V^T . P^T over half page k for all four row tiles, with the
-    // softmax of half page k + 1 spread between its MFMA groups so that the
-    // exp/max/convert work runs while the matrix cores are busy
-    // (sched_barrier(0) pins the order of the groups).  Each of the 8 V^T
-    // fragments (2 k-steps x 4 dim tiles) feeds four MFMAs; fragments are read
-    // four ahead.  The MFMAs are inline assembly with O tied to its
-    // accumulation registers, so the compiler never moves O out of the AGPRs.
-    // Their operands come straight from LDS reads (no VALU write precedes an
-    // MFMA read, which would need 2 wait states the compiler does not know to
-    // insert); the build scans the generated code for such a pair.
-    auto pv_softmax = [&](int k, const bf16x8_t (&pa)[4][2], f32x16& s, bf16x8_t (&pf)[2], float& alpha_out) {
+    // softmax of half page k + 1 cut into small pieces, one after each MFMA:
+    // a 32-clock MFMA hides about four VALU instructions, so the exp/max/
+    // convert work runs while the matrix core is busy (sched_barrier(0) pins
+    // the order).  Pieces: j = 0..3 running max over 4 logits each; 4 row max
+    // of the pair; 5 reference max, rescale factor, row sum rescale; 6..21
+    // one exp2 each; 22..25 bf16 conversion of 4 weights each; 26 row sum and
+    // publish.  Each of the 8 V^T fragments (2 k-steps x 4 dim tiles) feeds
+    // four MFMAs; fragments are read four ahead.  The MFMAs are inline
+    // assembly with O tied to its accumulation registers, so the compiler
+    // never moves O out of the AGPRs.  Their operands come straight from LDS
+    // reads (no VALU write precedes an MFMA read, which would need 2 wait
+    // states the compiler does not know to insert); the build scans the
+    // generated code for such a pair.
+    auto pv_softmax = [&](int k, const bf16x8_t (&pa)[4][2], const bf16x8_t (&vpre)[2], f32x16& s,
+                          bf16x8_t (&pf)[2], float& alpha_out) {
         lds_u8* cur = slot_ptr(k);
         constexpr int kVAhead = 4;
         bf16x8_t vf[kVAhead];
-#pragma unroll
-        for (int i = 0; i < kVAhead; ++i) vf[i] = vfrag(cur, i);
+        vf[0] = vpre[0];
+        vf[1] = vpre[1];
+        vf[2] = vfrag(cur, 2);
+        vf[3] = vfrag(cur, 3);
         float mx, mneg, sum0 = 0.f, sum1 = 0.f;
         const float c = p.scale_log2;
-        auto chunk = [&](int g) {
-            if (g == 0) {
-                mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-#pragma unroll
-                for (int i = 4; i < 16; ++i) mx = fmaxf(mx, s[i]);
-            } else if (g == 1) {
+        auto piece = [&](int j) {
+            if (j < 4) {
+                const int i = 4 * j;
+                const float v = fmaxf(fmaxf(s[i], s[i + 1]), fmaxf(s[i + 2], s[i + 3]));
+                mx = j == 0 ? v : fmaxf(mx, v);
+            } else if (j == 4) {
                 mx = pair_max(mx) * c;
+            } else if (j == 5) {
                 const bool grow = mx > m + kRescaleSlack;
                 const float m_new = grow ? mx : m;
                 // (nothing has been accumulated while m is still -inf: no rescale)
@@ -581,23 +578,17 @@ void decode_bf16_kernel(DecodeParams p) {
                 m = m_new;
                 mneg = m == -INFINITY ? 0.f : -m;
                 l *= alpha_out;
-            } else if (g >= 2 && g < 6) {
-                const int i = 4 * (g - 2);
+            } else if (j < 22) {
+                const int i = j - 6;
+                s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, mneg));
+                if (i & 1) sum1 += s[i];
+                else sum0 += s[i];
+            } else if (j < 26) {
+                const int h = (j - 22) >> 1, e0 = 4 * ((j - 22) & 1);
 #pragma unroll
-                for (int u = 0; u < 4; u += 2) {
-                    s[i + u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + u], c, mneg));
-                    s[i + u + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + u + 1], c, mneg));
-                    sum0 += s[i + u];
-                    sum1 += s[i + u + 1];
-                }
-            } else if (g == 6) {
+                for (int e = e0; e < e0 + 4; ++e) pf[h][e] = (__bf16)s[8 * h + e];
+            } else if (j == 26) {
                 l += sum0 + sum1;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pf[0][e] = (__bf16)s[e];
-                    pf[1][e] = (__bf16)s[8 + e];
-                }
-            } else if (g == 7) {
                 *(lds_bf16x8*)pbuf_mine = pf[0];
                 *(lds_bf16x8*)(pbuf_mine + 1024) = pf[1];
                 *abuf_mine = alpha_out;
@@ -607,14 +598,20 @@ void decode_bf16_kernel(DecodeParams p) {
         for (int i = 0; i < 8; ++i) {
             const bf16x8_t a = vf[i % kVAhead];
             const int k2 = i >> 2, dq = i & 3;
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int t = 0; t < 4; ++t) {
+                __builtin_amdgcn_sched_barrier(0);
                 asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                              : "+a"(o[t][dq]) : "v"(a), "v"(pa[t][k2]));
-            if (i + kVAhead < 8) vf[i % kVAhead] = vfrag(cur, i + kVAhead);
-            __builtin_amdgcn_sched_barrier(0);
-            chunk(i);
+                if (t == 3 && i + kVAhead < 8) vf[i % kVAhead] = vfrag(cur, i + kVAhead);
+                // Every wave has consumed all of P(k) (its second k-step feeds
+                // the MFMAs from here on), so once all waves are past this
+                // point P(k+1) may overwrite it (piece 26).  The barrier needs
+                // no LDS wait: the reads of P(k) have returned.
+                if (i == 4 && t == 0) __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                piece(4 * i + t);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -651,8 +648,17 @@ void decode_bf16_kernel(DecodeParams p) {
         // Top of iteration k: the copies of half page k + 1 have landed, P(k)
         // of every wave is visible, and every wave is past its reads of half
         // page k - 1 (whose slot the next copy refills).
+        // copy source of iteration k: half page k + 3, or past the end of the
+        // range half page k again (into the dead slot of k - 1: a cache hit
+        // that keeps the loop body free of branches)
+        auto copy_half = [&](int k) { return k + 3 < half_end ? k + 3 : min(k, half_end - 1); };
+        int pid_copy;
+        // (the page id of iteration k's copy is loaded right before the
+        // barrier, whose lgkmcnt(0) covers the scalar load: no scalar load is
+        // then pending when the QK^T waits for its LDS reads)
         auto enter = [&](int k) {
             wait_copies(k + 2 < half_end ? 1 : 0);
+            pid_copy = page_id(copy_half(k));
             lds_sync();
             if (k + 1 < half_end) zero_tail(k + 1);
         };
@@ -673,17 +679,19 @@ void decode_bf16_kernel(DecodeParams p) {
         // then the PV of half page k interleaved with the softmax of k + 1.
         for (;;) {
             f32x16 s;
-            // copy of half page k + 3 into the slot of k - 1; past the end of
-            // the range that slot is dead and receives half page k again (a
-            // cache hit that keeps this block free of branches)
-            const int kc = k + 3 < half_end ? k + 3 : k;
-            const uint8_t* csrc_w = half_src(kc) + wave * 8 * kRowBytes;
+            const uint8_t* csrc_w = half_src_of(pid_copy, copy_half(k)) + wave * 8 * kRowBytes;
             const uint32_t cdst = slot_addr(k + 3) + wave * 9 * 1024;
+            // (the first two V^T fragments of half page k are read while the
+            // last QK^T MFMA runs)
+            bf16x8_t vpre[2];
             qk(k + 1, s, [&](int j) {
                 dma16(cdst + j * 1024, csrc_w, (uint32_t)cp_off[j]);
                 if (j == 7) read_p();
+                if (j == 8) {
+                    vpre[0] = vfrag(slot_ptr(k), 0);
+                    vpre[1] = vfrag(slot_ptr(k), 1);
+                }
             });
-            lds_sync();   // every wave has read P(k): it may be overwritten
             if (__builtin_expect(__any(av[0] != 1.f || av[1] != 1.f || av[2] != 1.f || av[3] != 1.f), 0)) {
                 // a row max moved: rescale what the tile has accumulated so far
                 pv_drain();
@@ -692,7 +700,7 @@ void decode_bf16_kernel(DecodeParams p) {
             }
             if (needs_mask(k + 1)) mask_s(k + 1, s);
             float a_nxt;
-            pv_softmax(k, pa, s, pf_nxt, a_nxt);
+            pv_softmax(k, pa, vpre, s, pf_nxt, a_nxt);
             if (k + 1 >= half_end) break;
             ++k;
             enter(k);
@@ -866,23 +874,11 @@ void decode_fp8_kernel(DecodeParams p) {
         const int pc = qc - t * kRowChunks8;
         cp_off[j] = t * kRowBytes8 + ((pc ^ swz8(t)) << 4);
     }
-    int bt_grp = 0;
-    auto bt_load = [&](int g) {
-        const int pg = w.page_begin + 64 * g + lane;
-        return pg < w.page_end ? bt[pg] : 0;
-    };
-    int bt_cur = bt_load(0);
-    int bt_nxt = bt_load(1);
-    auto page_src = [&](int k) {
-        const int rel = k - w.page_begin;
-        while ((rel >> 6) > bt_grp) {
-            bt_cur = bt_nxt;
-            ++bt_grp;
-            bt_nxt = bt_load(bt_grp + 1);
-        }
-        const int pid = __builtin_amdgcn_readlane(bt_cur, rel & 63);
-        return kvbase + (size_t)pid * kPageBytes8;
-    };
+    // page ids through the scalar unit (see the bf16 kernel); callers pass
+    // pages inside [pg_begin, pg_end)
+    const __attribute__((address_space(4))) int32_t* bt_s = (const __attribute__((address_space(4))) int32_t*)bt;
+    auto page_src_of = [&](int pid) { return kvbase + (size_t)pid * kPageBytes8; };
+    auto page_src = [&](int k) { return page_src_of(bt_s[k]); };
     auto slot_addr = [&](int k) { return ring_addr + ((k - pg_begin) & 3) * kSlotBytes; };
     auto slot_ptr = [&](int k) { return ring + ((k - pg_begin) & 3) * kSlotBytes; };
 #pragma unroll
@@ -1155,8 +1151,14 @@ void decode_fp8_kernel(DecodeParams p) {
         // top of iteration k: page k + 1 landed, P(k) of both waves visible,
         // every wave past its reads of page k - 1; the partner's P(k) terms and
         // rescale shift are read here and first used after the QK^T
+        // copy source of iteration k: page k + 3, or past the end of the range
+        // page k again (into the dead slot of k - 1); its page id is loaded
+        // right before the barrier (see the bf16 kernel)
+        auto copy_page = [&](int k) { return k + 3 < pg_end ? k + 3 : min(k, pg_end - 1); };
+        int pid_copy;
         auto enter = [&](int k) {
             wait_copies(k + 2 < pg_end ? 1 : 0);
+            pid_copy = bt_s[copy_page(k)];
             lds_sync();
             if (k + 1 < pg_end) zero_tail(k + 1);
             const i32x4 h0 = *(const lds_i32x4*)pbuf_other;
@@ -1171,10 +1173,7 @@ void decode_fp8_kernel(DecodeParams p) {
         enter(k);
         for (;;) {
             f32x16 s0, s1;
-            // copy of page k + 3 into the slot of k - 1 (past the end of the
-            // range: page k again into that dead slot)
-            const int kc = k + 3 < pg_end ? k + 3 : k;
-            const uint8_t* csrc_w = page_src(kc) + wave * 16 * kRowBytes8;
+            const uint8_t* csrc_w = page_src_of(pid_copy) + wave * 16 * kRowBytes8;
             const uint32_t cdst = slot_addr(k + 3) + wave * 9 * 1024;
             qk(k + 1, s0, s1, [&](int j) { dma16(cdst + j * 1024, csrc_w, (uint32_t)cp_off[j]); });
             lds_sync();   // the partner has read P(k): it may be overwritten

@@ -1112,6 +1112,11 @@ void decode_fp8_kernel(DecodeParams p) {
                 else
                     asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(o1[dt]) : "v"(a), "v"(pl_oth));
                 if (q == 3 && dt + 2 < 8) vf[dt & 1] = vfrag(cur, dt + 2);
+                // Both waves of the pair have consumed the other's P(k) terms
+                // (the MFMAs above took them), so once both are past this
+                // point P(k+1) may overwrite them (piece 29).  No LDS wait is
+                // needed: those reads have returned.
+                if (dt == 0 && q == 3) __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_sched_barrier(0);
                 softmax_piece(s0, s1, ph, pl, d_out, st, 4 * dt + q);
             }
@@ -1149,9 +1154,8 @@ void decode_fp8_kernel(DecodeParams p) {
             for (int j = 0; j < 30; ++j) softmax_piece(s0, s1, ph_cur, pl_cur, d_cur, st, j);
         }
         // top of iteration k: page k + 1 landed, P(k) of both waves visible,
-        // every wave past its reads of page k - 1; the partner's P(k) terms and
-        // rescale shift are read here and first used after the QK^T
-        // copy source of iteration k: page k + 3, or past the end of the range
+        // every wave past its reads of page k - 1.
+        // Copy source of iteration k: page k + 3, or past the end of the range
         // page k again (into the dead slot of k - 1); its page id is loaded
         // right before the barrier (see the bf16 kernel)
         auto copy_page = [&](int k) { return k + 3 < pg_end ? k + 3 : min(k, pg_end - 1); };
@@ -1161,6 +1165,10 @@ void decode_fp8_kernel(DecodeParams p) {
             pid_copy = bt_s[copy_page(k)];
             lds_sync();
             if (k + 1 < pg_end) zero_tail(k + 1);
+        };
+        // the partner's P(k) terms and rescale shift (published before the
+        // top-of-step barrier), read late in the QK^T of page k + 1
+        auto read_partner = [&]() {
             const i32x4 h0 = *(const lds_i32x4*)pbuf_other;
             const i32x4 h1 = *(const lds_i32x4*)(pbuf_other + 1024);
             const i32x4 l0 = *(const lds_i32x4*)plo_other;
@@ -1175,8 +1183,10 @@ void decode_fp8_kernel(DecodeParams p) {
             f32x16 s0, s1;
             const uint8_t* csrc_w = page_src_of(pid_copy) + wave * 16 * kRowBytes8;
             const uint32_t cdst = slot_addr(k + 3) + wave * 9 * 1024;
-            qk(k + 1, s0, s1, [&](int j) { dma16(cdst + j * 1024, csrc_w, (uint32_t)cp_off[j]); });
-            lds_sync();   // the partner has read P(k): it may be overwritten
+            qk(k + 1, s0, s1, [&](int j) {
+                dma16(cdst + j * 1024, csrc_w, (uint32_t)cp_off[j]);
+                if (j == 6) read_partner();
+            });
             if (__builtin_expect(__any(d_cur != 0 || d_oth != 0), 0)) {
                 pv_drain();
                 scale_acc(o0, __builtin_ldexpf(1.f, -d_cur));

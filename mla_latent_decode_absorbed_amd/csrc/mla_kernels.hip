@@ -367,14 +367,17 @@ void decode_bf16_kernel(DecodeParams p) {
     auto issue_copy = [&](int k, int j, const uint8_t* src) {
         dma16(slot_addr(k) + wave * 9 * 1024 + j * 1024, src + wave * 8 * kRowBytes, (uint32_t)cp_off[j]);
     };
-    // prologue: three half pages in flight before the query loads
-#pragma unroll
-    for (int j3 = 0; j3 < 3; ++j3)
+    // prologue: the first half page, then the query, then two more half
+    // pages.  Loads retire in issue order, so the first QK^T (which needs the
+    // first half page and the query) does not wait for the other two.
+    auto issue_half = [&](int j3) {
         if (half_begin + j3 < half_end) {
             const uint8_t* src = half_src(half_begin + j3);
 #pragma unroll
             for (int j = 0; j < 9; ++j) issue_copy(half_begin + j3, j, src);
         }
+    };
+    issue_half(0);
 
     // this lane's query row, its visible length, and its Q^T fragments:
     // k-step ks covers dims 16 ks .. + 15, lane holds dims 16 ks + 8 G .. + 7
@@ -396,6 +399,8 @@ void decode_bf16_kernel(DecodeParams p) {
 #pragma unroll
         for (int ks = 0; ks < 36; ++ks) qf[ks] = *(const bf16x8_t*)(qr + 16 * ks);
     }
+    issue_half(1);
+    issue_half(2);
 
     // LDS read offsets within a slot.  QK: token lr, chunk c(ks) = 2 ks + G at
     // position (c & ~7) | ((c ^ swz(lr)) & 7); c(ks + 4) = c(ks) + 8, so four
@@ -553,7 +558,7 @@ void decode_bf16_kernel(DecodeParams p) {
     // states the compiler does not know to insert); the build scans the
     // generated code for such a pair.
     auto pv_softmax = [&](int k, const bf16x8_t (&pa)[4][2], const bf16x8_t (&vpre)[2], f32x16& s,
-                          bf16x8_t (&pf)[2], float& alpha_out) {
+                          bf16x8_t (&pf)[2], float& alpha_out, auto&& enter_next) {
         lds_u8* cur = slot_ptr(k);
         constexpr int kVAhead = 4;
         bf16x8_t vf[kVAhead];
@@ -581,8 +586,15 @@ void decode_bf16_kernel(DecodeParams p) {
             } else if (j < 22) {
                 const int i = j - 6;
                 s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, mneg));
-                if (i & 1) sum1 += s[i];
-                else sum0 += s[i];
+                // (the empty asm keeps each add here, between the MFMAs; the
+                // compiler would otherwise sink the whole sum to the loop end)
+                if (i & 1) {
+                    sum1 += s[i];
+                    asm volatile("" : "+v"(sum1));
+                } else {
+                    sum0 += s[i];
+                    asm volatile("" : "+v"(sum0));
+                }
             } else if (j < 26) {
                 const int h = (j - 22) >> 1, e0 = 4 * ((j - 22) & 1);
 #pragma unroll
@@ -609,6 +621,9 @@ void decode_bf16_kernel(DecodeParams p) {
                 // point P(k+1) may overwrite it (piece 26).  The barrier needs
                 // no LDS wait: the reads of P(k) have returned.
                 if (i == 4 && t == 0) __builtin_amdgcn_s_barrier();
+                // the top-of-step barrier of the next half page, once P(k+1)
+                // is published (piece 26): the wait overlaps the last MFMAs
+                if (i == 7 && t == 0) enter_next();
                 __builtin_amdgcn_sched_barrier(0);
                 piece(4 * i + t);
             }
@@ -656,10 +671,13 @@ void decode_bf16_kernel(DecodeParams p) {
         // (the page id of iteration k's copy is loaded right before the
         // barrier, whose lgkmcnt(0) covers the scalar load: no scalar load is
         // then pending when the QK^T waits for its LDS reads)
-        auto enter = [&](int k) {
+        auto enter_sync = [&](int k) {
             wait_copies(k + 2 < half_end ? 1 : 0);
             pid_copy = page_id(copy_half(k));
             lds_sync();
+        };
+        auto enter = [&](int k) {
+            enter_sync(k);
             if (k + 1 < half_end) zero_tail(k + 1);
         };
         // P(k) of all four tiles and their rescale factors, read late in the
@@ -700,10 +718,15 @@ void decode_bf16_kernel(DecodeParams p) {
             }
             if (needs_mask(k + 1)) mask_s(k + 1, s);
             float a_nxt;
-            pv_softmax(k, pa, vpre, s, pf_nxt, a_nxt);
-            if (k + 1 >= half_end) break;
+            // (the top of iteration k + 1 runs inside the PV, after P(k + 1) is
+            // published; only the rare zeroing of a sequence tail stays here)
+            const bool more = k + 1 < half_end;
+            pv_softmax(k, pa, vpre, s, pf_nxt, a_nxt, [&]() {
+                if (more) enter_sync(k + 1);
+            });
+            if (!more) break;
             ++k;
-            enter(k);
+            if (k + 1 < half_end) zero_tail(k + 1);
         }
     }
 
@@ -881,14 +904,16 @@ void decode_fp8_kernel(DecodeParams p) {
     auto page_src = [&](int k) { return page_src_of(bt_s[k]); };
     auto slot_addr = [&](int k) { return ring_addr + ((k - pg_begin) & 3) * kSlotBytes; };
     auto slot_ptr = [&](int k) { return ring + ((k - pg_begin) & 3) * kSlotBytes; };
-#pragma unroll
-    for (int j3 = 0; j3 < 3; ++j3)
+    // prologue: the first page, the query, then two more pages (see the bf16 kernel)
+    auto issue_page = [&](int j3) {
         if (pg_begin + j3 < pg_end) {
             const uint8_t* src = page_src(pg_begin + j3) + wave * 16 * kRowBytes8;
             const uint32_t dst = slot_addr(pg_begin + j3) + wave * 9 * 1024;
 #pragma unroll
             for (int j = 0; j < 9; ++j) dma16(dst + j * 1024, src, (uint32_t)cp_off[j]);
         }
+    };
+    issue_page(0);
 
     const int row = w.mt * kMTile + wave * 32 + lr;
     const bool row_ok = row < p.rows;
@@ -907,6 +932,8 @@ void decode_fp8_kernel(DecodeParams p) {
             qf[ks] = cat8(lo, hi);
         }
     }
+    issue_page(1);
+    issue_page(2);
     // QK A fragments: token 32 tau + lr, chunks 4 ks + 2 G + e (e = 0, 1) at
     // positions 4 ks + ((2 G + e) ^ swz8(lr)): two bases, immediates 64 ks and
     // 32 rows (18,432 bytes) per token tile

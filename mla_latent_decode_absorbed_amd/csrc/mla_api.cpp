@@ -105,7 +105,10 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     pp.target_units = target_units_for_current_device();
     pp.min_chunk = mla::kMinChunkPages;
     pp.units_max = (int32_t)L.units_max;
-    if (mla::launch_plan(pp, seq_lens, req_info, work, s) != hipSuccess) return MLA_ERR_HIP;
+    // small batches: every decode workgroup plans the splits itself (one
+    // launch fewer); larger ones: one planner workgroup writes the work list
+    const bool fused_plan = d->batch <= mla::kFusedPlanMax;
+    if (!fused_plan && mla::launch_plan(pp, seq_lens, req_info, work, s) != hipSuccess) return MLA_ERR_HIP;
 
     mla::DecodeParams dp;
     dp.q = q;
@@ -114,6 +117,10 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     dp.block_table = block_table;
     dp.seq_lens = seq_lens;
     dp.work = work;
+    dp.work_out = work;
+    dp.req_info = req_info;
+    dp.plan = pp;
+    dp.fused_plan = fused_plan ? 1 : 0;
     dp.out = out;
     dp.lse = lse;
     dp.ws_o = (float*)(ws + L.ws_o);

@@ -13,6 +13,7 @@ constexpr int kPage = 64;         // tokens per cache page
 constexpr int kMTile = 128;       // query rows per decode workgroup (heads x query tokens)
 constexpr int kTargetUnits = 256; // automatic split: at most this many workgroups (one per CU)
 constexpr int kMinChunkPages = 2; // smallest automatic split, in pages
+constexpr int kFusedPlanMax = 256; // batches up to this size are planned inside the decode kernel
 
 // One unit of split-KV work: rows [mt*kMTile, +kMTile) of request b over the
 // pages [page_begin, page_end) of its block table.  b < 0 marks an empty slot.
@@ -30,7 +31,11 @@ struct DecodeParams {
     const float* kv_scale;      // fp8 only: device float, the per-tensor cache scale
     const int32_t* block_table; // [B][max_pages]
     const int32_t* seq_lens;    // [B]
-    const WorkItem* work;       // [units_max]
+    const WorkItem* work;       // [units_max] (read when fused_plan == 0)
+    WorkItem* work_out;         // the same list (written when fused_plan == 1, one item per workgroup)
+    int32_t* req_info;          // [B][2] (written by workgroup 0 when fused_plan == 1)
+    PlanParams plan;            // the planner's inputs (fused_plan == 1)
+    int32_t fused_plan;         // 1: every workgroup plans the splits itself (batch <= kFusedPlanMax)
     void* out;                  // [B][M][512] of out_dtype
     float* lse;                 // [B][M]
     float* ws_o;                // [units_max][kMTile][512]

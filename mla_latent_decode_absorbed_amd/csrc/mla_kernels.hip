@@ -52,54 +52,101 @@ __device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 
 __device__ __forceinline__ int lds_off(int t, int c) { return t * kRowBytes + ((c ^ swz(t)) << 4); }
 
 // ---------------------------------------------------------------------------
-// plan: per-request split counts and the work list (one workgroup, no host sync)
+// split planner: per-request split counts, first kv-units and work items,
+// from seq_lens on the device (no host sync).  plan_splits runs on one block
+// of NT threads over LDS scratch the caller provides.  plan_kernel runs it
+// once (one 1024-thread workgroup) and writes the whole work list; for small
+// batches every decode workgroup runs it itself, in its still empty LDS ring,
+// and keeps only its own item (no separate launch).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t* __restrict__ seq_lens,
-                                                    int32_t* __restrict__ req_info,
-                                                    WorkItem* __restrict__ work) {
-    constexpr int kCached = 8192;            // page counts of up to this many requests stay in LDS
-    constexpr int kCand = 16;                // chunk sizes counted per round, one per wave
-    __shared__ int s_scan[1024];
-    __shared__ int s_pages[kCached];
-    __shared__ int s_first[kCached];         // first kv-unit of each request (when cached)
-    __shared__ unsigned long long s_total[16];   // per-wave partial sums of pages
-    __shared__ int s_longest[16];                // per-wave longest request (pages)
-    __shared__ unsigned int s_cnt[2][kCand];     // kv-units per candidate chunk, two rounds in turn
+typedef __attribute__((address_space(3))) int lds_int;
+typedef __attribute__((address_space(3))) unsigned int lds_uint;
+
+// Wave-wide inclusive prefix sum / running max through DPP (row shifts within
+// each 16-lane row, then the row broadcasts of lanes 15 and 31): six VALU
+// steps, where shuffles through the LDS crossbar would each take a round trip.
+// Lane 63 ends with the whole wave's sum / max.
+__device__ __forceinline__ int wave_scan_add(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+    return v;
+}
+__device__ __forceinline__ int wave_scan_max(int v) {   // v >= 0
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false));
+    return v;
+}
+__device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_scan_add(v), 63); }
+
+struct PlanScratch {
+    lds_int* pages;      // [cached] page counts
+    lds_int* first;      // [cached] first kv-unit of each request
+    lds_int* part;       // [3][waves] per-wave page sums (16-bit halves) and longest request
+    lds_uint* cnt;       // [2][16] kv-units per candidate chunk, two rounds in turn
+    lds_int* scan;       // [waves] kv-unit totals
+    lds_int* owner;      // [2] request and split of the kv-unit `probe` (when probe >= 0)
+    int cached;          // requests whose page count and first kv-unit stay in LDS
+};
+
+struct PlanResult {
+    int chunk;           // pages per split (automatic split)
+    int k_total;         // kv-units (request x split) in all
+};
+
+// Runs on all NT threads of the block (every barrier inside is reached by all
+// of them); req_info, if not null, receives (splits, first kv-unit) per
+// request.  probe_slot >= 0 names a work slot whose request and split the
+// thread that owns the request writes to L.owner (see plan_item).
+template <int NT>
+__device__ __forceinline__ PlanResult plan_splits(const PlanParams& p, const int32_t* __restrict__ seq_lens,
+                                                  const PlanScratch& L, int32_t* __restrict__ req_info,
+                                                  int probe_slot = -1) {
+    constexpr int kWaves = NT / 64;
+    constexpr int kCand = 16;                // chunk sizes counted per round
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
-    const int per = (p.batch + 1023) / 1024;
+    const int per = (p.batch + NT - 1) / NT;
     const int b0 = min(p.batch, tid * per), b1 = min(p.batch, b0 + per);
     const int cap = p.max_pages * kPage;
     auto pages_global = [&](int b) {
         const int n = min(max(seq_lens[b], 0), cap);
         return (n + kPage - 1) / kPage;
     };
-    // page counts into LDS, with the total and the longest request on the way
-    // (reduced within each wave by shuffles, then over the 16 wave partials)
+    // page counts into LDS, with the total and the longest request on the way.
+    // A lane's sum can pass 2^31 only in theory (2^20 requests of 2^24 pages),
+    // so the total travels as two 16-bit halves, each summed in 32 bits.
     unsigned long long my_total = 0;
     int my_longest = 0;
-    for (int b = tid; b < p.batch; b += 1024) {
+    for (int b = tid; b < p.batch; b += NT) {
         const int pg = pages_global(b);
-        if (b < kCached) s_pages[b] = pg;
+        if (b < L.cached) L.pages[b] = pg;
         my_total += (unsigned long long)pg;
         my_longest = max(my_longest, pg);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        my_total += __shfl_xor(my_total, off);
-        my_longest = max(my_longest, __shfl_xor(my_longest, off));
-    }
+    const int t_lo = wave_sum((int)(my_total & 0xffff));
+    const int t_hi = wave_sum((int)(my_total >> 16));
+    const int w_longest = __builtin_amdgcn_readlane(wave_scan_max(my_longest), 63);
     if (lane == 0) {
-        s_total[wv] = my_total;
-        s_longest[wv] = my_longest;
+        L.part[wv] = t_lo;
+        L.part[kWaves + wv] = t_hi;
+        L.part[2 * kWaves + wv] = w_longest;
     }
     __syncthreads();
-    auto pages_of = [&](int b) { return b < kCached ? s_pages[b] : pages_global(b); };
+    auto pages_of = [&](int b) { return b < L.cached ? L.pages[b] : pages_global(b); };
     unsigned long long total_pages = 0;
     int longest = 0;
-    for (int i = 0; i < 16; ++i) {
-        total_pages += s_total[i];
-        longest = max(longest, s_longest[i]);
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        total_pages += (unsigned long long)(unsigned)L.part[i] + ((unsigned long long)(unsigned)L.part[kWaves + i] << 16);
+        longest = max(longest, L.part[2 * kWaves + i]);
     }
 
     int chunk = 1;
@@ -110,10 +157,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
         // allows.  It lies between the averaging bound and the longest request
         // (any chunk at or past the longest request gives every request one
         // split, the same work list); when even that does not fit, the longest
-        // request is the chunk.  Each round counts 16 chunk sizes at once, wave
-        // w the w-th: first the 16 sizes from the averaging bound up (the answer
-        // is almost always among them), then 16 sizes spread evenly over what
-        // is left of the range, which shrinks it 16-fold per round.
+        // request is the chunk.  Each round counts 16 chunk sizes at once (the
+        // waves share them out): first the 16 sizes from the averaging bound
+        // up (the answer is almost always among them), then 16 sizes spread
+        // evenly over what is left of the range, which shrinks it 16-fold.
         const long long units_cap = p.target_units / p.m_tiles > 0 ? p.target_units / p.m_tiles : 1;
         const long long avg = (long long)((total_pages + units_cap - 1) / units_cap);
         const int hi0 = max(longest, 1);
@@ -127,9 +174,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
                 const unsigned int pg = (unsigned int)pages_of(b);
                 cnt += pg > (unsigned int)c ? (pg + c - 1) / (unsigned int)c : 1u;
             }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
-            return cnt;
+            return (unsigned int)wave_sum((int)cnt);
         };
         // invariant: the answer is the smallest fitting chunk in [lo, hi], or hi if none fits
         for (int round = 0;; ++round) {
@@ -137,9 +182,12 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
             auto cand = [&](int j) {
                 return dense ? min(lo + j, hi) : lo + (int)((long long)(hi - lo) * (j + 1) / kCand);
             };
-            unsigned int* cnt = s_cnt[round & 1];
-            const unsigned int mine = count(cand(wv));
-            if (lane == 0) cnt[wv] = mine;
+            lds_uint* cnt = L.cnt + (round & 1) * kCand;
+#pragma unroll
+            for (int j = wv; j < kCand; j += kWaves) {
+                const unsigned int mine = count(cand(j));
+                if (lane == 0) cnt[j] = mine;
+            }
             __syncthreads();
             int first = -1;   // first candidate that fits
             for (int j = kCand - 1; j >= 0; --j)
@@ -162,77 +210,161 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
     }
 
     // splits per request, and the first kv-unit of each request (exclusive
-    // scan: a wavefront scan, then the 16 wave totals through LDS)
+    // scan: a wavefront scan, then the wave totals through LDS)
     int my_k = 0;
     for (int b = b0; b < b1; ++b) {
         const int pages = pages_of(b);
         const int S = p.num_splits > 0 ? min(p.num_splits, pages) : (pages + chunk - 1) / chunk;
         my_k += max(S, 1);
     }
-    int incl = my_k;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
-    }
-    if (lane == 63) s_scan[wv] = incl;
+    const int incl = wave_scan_add(my_k);
+    if (lane == 63) L.scan[wv] = incl;
     __syncthreads();
     int wave_base = 0, k_total = 0;
-    for (int i = 0; i < 16; ++i) {
-        const int t = s_scan[i];
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const int t = L.scan[i];
         wave_base += i < wv ? t : 0;
         k_total += t;
+    }
+    // kv-unit of the probed slot (the layout of plan_item)
+    int probe_k = -1;
+    if (probe_slot >= 0) {
+        const int per_xcd = (k_total + 7) / 8;
+        const int kx = (probe_slot >> 3) / p.m_tiles;
+        probe_k = kx < per_xcd ? per_xcd * (probe_slot & 7) + kx : -1;
     }
     int base = wave_base + incl - my_k;
     for (int b = b0; b < b1; ++b) {
         const int pages = pages_of(b);
         const int S = p.num_splits > 0 ? max(1, min(p.num_splits, pages))
                                        : max(1, (pages + chunk - 1) / chunk);
-        req_info[2 * b] = S;
-        req_info[2 * b + 1] = base;
-        if (b < kCached) s_first[b] = base;
+        if (req_info) {
+            req_info[2 * b] = S;
+            req_info[2 * b + 1] = base;
+        }
+        if (b < L.cached) L.first[b] = base;
+        if (probe_k >= base && probe_k < base + S) {
+            L.owner[0] = b;
+            L.owner[1] = probe_k - base;
+        }
         base += S;
     }
-    __syncthreads();   // req_info of every request written (and visible to the block)
-    auto first_of = [&](int b) { return b < kCached ? s_first[b] : req_info[2 * b + 1]; };
+    __syncthreads();   // first kv-units of every cached request visible to the block
+    return PlanResult{chunk, k_total};
+}
 
-    // Work items, one thread per (kv-unit, row tile) slot.  Dispatch deals
-    // workgroups to the 8 XCDs round-robin, so slot u runs on XCD u % 8 as its
-    // (u / 8)-th workgroup there.  Each XCD takes a contiguous run of
-    // C = ceil(kv-units / 8) kv-units with all their row tiles: slot u holds
-    // kv-unit k = C (u % 8) + (u / 8) / m_tiles and row tile (u / 8) % m_tiles.
-    // The splits of one request (which read the same query rows) and the row
-    // tiles of one kv-unit (which read the same pages) then share one L2.  The
-    // request of kv-unit k is found by binary search over the first kv-units.
-    const int per_xcd = (k_total + 7) / 8;   // the same value the combine derives from req_info
-    for (int u = tid; u < p.units_max; u += 1024) {
-        const int pos = u >> 3;
-        const int kx = pos / p.m_tiles;
-        const int k = per_xcd * (u & 7) + kx;
-        const int mt = pos - kx * p.m_tiles;
-        WorkItem w;
-        w.pad0 = 0;
-        w.pad1 = 0;
-        if (kx >= per_xcd || k >= k_total) {
-            w.b = -1; w.mt = 0; w.split = 0; w.page_begin = 0; w.page_end = 0; w.nsplit = 0;
-        } else {
-            int lo = 0, hi = p.batch - 1;     // last request whose first kv-unit is <= k
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (first_of(mid) <= k) lo = mid; else hi = mid - 1;
-            }
-            const int b = lo;
-            const int s = k - first_of(b);
-            const int S = (b + 1 < p.batch ? first_of(b + 1) : k_total) - first_of(b);
-            const int pages = pages_of(b);
-            const int cb = p.num_splits > 0 ? (pages + S - 1) / S : chunk;
-            w.b = b; w.mt = mt; w.split = s;
-            w.page_begin = min(pages, s * cb);
-            w.page_end = min(pages, (s + 1) * cb);
-            w.nsplit = S;
-        }
-        work[u] = w;
+// Work item of slot u.  Dispatch deals workgroups to the 8 XCDs round-robin,
+// so slot u runs on XCD u % 8 as its (u / 8)-th workgroup there.  Each XCD
+// takes a contiguous run of C = ceil(kv-units / 8) kv-units with all their
+// row tiles: slot u holds kv-unit k = C (u % 8) + (u / 8) / m_tiles and row
+// tile (u / 8) % m_tiles.  The splits of one request (which read the same
+// query rows) and the row tiles of one kv-unit (which read the same pages)
+// then share one L2.  The request of kv-unit k is found by binary search over
+// the first kv-units; first_of(b) and pages_of(b) give any request's values.
+template <typename FirstOf, typename PagesOf>
+__device__ __forceinline__ WorkItem plan_item(const PlanParams& p, const PlanResult& r, int u,
+                                              FirstOf&& first_of, PagesOf&& pages_of) {
+    const int per_xcd = (r.k_total + 7) / 8;   // the same value the combine derives from req_info
+    const int pos = u >> 3;
+    const int kx = pos / p.m_tiles;
+    const int k = per_xcd * (u & 7) + kx;
+    const int mt = pos - kx * p.m_tiles;
+    WorkItem w;
+    w.pad0 = 0;
+    w.pad1 = 0;
+    if (kx >= per_xcd || k >= r.k_total) {
+        w.b = -1; w.mt = 0; w.split = 0; w.page_begin = 0; w.page_end = 0; w.nsplit = 0;
+        return w;
     }
+    int lo = 0, hi = p.batch - 1;     // last request whose first kv-unit is <= k
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (first_of(mid) <= k) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int s = k - first_of(b);
+    const int S = (b + 1 < p.batch ? first_of(b + 1) : r.k_total) - first_of(b);
+    const int pages = pages_of(b);
+    const int cb = p.num_splits > 0 ? (pages + S - 1) / S : r.chunk;
+    w.b = b; w.mt = mt; w.split = s;
+    w.page_begin = min(pages, s * cb);
+    w.page_end = min(pages, (s + 1) * cb);
+    w.nsplit = S;
+    return w;
+}
+
+__global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t* __restrict__ seq_lens,
+                                                    int32_t* __restrict__ req_info,
+                                                    WorkItem* __restrict__ work) {
+    constexpr int kCached = 8192;            // page counts of up to this many requests stay in LDS
+    __shared__ int s_pages[kCached];
+    __shared__ int s_first[kCached];
+    __shared__ int s_part[48];
+    __shared__ unsigned int s_cnt[32];
+    __shared__ int s_scan[16];
+    const PlanScratch L{(lds_int*)s_pages, (lds_int*)s_first, (lds_int*)s_part, (lds_uint*)s_cnt,
+                        (lds_int*)s_scan, nullptr, kCached};
+    const PlanResult r = plan_splits<1024>(p, seq_lens, L, req_info);
+    const int cap = p.max_pages * kPage;
+    auto pages_of = [&](int b) {
+        if (b < kCached) return s_pages[b];
+        const int n = min(max(seq_lens[b], 0), cap);
+        return (n + kPage - 1) / kPage;
+    };
+    auto first_of = [&](int b) { return b < kCached ? s_first[b] : req_info[2 * b + 1]; };
+    for (int u = threadIdx.x; u < p.units_max; u += 1024) work[u] = plan_item(p, r, u, first_of, pages_of);
+}
+
+// The decode kernels' own copy of the planner for batches of at most
+// kFusedPlanMax requests, in the first bytes of their LDS ring (before any
+// copy into it).  Every workgroup derives the same split list and keeps its
+// own item, which it also stores to the work list; workgroup 0 stores the
+// per-request (splits, first kv-unit) the combine reads.  The item is the
+// same value in every lane; readfirstlane makes that visible to the compiler.
+__device__ __forceinline__ WorkItem decode_work_item(const DecodeParams& p, uint8_t* lds) {
+    if (!p.fused_plan) return p.work[blockIdx.x];
+    lds_u8* l8 = (lds_u8*)lds;
+    constexpr int kOff = 8 * kFusedPlanMax;
+    const PlanScratch L{(lds_int*)l8, (lds_int*)(l8 + 4 * kFusedPlanMax), (lds_int*)(l8 + kOff),
+                        (lds_uint*)(l8 + kOff + 64), (lds_int*)(l8 + kOff + 192), (lds_int*)(l8 + kOff + 224),
+                        kFusedPlanMax};
+    const int u = blockIdx.x;
+    const PlanResult r = plan_splits<256>(p.plan, p.seq_lens, L, u == 0 ? p.req_info : nullptr, u);
+    // this slot's item (the layout of plan_item), its request and split
+    // written by the thread that owns the request
+    const PlanParams& q = p.plan;
+    const int per_xcd = (r.k_total + 7) / 8;
+    const int kx = (u >> 3) / q.m_tiles;
+    const int k = per_xcd * (u & 7) + kx;
+    WorkItem w;
+    w.pad0 = 0;
+    w.pad1 = 0;
+    if (kx >= per_xcd || k >= r.k_total) {
+        w.b = -1; w.mt = 0; w.split = 0; w.page_begin = 0; w.page_end = 0; w.nsplit = 0;
+    } else {
+        const int b = L.owner[0];
+        const int sp = L.owner[1];
+        const int pages = L.pages[b];
+        const int S = (b + 1 < q.batch ? (int)L.first[b + 1] : r.k_total) - (int)L.first[b];
+        const int cb = q.num_splits > 0 ? (pages + S - 1) / S : r.chunk;
+        w.b = b;
+        w.mt = (u >> 3) - kx * q.m_tiles;
+        w.split = sp;
+        w.page_begin = min(pages, sp * cb);
+        w.page_end = min(pages, (sp + 1) * cb);
+        w.nsplit = S;
+    }
+    // the same value in every lane: say so, so that it stays in scalar registers
+    w.b = __builtin_amdgcn_readfirstlane(w.b);
+    w.mt = __builtin_amdgcn_readfirstlane(w.mt);
+    w.split = __builtin_amdgcn_readfirstlane(w.split);
+    w.page_begin = __builtin_amdgcn_readfirstlane(w.page_begin);
+    w.page_end = __builtin_amdgcn_readfirstlane(w.page_end);
+    w.nsplit = __builtin_amdgcn_readfirstlane(w.nsplit);
+    if (threadIdx.x == 0) p.work_out[u] = w;
+    __syncthreads();   // the LDS ring is filled next
+    return w;
 }
 
 // ---------------------------------------------------------------------------
@@ -319,7 +451,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 void decode_bf16_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
 
-    const WorkItem w = p.work[blockIdx.x];
+    const WorkItem w = decode_work_item(p, lds);
     if (w.b < 0) return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -859,7 +991,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_pe
 void decode_fp8_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes8];
 
-    const WorkItem w = p.work[blockIdx.x];
+    const WorkItem w = decode_work_item(p, lds);
     if (w.b < 0) return;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -70,12 +70,12 @@ class HipEvents:
 
 
 def kernel_source_hash() -> str:
-    """sha256 (16 hex) of the bf16 split-KV decode kernel's source section (the
-    kernel the counter file describes); other kernels in the file do not count."""
-    src = open(KERNEL_SRC).read()
-    a = src.index("// split-KV decode, bf16 cache")
-    b = src.index("// split-KV decode, OCP fp8")
-    return hashlib.sha256(src[a:b].encode()).hexdigest()[:16]
+    """sha256 (16 hex) of the kernel sources (every kernel and the shared
+    header): the stored counter file is used only while this matches."""
+    h = hashlib.sha256()
+    for path in (KERNEL_SRC, os.path.join(os.path.dirname(KERNEL_SRC), "mla_internal.h")):
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def workload_accounting(inp) -> dict:

@@ -1427,44 +1427,48 @@ template <typename PartialAt>
 __device__ __forceinline__ void merge_row(int n, PartialAt at, void* out, float* lse_out, size_t orow,
                                           int out_bf16) {
     const int lane = threadIdx.x & 63;
-    float mx = -INFINITY;
-    for (int i = lane; i < n; i += 64) mx = fmaxf(mx, *at.lse(i));
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    // One pass with a running maximum, 8 partials at a time: all loads of a
+    // group (8 LSEs, the same address in every lane, and 2 x 16 bytes of each
+    // output row per lane) are issued before any is used, so a row with up to
+    // 8 partials costs one memory round trip.
+    float mx = -INFINITY, wsum = 0.f;
     f32x4 acc0 = (f32x4)0.f, acc1 = (f32x4)0.f;
-    float wsum = 0.f;
-    if (mx != -INFINITY) {
-        // eight partials per step, so that 16 KB of loads per wave are in flight
-        int i = 0;
-        for (; i + 8 <= n; i += 8) {
-            float li[8];
-            f32x4 v0[8], v1[8];
+    for (int i = 0; i < n; i += 8) {
+        float li[8];
+        f32x4 v0[8], v1[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 8; ++u) {
+            if (i + u < n) {
                 li[u] = *at.lse(i + u);
                 const f32x4* src = (const f32x4*)at.out(i + u) + 2 * lane;
                 v0[u] = src[0];
                 v1[u] = src[1];
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                // an empty partial (lse -inf) has weight 0 and its output is never used
-                const float wgt = li[u] == -INFINITY ? 0.f : __expf(li[u] - mx);
-                wsum += wgt;
-                if (wgt != 0.f) {
-                    acc0 += wgt * v0[u];
-                    acc1 += wgt * v1[u];
-                }
+            } else {
+                li[u] = -INFINITY;
             }
         }
-        for (; i < n; ++i) {
-            const float li = *at.lse(i);
-            if (li == -INFINITY) continue;
-            const float wgt = __expf(li - mx);
-            wsum += wgt;
-            const f32x4* src = (const f32x4*)at.out(i) + 2 * lane;
-            acc0 += wgt * src[0];
-            acc1 += wgt * src[1];
+        float gm = li[0];
+#pragma unroll
+        for (int u = 1; u < 8; ++u) gm = fmaxf(gm, li[u]);
+        if (gm > mx) {
+            // rescale what is accumulated to the new maximum (nothing yet if
+            // mx is still -inf)
+            const float r = mx == -INFINITY ? 0.f : __expf(mx - gm);
+            acc0 *= r;
+            acc1 *= r;
+            wsum *= r;
+            mx = gm;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            // an empty partial (lse -inf) has weight 0 and its output is never
+            // read into the sum (it may hold anything)
+            if (li[u] != -INFINITY) {
+                const float wgt = __expf(li[u] - mx);
+                wsum += wgt;
+                acc0 += wgt * v0[u];
+                acc1 += wgt * v1[u];
+            }
         }
     }
     const bool empty = mx == -INFINITY;

@@ -133,10 +133,51 @@ def workspace_size(desc: DecodeDesc) -> int:
     return n.value
 
 
+def _nbytes(x) -> int | None:
+    """Bytes of a tensor argument (None for a raw address, which cannot be checked)."""
+    if x is None or isinstance(x, int):
+        return None
+    return x.numel() * x.element_size()
+
+
+def _need(name: str, x, nbytes: int, itemsize: int | None = None) -> None:
+    if x is None or isinstance(x, int):
+        return
+    if itemsize is not None and x.element_size() != itemsize:
+        raise ValueError(f"{name}: element size {x.element_size()}, expected {itemsize}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if _nbytes(x) < nbytes:
+        raise ValueError(f"{name}: {_nbytes(x)} bytes, the descriptor needs {nbytes}")
+
+
+def check_decode_buffers(desc: DecodeDesc, q, kv_cache, kv_scale, block_table, seq_lens, out, lse) -> None:
+    """Host-side check of tensor arguments against the descriptor (sizes and
+    element sizes; raw integer addresses are not checked).  The C ABI takes
+    plain pointers and cannot see a buffer's size, so a too-small buffer would
+    otherwise be read or written out of bounds on the device."""
+    e = 2 if desc.kv_dtype == BF16 else 1
+    rows = desc.batch * desc.q_len * desc.num_heads
+    _need("q", q, rows * QK_DIM * e, e)
+    _need("kv_cache", kv_cache, desc.num_pages * desc.page_size * QK_DIM * e, e)
+    _need("block_table", block_table, desc.batch * desc.max_pages_per_seq * 4, 4)
+    _need("seq_lens", seq_lens, desc.batch * 4, 4)
+    _need("out", out, rows * LATENT_DIM * (4 if desc.out_dtype == F32 else 2), 4 if desc.out_dtype == F32 else 2)
+    _need("lse", lse, rows * 4, 4)
+    if desc.kv_dtype == FP8_E4M3:
+        if kv_scale is None:
+            raise ValueError("kv_scale is required for an fp8 cache")
+        _need("kv_scale", kv_scale, 4, 4)
+    elif kv_scale is not None:
+        raise ValueError("kv_scale must be None for a bf16 cache")
+
+
 def decode_partial(desc: DecodeDesc, q, kv_cache, kv_scale, block_table, seq_lens, scale: float,
                    out, lse, workspace, workspace_bytes: int | None = None, stream=None,
                    events=None) -> None:
-    """Enqueue mla_decode_partial on ``stream`` (default: torch's current stream)."""
+    """Enqueue mla_decode_partial on ``stream`` (default: torch's current stream).
+    Tensor arguments are checked against the descriptor first (ValueError)."""
+    check_decode_buffers(desc, q, kv_cache, kv_scale, block_table, seq_lens, out, lse)
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
     args = [ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(kv_scale), _ptr(block_table),
@@ -151,7 +192,12 @@ def decode_partial(desc: DecodeDesc, q, kv_cache, kv_scale, block_table, seq_len
 
 
 def merge_states(outs, lses, n: int, rows: int, out, lse, out_dtype: int = F32, stream=None) -> None:
-    """Enqueue mla_merge_states: outs [n][rows][512] f32, lses [n][rows] -> out, lse."""
+    """Enqueue mla_merge_states: outs [n][rows][512] f32, lses [n][rows] -> out, lse.
+    Tensor arguments are size-checked first (ValueError)."""
+    _need("outs", outs, n * rows * LATENT_DIM * 4, 4)
+    _need("lses", lses, n * rows * 4, 4)
+    _need("out", out, rows * LATENT_DIM * (4 if out_dtype == F32 else 2), 4 if out_dtype == F32 else 2)
+    _need("lse", lse, rows * 4, 4)
     st = lib.mla_merge_states(_ptr(outs), _ptr(lses), int(n), int(rows), _ptr(out), _ptr(lse),
                               int(out_dtype), _stream(stream))
     if st != OK:

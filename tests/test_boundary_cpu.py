@@ -127,3 +127,64 @@ def test_merge_argument_checks():
     assert f(None, 4096, 2, 10, 4096, 4096, mla.F32, None) == mla.ERR_INVALID_ARG
     assert f(4096 + 4, 4096, 2, 10, 4096, 4096, mla.F32, None) == mla.ERR_INVALID_ARG
     assert f(4096, 4096, 2, 0, None, None, mla.F32, None) == mla.OK          # nothing to do
+
+
+def _tensors(desc, kv_dtype_bytes=2, pages=None):
+    import torch
+    rows = desc.batch * desc.q_len * desc.num_heads
+    dt = torch.bfloat16 if kv_dtype_bytes == 2 else torch.uint8
+    return dict(
+        q=torch.zeros((rows, mla.QK_DIM), dtype=dt),
+        kv_cache=torch.zeros(((pages or desc.num_pages) * desc.page_size, mla.QK_DIM), dtype=dt),
+        block_table=torch.zeros((desc.batch, desc.max_pages_per_seq), dtype=torch.int32),
+        seq_lens=torch.zeros((desc.batch,), dtype=torch.int32),
+        out=torch.zeros((rows, mla.LATENT_DIM), dtype=torch.float32),
+        lse=torch.zeros((rows,), dtype=torch.float32),
+    )
+
+
+def test_buffer_checks_accept_matching_tensors():
+    """Host-side checks pass for tensors that match the descriptor (no device call)."""
+    d = mla.make_desc(3, 2, 16, 7, 5)
+    t = _tensors(d)
+    mla.check_decode_buffers(d, t["q"], t["kv_cache"], None, t["block_table"], t["seq_lens"], t["out"], t["lse"])
+
+
+@pytest.mark.parametrize("bad", ["q", "kv_cache", "block_table", "seq_lens", "out", "lse"])
+def test_buffer_checks_reject_short_or_mistyped(bad):
+    """A tensor smaller than the descriptor needs (or of the wrong element size)
+    raises before anything is launched: e.g. an fp8 cache passed with a bf16
+    descriptor is half the bytes the kernel would read."""
+    import torch
+    d = mla.make_desc(3, 2, 16, 7, 5)
+    t = _tensors(d)
+    x = t[bad]
+    t[bad] = x.flatten()[: x.numel() - 1].clone()
+    with pytest.raises(ValueError):
+        mla.check_decode_buffers(d, t["q"], t["kv_cache"], None, t["block_table"], t["seq_lens"], t["out"], t["lse"])
+    t = _tensors(d, kv_dtype_bytes=1)       # e4m3 bytes with a bf16 descriptor
+    with pytest.raises(ValueError):
+        mla.check_decode_buffers(d, t["q"], t["kv_cache"], None, t["block_table"], t["seq_lens"], t["out"], t["lse"])
+
+
+def test_buffer_checks_kv_scale_rules():
+    import torch
+    d8 = mla.make_desc(2, 1, 16, 4, 2, kv_dtype=mla.FP8_E4M3)
+    t = _tensors(d8, kv_dtype_bytes=1)
+    with pytest.raises(ValueError):
+        mla.check_decode_buffers(d8, t["q"], t["kv_cache"], None, t["block_table"], t["seq_lens"], t["out"], t["lse"])
+    mla.check_decode_buffers(d8, t["q"], t["kv_cache"], torch.ones(1), t["block_table"], t["seq_lens"],
+                             t["out"], t["lse"])
+    d = mla.make_desc(2, 1, 16, 4, 2)
+    t = _tensors(d)
+    with pytest.raises(ValueError):
+        mla.check_decode_buffers(d, t["q"], t["kv_cache"], torch.ones(1), t["block_table"], t["seq_lens"],
+                                 t["out"], t["lse"])
+
+
+def test_merge_buffer_checks():
+    import torch
+    outs = torch.zeros((4, 10, mla.LATENT_DIM))
+    lses = torch.zeros((4, 10))
+    with pytest.raises(ValueError):
+        mla.merge_states(outs, lses, 4, 11, torch.zeros((11, mla.LATENT_DIM)), torch.zeros(11))

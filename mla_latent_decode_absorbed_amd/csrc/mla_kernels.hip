@@ -509,8 +509,6 @@ void decode_bf16_kernel(DecodeParams p) {
             for (int j = 0; j < 9; ++j) issue_copy(half_begin + j3, j, src);
         }
     };
-    issue_half(0);
-
     // this lane's query row, its visible length, and its Q^T fragments:
     // k-step ks covers dims 16 ks .. + 15, lane holds dims 16 ks + 8 G .. + 7
     const int row = w.mt * kMTile + wave * 32 + lr;
@@ -523,14 +521,32 @@ void decode_bf16_kernel(DecodeParams p) {
     // smallest visible length over every row of the workgroup: half pages
     // entirely below it need no masking
     const int nvis_min = min(p.causal ? max(n - (p.q_len - 1), 0) : n, unit_end);
-    // (a row past the end of the tile reads the last row instead; its
-    // results are never stored)
+    // The query tile comes through the (still empty) LDS ring: wave w copies
+    // its 32 rows, 36,864 contiguous bytes, into ring slot w with 36 copies of
+    // 1 KB (whole cache lines; a direct load of the MFMA layout would touch 32
+    // rows x 32 bytes per instruction), waits for its own copies and reads
+    // its fragments back.  A row past the end of the tile copies the last row
+    // instead (its results are never stored).  Once every wave has its
+    // fragments, the ring takes the first three half pages of the cache.
     bf16x8_t qf[36];
     {
-        const __bf16* qr = (const __bf16*)p.q + ((size_t)b * p.rows + min(row, p.rows - 1)) * kQK + 8 * G;
+        const uint8_t* qreq = (const uint8_t*)p.q + (size_t)b * p.rows * kRowBytes;
+        const int row0 = w.mt * kMTile + wave * 32;           // first row of this wave
+        const uint32_t qdst = ring_addr + wave * kSlotBytes;
 #pragma unroll
-        for (int ks = 0; ks < 36; ++ks) qf[ks] = *(const bf16x8_t*)(qr + 16 * ks);
+        for (int j = 0; j < 36; ++j) {
+            const int q = j * 1024 + lane * 16;                // byte of the wave's 32 rows
+            const int r = q / kRowBytes;
+            const uint32_t src = (uint32_t)min(row0 + r, p.rows - 1) * kRowBytes + (q - r * kRowBytes);
+            dma16(qdst + j * 1024, qreq, src);
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        const lds_u8* qrow = ring + wave * kSlotBytes + lr * kRowBytes + 16 * G;
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) qf[ks] = *(const lds_bf16x8*)(qrow + 32 * ks);
     }
+    __syncthreads();   // every wave holds its query fragments: the ring is free
+    issue_half(0);
     issue_half(1);
     issue_half(2);
 

@@ -168,3 +168,10 @@ def test_plan_past_lds_cache():
 def test_plan_fixed_splits():
     """num_splits = 3 with requests shorter than 3 pages and empty ones."""
     check(ragged(50, 0, 600, 14, zeros=5), 32, 1, 10, 3, "fixed 3 splits")
+
+
+@pytest.mark.parametrize("batch", [256, 257])
+def test_plan_threshold_between_fused_and_planner_kernel(batch):
+    """256 requests are planned inside the decode kernel, 257 by the planner
+    kernel: both give the policy's split list."""
+    check(ragged(batch, 0, 5000, 15 + batch, zeros=7), 16, 1, 79, 0, f"batch {batch}")

@@ -1235,6 +1235,7 @@ void decode_fp8_kernel(DecodeParams p) {
                 for (int i = i0 + 4 * part; i < i0 + 4 * part + 4; ++i) {
                     s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_exp, st.mneg));
                     st.sum += s[i];
+                    asm volatile("" : "+v"(st.sum));   // keeps the add here (see the bf16 kernel)
                 }
             } else {
                 const int q = (part - 2) >> 1, i = i0 + 4 * q, r = 2 * g + q;
@@ -1266,7 +1267,8 @@ void decode_fp8_kernel(DecodeParams p) {
     // their operands come from LDS reads and registers no VALU instruction
     // writes right before them (the build checks the wait states).
     auto pv_softmax = [&](int k, const i32x8& ph_own, const i32x8& pl_own, const i32x8& ph_oth,
-                          const i32x8& pl_oth, f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out) {
+                          const i32x8& pl_oth, f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out,
+                          auto&& enter_next) {
         lds_u8* cur = slot_ptr(k);
         i32x8 vf[2];
         vf[0] = vfrag(cur, 0);
@@ -1292,6 +1294,9 @@ void decode_fp8_kernel(DecodeParams p) {
                 // point P(k+1) may overwrite them (piece 29).  No LDS wait is
                 // needed: those reads have returned.
                 if (dt == 0 && q == 3) __builtin_amdgcn_s_barrier();
+                // the top-of-step barrier of the next page, once P(k+1) is
+                // published (piece 29): the wait overlaps the last MFMAs
+                if (dt == 7 && q == 2) enter_next();
                 __builtin_amdgcn_sched_barrier(0);
                 softmax_piece(s0, s1, ph, pl, d_out, st, 4 * dt + q);
             }
@@ -1335,10 +1340,13 @@ void decode_fp8_kernel(DecodeParams p) {
         // right before the barrier (see the bf16 kernel)
         auto copy_page = [&](int k) { return k + 3 < pg_end ? k + 3 : min(k, pg_end - 1); };
         int pid_copy;
-        auto enter = [&](int k) {
+        auto enter_sync = [&](int k) {
             wait_copies(k + 2 < pg_end ? 1 : 0);
             pid_copy = bt_s[copy_page(k)];
             lds_sync();
+        };
+        auto enter = [&](int k) {
+            enter_sync(k);
             if (k + 1 < pg_end) zero_tail(k + 1);
         };
         // the partner's P(k) terms and rescale shift (published before the
@@ -1369,13 +1377,18 @@ void decode_fp8_kernel(DecodeParams p) {
             }
             if (needs_mask(k + 1)) mask_s(k + 1, s0, s1);
             int d_nxt;
-            pv_softmax(k, ph_cur, pl_cur, ph_oth, pl_oth, s0, s1, ph_nxt, pl_nxt, d_nxt);
-            if (k + 1 >= pg_end) break;
+            // (the top of iteration k + 1 runs inside the PV, after P(k + 1) is
+            // published; only the rare zeroing of a sequence tail stays here)
+            const bool more = k + 1 < pg_end;
+            pv_softmax(k, ph_cur, pl_cur, ph_oth, pl_oth, s0, s1, ph_nxt, pl_nxt, d_nxt, [&]() {
+                if (more) enter_sync(k + 1);
+            });
+            if (!more) break;
             ++k;
             ph_cur = ph_nxt;
             pl_cur = pl_nxt;
             d_cur = d_nxt;
-            enter(k);
+            if (k + 1 < pg_end) zero_tail(k + 1);
         }
     }
 

@@ -208,3 +208,46 @@ def test_fp8_bf16_output_and_determinism():
     a = run_hip(inp)
     b = run_hip(inp)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_max_qlen16_causal_with_short_sequences(dtype):
+    """q_len 16 (the largest supported) x 8 heads = one 128-row tile, causal:
+    query token t sees seq_len - (15 - t) tokens, so a 5-token sequence leaves
+    tokens 0..10 with nothing visible (out 0, lse -inf)."""
+    say(f"q_len=16 causal {dtype}")
+    inp = workloads.make_decode_inputs(3, 16, 8, [5, 16, 700], dtype, seed=41, device=dev())
+    out, lse = run_hip(inp)
+    o_ref, l_ref = run_oracle(inp)
+    compare(out, lse, o_ref, l_ref, dtype=dtype, what=f"qlen16 causal {dtype}")
+    assert torch.isneginf(lse[0, :11]).all() and torch.all(out[0, :11] == 0)
+
+
+def test_qlen4_not_causal():
+    """q_len 4 with causal = 0: every query token sees every cache token."""
+    say("q_len=4 not causal")
+    inp = workloads.make_decode_inputs(2, 4, 32, [90, 257], "bf16", seed=42, device=dev(), causal=False)
+    assert not inp.causal
+    out, lse = run_hip(inp)
+    o_ref, l_ref = run_oracle(inp)
+    compare(out, lse, o_ref, l_ref, what="qlen4 not causal")
+
+
+def test_more_fixed_splits_than_pages():
+    """num_splits = 8 on sequences of 1-3 pages: each request gets min(8, pages) splits."""
+    say("num_splits=8, 1-3 pages")
+    inp = workloads.make_decode_inputs(3, 1, 64, [40, 128, 150], "bf16", seed=43, device=dev())
+    out, lse = run_hip(inp, num_splits=8)
+    o_ref, l_ref = run_oracle(inp)
+    compare(out, lse, o_ref, l_ref, what="splits 8 > pages")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_three_row_tiles_partial_last(dtype):
+    """q_len 3 x 100 heads = 300 rows: tiles of 128, 128 and 44 rows (the last
+    tile's missing rows read a clamped query row and are never stored)."""
+    say(f"300 rows {dtype}")
+    inp = workloads.make_decode_inputs(2, 3, 100, [333, 64], dtype, seed=44, device=dev())
+    out, lse = run_hip(inp, num_splits=2)
+    o_ref, l_ref = run_oracle(inp)
+    compare(out, lse, o_ref, l_ref, dtype=dtype, what=f"300 rows {dtype}")

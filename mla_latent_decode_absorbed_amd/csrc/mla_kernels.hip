@@ -499,12 +499,14 @@ void decode_bf16_kernel(DecodeParams p) {
     auto issue_copy = [&](int k, int j, const uint8_t* src) {
         dma16(slot_addr(k) + wave * 9 * 1024 + j * 1024, src + wave * 8 * kRowBytes, (uint32_t)cp_off[j]);
     };
-    // prologue: the first half page, then the query, then two more half
-    // pages.  Loads retire in issue order, so the first QK^T (which needs the
-    // first half page and the query) does not wait for the other two.
+    // prologue copies of the first three half pages (after the query, below);
+    // their page ids (half pages 0 and 1 share a page) are loaded now, so that
+    // the scalar loads' latency overlaps the query's
+    const int pid_first = half_begin < half_end ? page_id(half_begin) : 0;
+    const int pid_second = half_begin + 2 < half_end ? page_id(half_begin + 2) : 0;
     auto issue_half = [&](int j3) {
         if (half_begin + j3 < half_end) {
-            const uint8_t* src = half_src(half_begin + j3);
+            const uint8_t* src = half_src_of(j3 < 2 ? pid_first : pid_second, half_begin + j3);
 #pragma unroll
             for (int j = 0; j < 9; ++j) issue_copy(half_begin + j3, j, src);
         }
@@ -1052,10 +1054,16 @@ void decode_fp8_kernel(DecodeParams p) {
     auto page_src = [&](int k) { return page_src_of(bt_s[k]); };
     auto slot_addr = [&](int k) { return ring_addr + ((k - pg_begin) & 3) * kSlotBytes; };
     auto slot_ptr = [&](int k) { return ring + ((k - pg_begin) & 3) * kSlotBytes; };
-    // prologue: the first page, the query, then two more pages (see the bf16 kernel)
+    // prologue: the first page, the query, then two more pages; loads retire
+    // in issue order, so the first QK^T (which needs the first page and the
+    // query) does not wait for the other two.  The three page ids are loaded
+    // together up front.
+    const int pid0 = pg_begin < pg_end ? bt_s[pg_begin] : 0;
+    const int pid1 = pg_begin + 1 < pg_end ? bt_s[pg_begin + 1] : 0;
+    const int pid2 = pg_begin + 2 < pg_end ? bt_s[pg_begin + 2] : 0;
     auto issue_page = [&](int j3) {
         if (pg_begin + j3 < pg_end) {
-            const uint8_t* src = page_src(pg_begin + j3) + wave * 16 * kRowBytes8;
+            const uint8_t* src = page_src_of(j3 == 0 ? pid0 : j3 == 1 ? pid1 : pid2) + wave * 16 * kRowBytes8;
             const uint32_t dst = slot_addr(pg_begin + j3) + wave * 9 * 1024;
 #pragma unroll
             for (int j = 0; j < 9; ++j) dma16(dst + j * 1024, src, (uint32_t)cp_off[j]);

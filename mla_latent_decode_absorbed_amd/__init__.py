@@ -72,7 +72,7 @@ class DecodeDesc(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m mla_latent_decode_absorbed_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python mla_latent_decode_absorbed_amd/build.py` "
                           "or __graft_entry__.build()")
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float

@@ -1,6 +1,12 @@
-"""Build libmla_decode.so (gfx950 HIP kernels + C ABI) in the package directory."""
+"""Build libmla_decode.so (gfx950 HIP kernels + C ABI) in the package directory.
+
+Run as a script (``python mla_latent_decode_absorbed_amd/build.py``) or load it
+by file path: importing it as a submodule would first run the package's
+``__init__``, which refuses to import while the library is not built yet.
+"""
 from __future__ import annotations
 
+import importlib.util
 import os
 import shutil
 import subprocess
@@ -31,7 +37,9 @@ def hipcc() -> str:
 def check_wait_states(verbose: bool = False) -> None:
     """Compile the kernels to gfx950 assembly and verify the wait states around
     the inline-assembly MFMAs (see isa_check.py); raises on a violation."""
-    from mla_latent_decode_absorbed_amd import isa_check  # noqa: WPS433 (import inside: plain module)
+    spec = importlib.util.spec_from_file_location("_mla_isa_check", os.path.join(PKG, "isa_check.py"))
+    isa_check = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(isa_check)
     asm = os.path.join(PKG, "_kernels_gfx950.s")
     flags = [f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")]
     cmd = [hipcc(), *flags, "--cuda-device-only", "-S", "-I", INCLUDE, "-I", CSRC, "-o", asm, SOURCES[0]]

@@ -188,3 +188,24 @@ def test_merge_buffer_checks():
     lses = torch.zeros((4, 10))
     with pytest.raises(ValueError):
         mla.merge_states(outs, lses, 4, 11, torch.zeros((11, mla.LATENT_DIM)), torch.zeros(11))
+
+
+def test_build_script_loads_without_the_package():
+    """A fresh checkout has no library yet, and the package refuses to import
+    without it: the build script (and the checker it runs) must therefore load
+    without importing the package."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import importlib.util, os, sys\n"
+        f"p = os.path.join({root!r}, 'mla_latent_decode_absorbed_amd', 'build.py')\n"
+        "spec = importlib.util.spec_from_file_location('_b', p)\n"
+        "m = importlib.util.module_from_spec(spec); spec.loader.exec_module(m)\n"
+        "assert callable(m.build) and callable(m.check_wait_states)\n"
+        "assert 'mla_latent_decode_absorbed_amd' not in sys.modules\n"
+    )
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd="/")
+    assert res.returncode == 0, res.stderr
+    src = open(os.path.join(root, "mla_latent_decode_absorbed_amd", "build.py")).read()
+    assert "from mla_latent_decode_absorbed_amd" not in src and "import mla_latent_decode_absorbed_amd" not in src

@@ -43,13 +43,17 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
 // LDS page layout: row t (token) of 1152 bytes, its 16-byte chunks permuted
-// within aligned groups of 8 by c -> c ^ swz(t).  swz maps 8 consecutive tokens
-// to 8 distinct values (row-fragment reads of 8 tokens x 16 B hit distinct
-// banks) and 4 consecutive tokens to 4 distinct even values (transpose reads of
-// 4 tokens x 2 chunks hit distinct banks).
+// within aligned groups of 8 by c -> c ^ swz(t).  gfx950's LDS has 64 banks of
+// 4 bytes and serves a 16-byte-per-lane read 16 lanes (256 bytes) at a time.
+// A 1152-byte row stride moves the bank window by 128 bytes per token, so
+// tokens of one parity share their window offset: swz is 16-periodic and gives
+// the 8 even and the 8 odd tokens of any 16 distinct values (row-fragment reads
+// of 16 tokens x 16 B hit all 64 banks once; with an 8-periodic swizzle tokens
+// t and t + 8 collide), and keeps bit 2 different between tokens 4j + i and
+// 4j + i + 2 (transpose reads of 4 tokens x 4 chunks hit distinct banks).
+// swz(t + 8) = swz(t) ^ 2 and swz(t + 16) = swz(t).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
-__device__ __forceinline__ int lds_off(int t, int c) { return t * kRowBytes + ((c ^ swz(t)) << 4); }
+__device__ __forceinline__ int swz(int t) { return (((t & 3) << 1) | ((t >> 2) & 1)) ^ ((t >> 2) & 2); }
 
 // ---------------------------------------------------------------------------
 // split planner: per-request split counts, first kv-units and work items,
@@ -475,15 +479,16 @@ void decode_bf16_kernel(DecodeParams p) {
     const int half_end = min(2 * w.page_end, (n + kHalfTok - 1) / kHalfTok);
 
     // per-lane copy offsets within an 8-token group: LDS chunk q = 64 j + lane
-    // of copy j holds (token q / 72, position q % 72) = global chunk
-    // (position ^ swz(token)) of that token; wave w copies tokens 8w .. 8w + 7
+    // of copy j holds (token q / 72, position q % 72) of the group; wave w
+    // copies slot tokens 8w .. 8w + 7, so that position holds global chunk
+    // (position ^ swz(8 w + token)) of its token
     int cp_off[9];
 #pragma unroll
     for (int j = 0; j < 9; ++j) {
         const int qc = j * 64 + lane;
         const int t = qc / kRowChunks;
         const int pc = qc - t * kRowChunks;
-        cp_off[j] = t * kRowBytes + ((pc ^ swz(t)) << 4);
+        cp_off[j] = t * kRowBytes + ((pc ^ swz(8 * wave + t)) << 4);
     }
     // Page ids come through the scalar unit (the block table is read-only
     // while the kernel runs, and a page id is the same for the whole wave):
@@ -537,15 +542,23 @@ void decode_bf16_kernel(DecodeParams p) {
         const uint32_t qdst = ring_addr + wave * kSlotBytes;
 #pragma unroll
         for (int j = 0; j < 36; ++j) {
-            const int q = j * 1024 + lane * 16;                // byte of the wave's 32 rows
-            const int r = q / kRowBytes;
-            const uint32_t src = (uint32_t)min(row0 + r, p.rows - 1) * kRowBytes + (q - r * kRowBytes);
+            // LDS chunk q of the wave's 32 rows is (row r, position pc), which
+            // holds chunk pc ^ swz(r) of that query row (the cache's layout)
+            const int qc = j * 64 + lane;
+            const int r = qc / kRowChunks;
+            const int pc = qc - r * kRowChunks;
+            const uint32_t src = (uint32_t)min(row0 + r, p.rows - 1) * kRowBytes + ((pc ^ swz(r)) << 4);
             dma16(qdst + j * 1024, qreq, src);
         }
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        const lds_u8* qrow = ring + wave * kSlotBytes + lr * kRowBytes + 16 * G;
+        // chunk 2 ks + G of row lr, read like a K fragment (bases for ks % 4,
+        // immediate 128 (ks / 4))
+        const lds_u8* qslot = ring + wave * kSlotBytes;
+        int qb[4];
 #pragma unroll
-        for (int ks = 0; ks < 36; ++ks) qf[ks] = *(const lds_bf16x8*)(qrow + 32 * ks);
+        for (int k4 = 0; k4 < 4; ++k4) qb[k4] = lr * kRowBytes + ((((2 * k4 + G) ^ swz(lr)) & 7) << 4);
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) qf[ks] = *(const lds_bf16x8*)(qslot + qb[ks & 3] + (ks >> 2) * 128);
     }
     __syncthreads();   // every wave holds its query fragments: the ring is free
     issue_half(0);
@@ -565,9 +578,11 @@ void decode_bf16_kernel(DecodeParams p) {
     // 16 (bk % 2) .. + 15 of a 32-dim tile and tokens 16 k2 + 4 G + e (first
     // read) and + 8 (second read), e = (lane % 16) / 4; the lane supplies dims
     // 4 (lane % 4) .. + 3 of its token.  Dim tile dq of quarter w starts at dim
-    // 128 w + 32 dq: chunk 16 w + 4 dq + 2 (bk % 2) + (lane % 4) / 2, and every
-    // token read has swizzle 2 e + G (the XOR touches the 3 low chunk bits
-    // only, so 16 w and 4 (dq / 2) stay outside it).
+    // 128 w + 32 dq: chunk 16 w + 4 dq + 2 (bk % 2) + (lane % 4) / 2.  The
+    // first read's tokens have swizzle swz(4 G + e), the second read's that
+    // value ^ 2, i.e. byte offset ^ 32 (the XOR touches the 3 low chunk bits
+    // only, so 16 w and 4 (dq / 2) stay outside it, and every other term of
+    // the offset is a multiple of 128).
     int tr_off[2];
     {
         const int li = lane & 15, e = li >> 2, cc = li & 3, dh = (lane >> 4) & 1;
@@ -615,7 +630,7 @@ void decode_bf16_kernel(DecodeParams p) {
         const int k2 = i >> 2, dq = i & 3;
         const int off = tr_off[dq & 1] + (dq >> 1) * 128 + k2 * 16 * kRowBytes;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off + 8 * kRowBytes));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + ((off ^ 32) + 8 * kRowBytes)));
         return __builtin_bit_cast(bf16x8_t, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
     };
 

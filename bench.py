@@ -31,7 +31,10 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 FLOP_PER_ROW_TOKEN = 2 * (576 + 512)
 KERNEL_SRC = os.path.join(ROOT, "mla_latent_decode_absorbed_amd", "csrc", "mla_kernels.hip")
-PMC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_c2_pmc.json")
+# rocprofv3 counter summaries (HBM traffic, MFMA/LDS utilisation) of the decode
+# kernel on a workload, used while the kernel sources hash to the profiled ones
+PMC_FILES = {"c2": os.path.join(ROOT, "profiles", "decode_kernel_c2_pmc.json"),
+             "c4": os.path.join(ROOT, "profiles", "decode_fp8_kernel_c4_pmc.json")}
 
 WORKLOAD_NAMES = {
     "c2": "DeepSeek-V3-shape decode on one unsharded cache: batch 64, q_len 1, 128 heads, "
@@ -225,12 +228,16 @@ def main(argv=None) -> int:
         achieved = acc["flops"] / (kern_avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": round(achieved / peak_tf, 4)}
-    traffic = None
-    if os.path.exists(PMC_FILE) and args.config == "c2" and args.num_splits == 0:
-        pmc = json.load(open(PMC_FILE))
+    traffic, counters = None, None
+    pmc_file = PMC_FILES.get(args.config)
+    if pmc_file and os.path.exists(pmc_file) and args.num_splits == 0 and args.seed is None:
+        pmc = json.load(open(pmc_file))
         if pmc.get("kernel_source_sha256_16") == kernel_source_hash():
             traffic = pmc.get("hbm_bytes_per_launch")
+            counters = {k: pmc.get(k) for k in ("MfmaUtil_percent", "LdsUtil_percent",
+                                                "LdsBankConflict_per_access", "mfma_flops_per_launch")}
     roof["traffic"] = traffic
+    roof["counters"] = counters
     roof["kernel_ms"] = round(kern_avg_ms, 5)
     roof["algorithmic_bytes_per_launch"] = k_bytes
 

@@ -7,4 +7,5 @@ from .mla_oracle import (  # noqa: F401
     bf16_bits_to_f64, e4m3_bits_to_f64, gather_request_rows, visible_lengths,
     attend_rows, decode_partial_ref, merge_ref, dcp_shard_len, dcp_shard_positions,
     absorb_query, mha_unabsorbed_ref,
+    query_prep_ref, bf16_encode, e4m3_encode, E4M3_MAX, query_prep_codes,
 )

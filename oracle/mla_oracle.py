@@ -244,3 +244,83 @@ def mha_unabsorbed_ref(q_nope, q_pe, kv_c, k_pe, w_uk, w_uv, scale):
         lses.append(mu + np.log(l))
         scores.append(s)
     return np.stack(outs), np.array(lses), np.stack(scores).reshape(H, n)
+
+
+# --------------------------------------------------------------------------
+# query preparation: absorption, concatenation and quantisation of the query
+# --------------------------------------------------------------------------
+# The decode path consumes the absorbed query: head h's no-rope part is mapped
+# into the latent space by the per-head W_UK_T batched matmul (page 1,
+# "实现拆解" item 5; page 4, "MLA Prefill vs Decode", the query absorbed by an
+# einsum into the latent space), then joined with the rope part, either as a
+# plain concatenation or as a concatenation quantised to fp8 with a per-tensor
+# query scale (page 2, the ``forward_impl`` decode excerpt:
+# ``_decode_concat_quant_fp8_op(mqa_ql_nope, mqa_q_pe, self._q_scale)``).
+def query_prep_ref(q_nope: np.ndarray, q_pe: np.ndarray, w_uk_lp: np.ndarray) -> np.ndarray:
+    """Exact absorbed query rows: [R][H][512 + 64] in fp64.
+
+    q_nope [R][H][P], q_pe [R][H][64], w_uk_lp [H][512][P], where w_uk_lp[h][l][p]
+    is W_UK_T[h][p][l] (the weights stored latent-major).  Each (row, head) is
+    ``absorb_query`` of that row: q_lat[l] = sum_p q_nope[p] W_UK_T[h][p][l].
+    """
+    R, H, _ = q_nope.shape
+    w_uk = np.transpose(w_uk_lp, (0, 2, 1))            # [H][P][512]
+    return np.stack([absorb_query(q_nope[r], q_pe[r], w_uk) for r in range(R)])
+
+
+def bf16_encode(x: np.ndarray) -> np.ndarray:
+    """float64 -> bfloat16 bit patterns (uint16), round to nearest, ties to even.
+
+    A finite bf16 has 8 significant bits: values in [2^e, 2^(e+1)) are spaced
+    2^(e-7), down to the subnormal spacing 2^-133 below 2^-126.  Values past the
+    largest finite bf16 (by half a spacing or more) round to infinity.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    spacing = np.exp2(np.maximum(e, -126.0) - 7.0)
+    q = np.rint(a / spacing) * spacing                  # rint: ties to even
+    q = np.where(q >= 2.0 ** 128, np.inf, q)
+    q = np.where(np.isnan(x), np.nan, q)
+    v = np.where(np.signbit(x), -q, q).astype(np.float32)   # exact: q is a bf16 value
+    return (v.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+#: largest finite OCP e4m3 magnitude, 1.75 * 2^8
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """float64 -> OCP FP8 E4M3 codes (uint8), round to nearest, ties to even,
+    saturating: magnitudes above 448 give +-448 (a quantiser with a fixed scale
+    clamps to the format's range; the format has no infinities).
+
+    Normal values in [2^e, 2^(e+1)), e >= -6, have 4 significant bits (spacing
+    2^(e-3)); below 2^-6 the subnormal spacing is 2^-9.  NaN gives 0x7F.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    # magnitudes of 1024 and more (and infinities) saturate like 1024; NaN is
+    # set aside and coded at the end
+    a = np.where(np.isnan(x), 0.0, np.minimum(np.abs(x), 1024.0))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    spacing = np.exp2(np.maximum(e, -6.0) - 3.0)
+    q = np.minimum(np.rint(a / spacing) * spacing, E4M3_MAX)
+    ee = np.floor(np.log2(np.where(q > 0, q, 1.0)))
+    normal = q >= 2.0 ** -6
+    E = np.where(normal, ee + 7.0, 0.0)
+    M = np.where(normal, (q / np.exp2(ee) - 1.0) * 8.0, q / 2.0 ** -9)
+    code = (E.astype(np.int64) << 3) | np.rint(M).astype(np.int64)
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    code = np.where(np.isnan(x), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def query_prep_codes(q_exact: np.ndarray, out_dtype: str, q_scale: float = 1.0) -> np.ndarray:
+    """Encode exact query values as the prepared query's storage: bf16 bit
+    patterns, or e4m3 codes of the value divided by the per-tensor q_scale
+    (the division taken in fp32, as the stored scale is an fp32 number)."""
+    if out_dtype == "bf16":
+        return bf16_encode(q_exact)
+    if out_dtype == "fp8":
+        return e4m3_encode(np.float32(q_exact) / np.float32(q_scale))
+    raise ValueError(out_dtype)

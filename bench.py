@@ -140,6 +140,94 @@ def cpu_baseline(inp, budget_s: float = 20.0) -> dict:
                       f"{done_bytes / 1e6:.1f} MB of KV, {spent:.2f} s of fp64 numpy on the host"}
 
 
+def bench_query_prep(args) -> int:
+    """mla_query_prep (W_UK_T absorption + rope concat, bf16 or e4m3 storage) on
+    the query rows and heads of a decode workload, P = 128.  The weights rotate
+    over copies totalling more than the 256 MB Infinity Cache (one layer's
+    weights are read once per decode step).  Prints ONE JSON line."""
+    import torch
+    import mla_latent_decode_absorbed_amd as mla
+    import workloads
+
+    dev = torch.device("cuda:0")
+    c = workloads.QPREP_CONFIGS[args.config]
+    R, H, P = c["rows"], c["heads"], 128
+    fp8 = args.config == "c4"
+    inp = workloads.make_query_prep_inputs(R, H, P, seed=args.seed or 0, device=dev, fp8=fp8)
+    w_bytes = inp.w_uk.numel() * 2
+    n_w = max(2, -(-(300 << 20) // w_bytes))
+    ws = [inp.w_uk] + [inp.w_uk.clone() for _ in range(n_w - 1)]
+    out = torch.empty((R, H, 576), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+    e = 1 if fp8 else 2
+    alg = w_bytes + R * H * P * 2 + R * H * 64 * 2 + R * H * 576 * e + (4 if fp8 else 0)
+    flops = 2 * R * H * P * 512
+    torch.cuda.synchronize()
+
+    # checked once through the binding, then called with pre-built arguments so
+    # that the loop times the GPU, not the per-call argument marshalling
+    mla.query_prep(inp.q_nope, inp.q_pe, inp.w_uk, out, q_scale=inp.q_scale)
+    desc = mla.QueryPrepDesc(R, H, P, mla.FP8_E4M3 if fp8 else mla.BF16)
+    stream = torch.cuda.current_stream().cuda_stream
+    call = mla.lib.mla_query_prep
+    qs_ptr = inp.q_scale.data_ptr() if fp8 else None
+    args_of = [(ctypes.byref(desc), inp.q_nope.data_ptr(), inp.q_pe.data_ptr(), w.data_ptr(), qs_ptr,
+                out.data_ptr(), stream) for w in ws]
+
+    def step(i):
+        if call(*args_of[i % n_w]) != mla.OK:
+            raise RuntimeError("mla_query_prep failed")
+
+    step(0)
+    torch.cuda.synchronize()
+    n_warm, t_w = 1, time.perf_counter()
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
+        step(n_warm)
+        n_warm += 1
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    ms = wall * 1e3 / args.steps
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    res = {
+        "metric": "MLA query preparation GB/s (fraction of MI355X HBM roofline)",
+        "value": round(alg / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) query, N(0,1/P) W_UK_T, bf16)",
+        "config": {"workload": f"{args.config} query rows and heads: rows {R}, heads {H}, P {P}, "
+                               f"out {'e4m3 (q_scale 1/64)' if fp8 else 'bf16'}",
+                   "rows": R, "heads": H, "nope_dim": P, "weight_copies_rotated": n_w},
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel_ms": round(kern_ms, 5),
+                     "algorithmic_bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from oracle import bf16_bits_to_f64, query_prep_ref
+        f64 = lambda t: bf16_bits_to_f64(t.view(torch.int16).cpu().numpy())
+        qn, qp, w = f64(inp.q_nope), f64(inp.q_pe), f64(inp.w_uk)
+        done, spent = 0, 0.0
+        while done < R and spent < 20.0:
+            t = time.perf_counter()
+            query_prep_ref(qn[done:done + 1], qp[done:done + 1], w)
+            spent += time.perf_counter() - t
+            done += 1
+        per_row = (H * P * 2 + H * 64 * 2 + H * 576 * e)
+        res["cpu_baseline"] = {"value": round((w_bytes * done / R + per_row * done) / spent / 1e9, 4),
+                               "unit": "GB/s", "cores": int(os.cpu_count() or 1), "kind": "oracle",
+                               "sample": f"{done} of {R} rows (all heads), {spent:.2f} s of fp64 numpy"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,12 +240,18 @@ def main(argv=None) -> int:
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--op", default="decode", choices=["decode", "qprep"],
+                    help="decode (default): mla_decode_partial; qprep: mla_query_prep on the "
+                         "workload's query rows and heads")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "DCP shards are materialised on one device, so run with --gpus 1.", file=sys.stderr)
         return 2
+
+    if args.op == "qprep":
+        return bench_query_prep(args)
 
     import torch
     import mla_latent_decode_absorbed_amd as mla

@@ -152,6 +152,39 @@ int mla_decode_partial_timed(const mla_decode_desc* desc, const void* q, const v
 int mla_merge_states(const float* outs, const float* lses, int32_t n, int32_t rows,
                      void* out, float* lse, int32_t out_dtype, void* stream);
 
+/* Shape and type descriptor of a query preparation. */
+typedef struct mla_query_prep_desc {
+    int32_t rows;       /* query rows R >= 0 (requests x query tokens) */
+    int32_t num_heads;  /* H >= 1 */
+    int32_t nope_dim;   /* P: per-head no-rope query width, a multiple of 16 in 16 .. 256 */
+    int32_t out_dtype;  /* MLA_BF16 or MLA_FP8_E4M3 */
+} mla_query_prep_desc;
+
+/* Prepare the decode query: absorb each head's no-rope part into the latent
+ * space through W_UK_T and join the rope part (page 1, "实现拆解" item 5, the
+ * W_UK_T batched matmul; page 4, "MLA Prefill vs Decode", the query absorbed
+ * into the latent space; page 2, the decode section of the forward_impl
+ * excerpt: nope and pe concatenated, or concatenated and quantised to fp8
+ * with a per-tensor query scale).  For every row r and head h:
+ *     q_out[r][h][0:512]   = sum_p q_nope[r][h][p] * W_UK_T[h][p][0:512]   (fp32 sums)
+ *     q_out[r][h][512:576] = q_pe[r][h][0:64]
+ * stored as bf16 (round to nearest even), or for MLA_FP8_E4M3 as the e4m3
+ * code of value / q_scale (fp32 division; round to nearest even, saturating
+ * at +-448).  The result is the `q` mla_decode_partial takes; with fp8 the
+ * caller folds q_scale into the decode's `scale`.
+ *   q_nope   device bf16 [R][H][P], 16-byte aligned
+ *   q_pe     device bf16 [R][H][64], 16-byte aligned
+ *   w_uk     device bf16 [H][512][P], 16-byte aligned: w_uk[h][l][p] =
+ *            W_UK_T[h][p][l] (the weights stored latent-major, a one-time
+ *            permutation at weight load)
+ *   q_scale  device float[1], required for MLA_FP8_E4M3 (finite, > 0), NULL for bf16
+ *   q_out    device [R][H][576] of out_dtype, 16-byte aligned; must not
+ *            overlap the inputs
+ * R = 0 enqueues nothing.  Returns MLA_OK or a negative mla_status before any
+ * device work on a bad argument. */
+int mla_query_prep(const mla_query_prep_desc* desc, const void* q_nope, const void* q_pe,
+                   const void* w_uk, const float* q_scale, void* q_out, void* stream);
+
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* mla_status_string(int status);
 

@@ -9,6 +9,7 @@ and the current stream.  The entry points mirror include/mla_decode.h:
     decode_partial(desc, q, kv_cache, kv_scale, block_table, seq_lens, scale,
                    out, lse, workspace, stream=None)
     merge_states(outs, lses, n, rows, out, lse, out_dtype=F32, stream=None)
+    query_prep(q_nope, q_pe, w_uk, q_out, q_scale=None, stream=None)
 
 plus ``Decoder``, which owns a workspace and allocates outputs.
 
@@ -41,6 +42,7 @@ EXPORTS = (
     "mla_decode_partial",
     "mla_decode_partial_timed",
     "mla_merge_states",
+    "mla_query_prep",
     "mla_status_string",
 )
 
@@ -70,6 +72,16 @@ class DecodeDesc(ctypes.Structure):
         return "DecodeDesc(" + ", ".join(f"{k}={getattr(self, k)}" for k, _ in self._fields_) + ")"
 
 
+class QueryPrepDesc(ctypes.Structure):
+    """mla_query_prep_desc of include/mla_decode.h."""
+    _fields_ = [
+        ("rows", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("nope_dim", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python mla_latent_decode_absorbed_amd/build.py` "
@@ -86,6 +98,8 @@ def _load():
     lib.mla_decode_partial_timed.restype = ctypes.c_int
     lib.mla_merge_states.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp]
     lib.mla_merge_states.restype = ctypes.c_int
+    lib.mla_query_prep.argtypes = [ctypes.POINTER(QueryPrepDesc), vp, vp, vp, vp, vp, vp]
+    lib.mla_query_prep.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     return lib
@@ -202,6 +216,29 @@ def merge_states(outs, lses, n: int, rows: int, out, lse, out_dtype: int = F32, 
                               int(out_dtype), _stream(stream))
     if st != OK:
         raise MlaError(st, "mla_merge_states")
+
+
+def query_prep(q_nope, q_pe, w_uk, q_out, q_scale=None, stream=None) -> None:
+    """Enqueue mla_query_prep: q_nope [R][H][P] bf16, q_pe [R][H][64] bf16,
+    w_uk [H][512][P] bf16 (latent-major W_UK_T) -> q_out [R][H][576], bf16 when
+    q_scale is None, else e4m3 codes of value / q_scale (q_scale: a device
+    float).  Shapes and element sizes are checked first (ValueError)."""
+    if q_nope.dim() != 3 or q_pe.dim() != 3 or w_uk.dim() != 3:
+        raise ValueError("q_nope, q_pe and w_uk must be 3-d")
+    R, H, P = q_nope.shape
+    if tuple(q_pe.shape) != (R, H, ROPE_DIM) or tuple(w_uk.shape) != (H, LATENT_DIM, P):
+        raise ValueError(f"shapes {tuple(q_pe.shape)}, {tuple(w_uk.shape)} do not match q_nope {tuple(q_nope.shape)}")
+    fp8 = q_scale is not None
+    for name, x in (("q_nope", q_nope), ("q_pe", q_pe), ("w_uk", w_uk)):
+        _need(name, x, x.numel() * 2, 2)
+    _need("q_out", q_out, R * H * QK_DIM * (1 if fp8 else 2), 1 if fp8 else 2)
+    if fp8:
+        _need("q_scale", q_scale, 4, 4)
+    desc = QueryPrepDesc(int(R), int(H), int(P), FP8_E4M3 if fp8 else BF16)
+    st = lib.mla_query_prep(ctypes.byref(desc), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(q_scale),
+                            _ptr(q_out), _stream(stream))
+    if st != OK:
+        raise MlaError(st, "mla_query_prep")
 
 
 class Decoder:

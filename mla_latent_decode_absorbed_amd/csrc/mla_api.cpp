@@ -2,6 +2,7 @@
 // layout and kernel launches.  Declarations and contracts: include/mla_decode.h.
 #include "mla_decode.h"
 #include "mla_internal.h"
+#include "mla_qprep.h"
 
 #include <atomic>
 #include <math.h>
@@ -197,6 +198,33 @@ int mla_merge_states(const float* outs, const float* lses, int32_t n, int32_t ro
     mp.rows = rows;
     mp.out_bf16 = out_dtype == MLA_BF16;
     if (mla::launch_merge(mp, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+int mla_query_prep(const mla_query_prep_desc* d, const void* q_nope, const void* q_pe,
+                   const void* w_uk, const float* q_scale, void* q_out, void* stream) {
+    if (!d) return MLA_ERR_INVALID_ARG;
+    if (d->rows < 0 || d->num_heads < 1) return MLA_ERR_INVALID_ARG;
+    if (d->out_dtype != MLA_BF16 && d->out_dtype != MLA_FP8_E4M3) return MLA_ERR_INVALID_ARG;
+    if (d->nope_dim < 16 || d->nope_dim > 256 || d->nope_dim % 16 != 0) return MLA_ERR_UNSUPPORTED;
+    if (d->num_heads > (1 << 16) || (int64_t)d->rows * d->num_heads > (int64_t)1 << 28) return MLA_ERR_UNSUPPORTED;
+    if ((d->out_dtype == MLA_FP8_E4M3) != (q_scale != nullptr)) return MLA_ERR_INVALID_ARG;
+    if (d->rows == 0) return MLA_OK;
+    if (!q_nope || !q_pe || !w_uk || !q_out) return MLA_ERR_INVALID_ARG;
+    if (!aligned(q_nope, 16) || !aligned(q_pe, 16) || !aligned(w_uk, 16) || !aligned(q_out, 16) ||
+        (q_scale && !aligned(q_scale, 4)))
+        return MLA_ERR_INVALID_ARG;
+    mla::QueryPrepParams p;
+    p.q_nope = q_nope;
+    p.q_pe = q_pe;
+    p.w_uk = w_uk;
+    p.q_scale = q_scale;
+    p.q_out = q_out;
+    p.rows = d->rows;
+    p.heads = d->num_heads;
+    p.nope_dim = d->nope_dim;
+    p.out_fp8 = d->out_dtype == MLA_FP8_E4M3;
+    if (mla::launch_query_prep(p, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }
 

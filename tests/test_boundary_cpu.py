@@ -209,3 +209,34 @@ def test_build_script_loads_without_the_package():
     assert res.returncode == 0, res.stderr
     src = open(os.path.join(root, "mla_latent_decode_absorbed_amd", "build.py")).read()
     assert "from mla_latent_decode_absorbed_amd" not in src and "import mla_latent_decode_absorbed_amd" not in src
+
+
+def _qdesc(**kw):
+    d = dict(rows=4, num_heads=2, nope_dim=128, out_dtype=mla.BF16)
+    d.update(kw)
+    return mla.QueryPrepDesc(d["rows"], d["num_heads"], d["nope_dim"], d["out_dtype"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), mla.ERR_INVALID_ARG),
+    (dict(num_heads=0), mla.ERR_INVALID_ARG),
+    (dict(out_dtype=mla.F32), mla.ERR_INVALID_ARG),
+    (dict(nope_dim=136), mla.ERR_UNSUPPORTED),
+    (dict(nope_dim=272), mla.ERR_UNSUPPORTED),
+    (dict(nope_dim=0), mla.ERR_UNSUPPORTED),
+])
+def test_query_prep_rejects_bad_descriptor(kw, status):
+    d = _qdesc(**kw)
+    assert mla.lib.mla_query_prep(ctypes.byref(d), 16, 16, 16, None, 16, None) == status
+
+
+def test_query_prep_pointer_and_scale_rules():
+    d = _qdesc()
+    assert mla.lib.mla_query_prep(None, 16, 16, 16, None, 16, None) == mla.ERR_INVALID_ARG
+    assert mla.lib.mla_query_prep(ctypes.byref(d), None, 16, 16, None, 16, None) == mla.ERR_INVALID_ARG
+    assert mla.lib.mla_query_prep(ctypes.byref(d), 16, 16, 16, None, 8, None) == mla.ERR_INVALID_ARG
+    assert mla.lib.mla_query_prep(ctypes.byref(d), 16, 16, 16, 16, 16, None) == mla.ERR_INVALID_ARG
+    d8 = _qdesc(out_dtype=mla.FP8_E4M3)
+    assert mla.lib.mla_query_prep(ctypes.byref(d8), 16, 16, 16, None, 16, None) == mla.ERR_INVALID_ARG
+    # zero rows: nothing to do, no device work
+    assert mla.lib.mla_query_prep(ctypes.byref(_qdesc(rows=0)), None, None, None, None, None, None) == mla.OK

@@ -229,3 +229,43 @@ def make_config(name: str, seed: int | None = None, device="cpu", poison: bool =
     return make_decode_inputs(cfg["batch"], cfg["q_len"], cfg["heads"], lens, cfg["dtype"],
                               seed=seed, device=device, poison=poison, extra_pages=extra_pages,
                               dcp=D)
+
+
+# ---------------------------------------------------------------------------
+# query preparation inputs
+# ---------------------------------------------------------------------------
+@dataclass
+class QueryPrepInputs:
+    """Inputs of the query preparation (absorption + rope concat + storage)."""
+    q_nope: torch.Tensor     # [R][H][P] bfloat16
+    q_pe: torch.Tensor       # [R][H][64] bfloat16
+    w_uk: torch.Tensor       # [H][512][P] bfloat16, w_uk[h][l][p] = W_UK_T[h][p][l]
+    q_scale: torch.Tensor | None   # device float[1] for e4m3 output, else None
+    q_scale_value: float
+
+
+#: query-preparation shapes: the query rows and heads of the decode workloads
+#: (rows = batch x q_len), DeepSeek's no-rope width P = 128
+QPREP_CONFIGS = {
+    "c1": dict(rows=2, heads=16),
+    "c2": dict(rows=64, heads=128),
+    "c3": dict(rows=32, heads=512),
+    "c4": dict(rows=128, heads=128),
+    "c5": dict(rows=8, heads=128),
+}
+
+
+def make_query_prep_inputs(rows: int, heads: int, nope_dim: int = 128, seed: int = 0, device="cpu",
+                           fp8: bool = False, q_scale: float = 1.0 / 64.0) -> QueryPrepInputs:
+    """Seeded query-preparation inputs: q_nope and q_pe ~ N(0, 1), W_UK_T ~ N(0, 1/P)
+    (so that the absorbed values are about N(0, 1), like the decode workloads'
+    query), all rounded to bf16; the weights are laid out latent-major.  The
+    fp8 query scale is a fixed input (a calibrated per-tensor scale in a
+    model); the default 1/64 represents magnitudes up to 7."""
+    gen = make_generator(seed, device)
+    qn = torch.randn((rows, heads, nope_dim), generator=gen, device=device)
+    qp = torch.randn((rows, heads, 64), generator=gen, device=device)
+    w_t = torch.randn((heads, nope_dim, V_DIM), generator=gen, device=device) / math.sqrt(nope_dim)
+    w = w_t.transpose(1, 2).contiguous()
+    qs = torch.tensor([q_scale], dtype=torch.float32, device=device) if fp8 else None
+    return QueryPrepInputs(to_bf16(qn), to_bf16(qp), to_bf16(w), qs, float(q_scale))

@@ -324,3 +324,23 @@ def query_prep_codes(q_exact: np.ndarray, out_dtype: str, q_scale: float = 1.0) 
     if out_dtype == "fp8":
         return e4m3_encode(np.float32(q_exact) / np.float32(q_scale))
     raise ValueError(out_dtype)
+
+
+# --------------------------------------------------------------------------
+# output up-projection: latent attention output -> per-head value space
+# --------------------------------------------------------------------------
+# The attention layer's output is num_heads x v_head_dim per token (page 1,
+# "关键源码片段", the output_shape of the MultiHeadLatentAttentionWrapper
+# excerpt), while decode attends in the latent space (page 4, "MLA Prefill vs
+# Decode": W_UV is what decompresses kv_c into per-head values), so head h's
+# 512-dim latent output is mapped through that head's W_UV.
+def up_project_ref(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """out[r][h][v] = sum_l W_UV[h][v][l] * o_lat[r][h][l] in fp64.
+
+    o_lat [R][H][512], w_uv [H][Vd][512] (row v of head h holds the 512 latent
+    weights of value dim v) -> [R][H][Vd].
+    """
+    o_lat = np.asarray(o_lat, dtype=np.float64)
+    w_uv = np.asarray(w_uv, dtype=np.float64)
+    return np.stack([np.stack([w_uv[h] @ o_lat[r, h] for h in range(o_lat.shape[1])])
+                     for r in range(o_lat.shape[0])])

@@ -228,6 +228,92 @@ def bench_query_prep(args) -> int:
     return 0
 
 
+def _time_launches(step, args):
+    """Warm-up (at least W calls and --warmup-seconds), then K timed calls with
+    torch events around each; returns (ms per call by the wall clock, average
+    event-timed ms, warm-up calls run)."""
+    import torch
+    step(0)
+    torch.cuda.synchronize()
+    n_warm, t_w = 1, time.perf_counter()
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
+        step(n_warm)
+        n_warm += 1
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / args.steps, sum(a.elapsed_time(b) for a, b in evs) / args.steps, n_warm
+
+
+def bench_up_project(args) -> int:
+    """mla_up_project (latent output through W_UV, v_head_dim 128) on the rows
+    and heads of a decode workload: fp32 latent input, bf16 output.  The
+    weights rotate over copies totalling more than the 256 MB Infinity Cache.
+    Prints ONE JSON line."""
+    import torch
+    import mla_latent_decode_absorbed_amd as mla
+    import workloads
+
+    dev = torch.device("cuda:0")
+    c = workloads.QPREP_CONFIGS[args.config]
+    R, H, Vd = c["rows"], c["heads"], 128
+    inp = workloads.make_up_project_inputs(R, H, Vd, seed=args.seed or 0, device=dev)
+    w_bytes = inp.w_uv.numel() * 2
+    n_w = max(2, -(-(300 << 20) // w_bytes))
+    ws = [inp.w_uv] + [inp.w_uv.clone() for _ in range(n_w - 1)]
+    out = torch.empty((R, H, Vd), dtype=torch.bfloat16, device=dev)
+    alg = w_bytes + R * H * 512 * 4 + R * H * Vd * 2
+    flops = 2 * R * H * 512 * Vd
+    mla.up_project(inp.o_lat, inp.w_uv, out)           # checked once through the binding
+    desc = mla.UpProjectDesc(R, H, Vd, mla.F32, mla.BF16)
+    stream = torch.cuda.current_stream().cuda_stream
+    call = mla.lib.mla_up_project
+    args_of = [(ctypes.byref(desc), inp.o_lat.data_ptr(), w.data_ptr(), out.data_ptr(), stream) for w in ws]
+
+    def step(i):
+        if call(*args_of[i % n_w]) != mla.OK:
+            raise RuntimeError("mla_up_project failed")
+
+    ms, kern_ms, n_warm = _time_launches(step, args)
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    res = {
+        "metric": "MLA output up-projection GB/s (fraction of MI355X HBM roofline)",
+        "value": round(alg / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) fp32 latent output, N(0,1/512) W_UV, bf16)",
+        "config": {"workload": f"{args.config} rows and heads: rows {R}, heads {H}, v_head_dim {Vd}, "
+                               "fp32 in, bf16 out",
+                   "rows": R, "heads": H, "v_head_dim": Vd, "weight_copies_rotated": n_w},
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel_ms": round(kern_ms, 5),
+                     "algorithmic_bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import bf16_bits_to_f64, up_project_ref
+        x = inp.o_lat.double().cpu().numpy()
+        w = bf16_bits_to_f64(inp.w_uv.view(torch.int16).cpu().numpy())
+        done, spent = 0, 0.0
+        while done < R and spent < 20.0:
+            t = time.perf_counter()
+            up_project_ref(x[done:done + 1], w)
+            spent += time.perf_counter() - t
+            done += 1
+        per_row = H * 512 * 4 + H * Vd * 2
+        res["cpu_baseline"] = {"value": round((w_bytes * done / R + per_row * done) / spent / 1e9, 4),
+                               "unit": "GB/s", "cores": int(os.cpu_count() or 1), "kind": "oracle",
+                               "sample": f"{done} of {R} rows (all heads), {spent:.2f} s of fp64 numpy"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,9 +326,9 @@ def main(argv=None) -> int:
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--op", default="decode", choices=["decode", "qprep"],
+    ap.add_argument("--op", default="decode", choices=["decode", "qprep", "upproj"],
                     help="decode (default): mla_decode_partial; qprep: mla_query_prep on the "
-                         "workload's query rows and heads")
+                         "workload's query rows and heads; upproj: mla_up_project of its latent output")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -252,6 +338,8 @@ def main(argv=None) -> int:
 
     if args.op == "qprep":
         return bench_query_prep(args)
+    if args.op == "upproj":
+        return bench_up_project(args)
 
     import torch
     import mla_latent_decode_absorbed_amd as mla

@@ -185,6 +185,34 @@ typedef struct mla_query_prep_desc {
 int mla_query_prep(const mla_query_prep_desc* desc, const void* q_nope, const void* q_pe,
                    const void* w_uk, const float* q_scale, void* q_out, void* stream);
 
+/* Shape and type descriptor of an output up-projection. */
+typedef struct mla_up_project_desc {
+    int32_t rows;        /* R >= 0 (requests x query tokens) */
+    int32_t num_heads;   /* H >= 1 */
+    int32_t v_head_dim;  /* Vd: per-head value width, a multiple of 32 in 32 .. 512 */
+    int32_t in_dtype;    /* MLA_F32 or MLA_BF16: the latent output's type */
+    int32_t out_dtype;   /* MLA_F32 or MLA_BF16 */
+} mla_up_project_desc;
+
+/* Map each head's 512-dim latent attention output into its value space
+ * through W_UV (page 1, "关键源码片段": the attention output is
+ * num_heads x v_head_dim per token; page 4, "MLA Prefill vs Decode": W_UV
+ * decompresses the latent into per-head values):
+ *     out[r][h][v] = sum_l W_UV[h][v][l] * o_lat[r][h][l]
+ * with fp32 sums; an fp32 o_lat enters the bf16 matrix cores as two bf16
+ * terms (x = hi + lo to within 2^-17 |x|), so the result keeps near-fp32
+ * accuracy; a bf16 output is rounded to nearest even.
+ *   o_lat  device [R][H][512] of in_dtype, 16-byte aligned (mla_decode_partial's
+ *          or mla_merge_states' out)
+ *   w_uv   device bf16 [H][Vd][512], 16-byte aligned (row v of head h: the
+ *          512 latent weights of value dim v)
+ *   out    device [R][H][Vd] of out_dtype, 16-byte aligned; must not overlap
+ *          the inputs
+ * R = 0 enqueues nothing.  Returns MLA_OK or a negative mla_status before any
+ * device work on a bad argument. */
+int mla_up_project(const mla_up_project_desc* desc, const void* o_lat, const void* w_uv,
+                   void* out, void* stream);
+
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* mla_status_string(int status);
 

@@ -10,6 +10,7 @@ and the current stream.  The entry points mirror include/mla_decode.h:
                    out, lse, workspace, stream=None)
     merge_states(outs, lses, n, rows, out, lse, out_dtype=F32, stream=None)
     query_prep(q_nope, q_pe, w_uk, q_out, q_scale=None, stream=None)
+    up_project(o_lat, w_uv, out, stream=None)
 
 plus ``Decoder``, which owns a workspace and allocates outputs.
 
@@ -43,6 +44,7 @@ EXPORTS = (
     "mla_decode_partial_timed",
     "mla_merge_states",
     "mla_query_prep",
+    "mla_up_project",
     "mla_status_string",
 )
 
@@ -82,6 +84,17 @@ class QueryPrepDesc(ctypes.Structure):
     ]
 
 
+class UpProjectDesc(ctypes.Structure):
+    """mla_up_project_desc of include/mla_decode.h."""
+    _fields_ = [
+        ("rows", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("v_head_dim", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+    ]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python mla_latent_decode_absorbed_amd/build.py` "
@@ -100,6 +113,8 @@ def _load():
     lib.mla_merge_states.restype = ctypes.c_int
     lib.mla_query_prep.argtypes = [ctypes.POINTER(QueryPrepDesc), vp, vp, vp, vp, vp, vp]
     lib.mla_query_prep.restype = ctypes.c_int
+    lib.mla_up_project.argtypes = [ctypes.POINTER(UpProjectDesc), vp, vp, vp, vp]
+    lib.mla_up_project.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     return lib
@@ -239,6 +254,28 @@ def query_prep(q_nope, q_pe, w_uk, q_out, q_scale=None, stream=None) -> None:
                             _ptr(q_out), _stream(stream))
     if st != OK:
         raise MlaError(st, "mla_query_prep")
+
+
+def up_project(o_lat, w_uv, out, stream=None) -> None:
+    """Enqueue mla_up_project: o_lat [R][H][512] (fp32 or bf16), w_uv [H][Vd][512]
+    bf16 -> out [R][H][Vd] (fp32 or bf16, by the tensor's element size).
+    Shapes and element sizes are checked first (ValueError)."""
+    if o_lat.dim() != 3 or w_uv.dim() != 3:
+        raise ValueError("o_lat and w_uv must be 3-d")
+    R, H, L = o_lat.shape
+    Vd = w_uv.shape[1]
+    if L != LATENT_DIM or tuple(w_uv.shape) != (H, Vd, LATENT_DIM):
+        raise ValueError(f"shapes {tuple(o_lat.shape)}, {tuple(w_uv.shape)} do not match")
+    if o_lat.element_size() not in (2, 4) or out.element_size() not in (2, 4):
+        raise ValueError("o_lat and out must be fp32 or bf16")
+    _need("o_lat", o_lat, R * H * LATENT_DIM * o_lat.element_size())
+    _need("w_uv", w_uv, H * Vd * LATENT_DIM * 2, 2)
+    _need("out", out, R * H * Vd * out.element_size())
+    desc = UpProjectDesc(int(R), int(H), int(Vd), F32 if o_lat.element_size() == 4 else BF16,
+                         F32 if out.element_size() == 4 else BF16)
+    st = lib.mla_up_project(ctypes.byref(desc), _ptr(o_lat), _ptr(w_uv), _ptr(out), _stream(stream))
+    if st != OK:
+        raise MlaError(st, "mla_up_project")
 
 
 class Decoder:

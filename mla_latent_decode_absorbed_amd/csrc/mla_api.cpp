@@ -3,6 +3,7 @@
 #include "mla_decode.h"
 #include "mla_internal.h"
 #include "mla_qprep.h"
+#include "mla_upproj.h"
 
 #include <atomic>
 #include <math.h>
@@ -225,6 +226,30 @@ int mla_query_prep(const mla_query_prep_desc* d, const void* q_nope, const void*
     p.nope_dim = d->nope_dim;
     p.out_fp8 = d->out_dtype == MLA_FP8_E4M3;
     if (mla::launch_query_prep(p, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+int mla_up_project(const mla_up_project_desc* d, const void* o_lat, const void* w_uv, void* out,
+                   void* stream) {
+    if (!d) return MLA_ERR_INVALID_ARG;
+    if (d->rows < 0 || d->num_heads < 1) return MLA_ERR_INVALID_ARG;
+    if ((d->in_dtype != MLA_F32 && d->in_dtype != MLA_BF16) || (d->out_dtype != MLA_F32 && d->out_dtype != MLA_BF16))
+        return MLA_ERR_INVALID_ARG;
+    if (d->v_head_dim < 32 || d->v_head_dim > 512 || d->v_head_dim % 32 != 0) return MLA_ERR_UNSUPPORTED;
+    if (d->num_heads > (1 << 16) || (int64_t)d->rows * d->num_heads > (int64_t)1 << 26) return MLA_ERR_UNSUPPORTED;
+    if (d->rows == 0) return MLA_OK;
+    if (!o_lat || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+    if (!aligned(o_lat, 16) || !aligned(w_uv, 16) || !aligned(out, 16)) return MLA_ERR_INVALID_ARG;
+    mla::UpProjParams p;
+    p.o_lat = o_lat;
+    p.w_uv = w_uv;
+    p.out = out;
+    p.rows = d->rows;
+    p.heads = d->num_heads;
+    p.vdim = d->v_head_dim;
+    p.in_f32 = d->in_dtype == MLA_F32;
+    p.out_f32 = d->out_dtype == MLA_F32;
+    if (mla::launch_up_project(p, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }
 

@@ -240,3 +240,30 @@ def test_query_prep_pointer_and_scale_rules():
     assert mla.lib.mla_query_prep(ctypes.byref(d8), 16, 16, 16, None, 16, None) == mla.ERR_INVALID_ARG
     # zero rows: nothing to do, no device work
     assert mla.lib.mla_query_prep(ctypes.byref(_qdesc(rows=0)), None, None, None, None, None, None) == mla.OK
+
+
+def _udesc(**kw):
+    d = dict(rows=4, num_heads=2, v_head_dim=128, in_dtype=mla.F32, out_dtype=mla.BF16)
+    d.update(kw)
+    return mla.UpProjectDesc(d["rows"], d["num_heads"], d["v_head_dim"], d["in_dtype"], d["out_dtype"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), mla.ERR_INVALID_ARG),
+    (dict(num_heads=0), mla.ERR_INVALID_ARG),
+    (dict(in_dtype=mla.FP8_E4M3), mla.ERR_INVALID_ARG),
+    (dict(out_dtype=7), mla.ERR_INVALID_ARG),
+    (dict(v_head_dim=48), mla.ERR_UNSUPPORTED),
+    (dict(v_head_dim=544), mla.ERR_UNSUPPORTED),
+    (dict(v_head_dim=0), mla.ERR_UNSUPPORTED),
+])
+def test_up_project_rejects_bad_descriptor(kw, status):
+    assert mla.lib.mla_up_project(ctypes.byref(_udesc(**kw)), 16, 16, 16, None) == status
+
+
+def test_up_project_pointer_rules():
+    d = _udesc()
+    assert mla.lib.mla_up_project(None, 16, 16, 16, None) == mla.ERR_INVALID_ARG
+    assert mla.lib.mla_up_project(ctypes.byref(d), None, 16, 16, None) == mla.ERR_INVALID_ARG
+    assert mla.lib.mla_up_project(ctypes.byref(d), 16, 16, 8, None) == mla.ERR_INVALID_ARG
+    assert mla.lib.mla_up_project(ctypes.byref(_udesc(rows=0)), None, None, None, None) == mla.OK

@@ -269,3 +269,24 @@ def make_query_prep_inputs(rows: int, heads: int, nope_dim: int = 128, seed: int
     w = w_t.transpose(1, 2).contiguous()
     qs = torch.tensor([q_scale], dtype=torch.float32, device=device) if fp8 else None
     return QueryPrepInputs(to_bf16(qn), to_bf16(qp), to_bf16(w), qs, float(q_scale))
+
+
+# ---------------------------------------------------------------------------
+# output up-projection inputs
+# ---------------------------------------------------------------------------
+@dataclass
+class UpProjectInputs:
+    o_lat: torch.Tensor      # [R][H][512] float32 or bfloat16 (latent attention output)
+    w_uv: torch.Tensor       # [H][Vd][512] bfloat16
+
+
+def make_up_project_inputs(rows: int, heads: int, vdim: int = 128, seed: int = 0, device="cpu",
+                           in_dtype: str = "f32") -> UpProjectInputs:
+    """Seeded up-projection inputs: the latent output ~ N(0, 1) in fp32 (or
+    rounded to bf16), W_UV ~ N(0, 1/512) rounded to bf16, laid out [H][Vd][512]."""
+    gen = make_generator(seed, device)
+    o = torch.randn((rows, heads, V_DIM), generator=gen, device=device)
+    w = torch.randn((heads, vdim, V_DIM), generator=gen, device=device) / math.sqrt(V_DIM)
+    if in_dtype == "bf16":
+        o = to_bf16(o)
+    return UpProjectInputs(o.contiguous(), to_bf16(w).contiguous())

@@ -8,5 +8,5 @@ from .mla_oracle import (  # noqa: F401
     attend_rows, decode_partial_ref, merge_ref, dcp_shard_len, dcp_shard_positions,
     absorb_query, mha_unabsorbed_ref,
     query_prep_ref, bf16_encode, e4m3_encode, E4M3_MAX, query_prep_codes,
-    up_project_ref,
+    up_project_ref, gather_cache_ref, merge_two_ref,
 )

@@ -344,3 +344,44 @@ def up_project_ref(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
     w_uv = np.asarray(w_uv, dtype=np.float64)
     return np.stack([np.stack([w_uv[h] @ o_lat[r, h] for h in range(o_lat.shape[1])])
                      for r in range(o_lat.shape[0])])
+
+
+# --------------------------------------------------------------------------
+# chunked-prefill context: paged gather with dequantisation, two-way merge
+# --------------------------------------------------------------------------
+# A prefill with cached context reads the context chunk by chunk: each chunk's
+# latent cache rows are gathered out of the paged cache into a contiguous
+# buffer and dequantised (page 4, "与非 DCP 的流程对比":
+# gather_and_maybe_dequant_cache; page 2, "实现拆解" items 3 and 4, the gather
+# whose requests start at seq_starts), and the chunks' partial attention
+# results are merged with the LSE rule (page 4, "Chunked Prefill 与 LSE
+# Merge": merge_attn_states of a prefix and a suffix result).
+def gather_cache_ref(kv_cache: np.ndarray, block_table: np.ndarray, seq_starts: np.ndarray,
+                     chunk_lens: np.ndarray, kv_dtype: str, kv_scale: float = 1.0) -> np.ndarray:
+    """Gathered latent rows as bf16 bit patterns: [sum chunk_lens][576] uint16.
+
+    kv_cache holds bf16 bit patterns [P][64][576] (uint16) or e4m3 codes
+    (uint8).  Request b contributes its logical tokens seq_starts[b] ..
+    seq_starts[b] + chunk_lens[b] - 1 (token t at row t % 64 of page
+    block_table[b][t // 64]), in order, after request b - 1's.  bf16 rows are
+    copied; e4m3 rows become bf16(fp32(value) * fp32(kv_scale)): the fp32
+    product, rounded to nearest even.
+    """
+    out = []
+    for b in range(len(chunk_lens)):
+        t = int(seq_starts[b]) + np.arange(int(chunk_lens[b]))
+        rows = kv_cache[np.asarray(block_table[b])[t // PAGE_SIZE], t % PAGE_SIZE]
+        if kv_dtype == "bf16":
+            out.append(np.asarray(rows).view(np.uint16))
+        else:
+            v = e4m3_bits_to_f64(rows).astype(np.float32) * np.float32(kv_scale)
+            out.append(bf16_encode(v.astype(np.float64)))
+    if not out:
+        return np.zeros((0, kv_cache.shape[-1]), dtype=np.uint16)
+    return np.concatenate(out, axis=0).reshape(-1, kv_cache.shape[-1])
+
+
+def merge_two_ref(prefix_out, prefix_lse, suffix_out, suffix_lse):
+    """merge_attn_states of a prefix and a suffix partial result: the LSE merge
+    of exactly two inputs (``merge_ref`` with n = 2)."""
+    return merge_ref(np.stack([prefix_out, suffix_out]), np.stack([prefix_lse, suffix_lse]))

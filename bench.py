@@ -314,6 +314,76 @@ def bench_up_project(args) -> int:
     return 0
 
 
+def bench_gather(args) -> int:
+    """mla_gather_cache of each request's first min(seq_len, 2048) cache tokens
+    (a chunked-prefill context chunk) out of the workload's paged cache into a
+    contiguous bf16 buffer (e4m3 caches dequantised).  Prints ONE JSON line."""
+    import numpy as np
+    import torch
+    import mla_latent_decode_absorbed_amd as mla
+    import workloads
+
+    dev = torch.device("cuda:0")
+    kw = dict(shard_only=0) if args.config == "c3" else {}
+    inp = workloads.make_config(args.config, seed=args.seed, device=dev, poison=False, extra_pages=0, **kw)
+    sl = inp.seq_lens.cpu().numpy()
+    lens = np.minimum(sl, 2048).astype(np.int32)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    starts = torch.zeros(len(sl), dtype=torch.int32, device=dev)
+    total = int(lens.sum())
+    out = torch.empty((total, 576), dtype=torch.bfloat16, device=dev)
+    e = 2 if inp.dtype == "bf16" else 1
+    alg = total * 576 * (e + 2) + int(((lens + 63) // 64).sum()) * 4 + (2 * len(sl) + 1) * 4
+    copies = [inp.kv_cache] + [inp.kv_cache.clone() for _ in range(max(args.copies, 1) - 1)]
+    mla.gather_cache(inp.kv_cache, inp.block_table, starts, cu, total, out, kv_scale=inp.kv_scale)
+    call = mla.lib.mla_gather_cache
+    stream = torch.cuda.current_stream().cuda_stream
+    kvs = inp.kv_scale.data_ptr() if inp.kv_scale is not None else None
+    dt = mla.BF16 if inp.dtype == "bf16" else mla.FP8_E4M3
+    B, maxp = inp.block_table.shape
+    args_of = [(c.data_ptr(), dt, kvs, inp.block_table.data_ptr(), B, c.shape[0], maxp, starts.data_ptr(),
+                cu.data_ptr(), ctypes.c_int64(total), out.data_ptr(), stream) for c in copies]
+
+    def step(i):
+        if call(*args_of[i % len(copies)]) != mla.OK:
+            raise RuntimeError("mla_gather_cache failed")
+
+    ms, kern_ms, n_warm = _time_launches(step, args)
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    res = {
+        "metric": "MLA context gather GB/s (fraction of MI355X HBM roofline)",
+        "value": round(alg / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": inp.dtype, "data": "synthetic (seeded N(0,1) latent cache, shuffled 64-token pages)",
+        "config": {"workload": f"{args.config}: first min(seq_len, 2048) tokens of each of {B} requests "
+                               f"({total} rows) out of the {inp.dtype} paged cache into bf16",
+                   "rows": total, "cache_copies_rotated": len(copies)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel_ms": round(kern_ms, 5),
+                     "algorithmic_bytes_per_launch": alg},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import gather_cache_ref
+        cache = inp.kv_cache.cpu()
+        cache = cache.view(torch.int16).numpy().view(np.uint16) if inp.dtype == "bf16" else cache.numpy()
+        bt = inp.block_table.cpu().numpy()
+        st = np.zeros(len(sl), dtype=np.int64)
+        done, spent, rows_done = 0, 0.0, 0
+        while done < B and spent < 20.0:
+            t = time.perf_counter()
+            gather_cache_ref(cache, bt[done:done + 1], st[done:done + 1], lens[done:done + 1], inp.dtype,
+                             inp.kv_scale_value)
+            spent += time.perf_counter() - t
+            rows_done += int(lens[done])
+            done += 1
+        res["cpu_baseline"] = {"value": round(rows_done * 576 * (e + 2) / spent / 1e9, 4), "unit": "GB/s",
+                               "cores": int(os.cpu_count() or 1), "kind": "oracle",
+                               "sample": f"{done} of {B} requests ({rows_done} rows), {spent:.2f} s of numpy"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -326,9 +396,10 @@ def main(argv=None) -> int:
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--op", default="decode", choices=["decode", "qprep", "upproj"],
+    ap.add_argument("--op", default="decode", choices=["decode", "qprep", "upproj", "gather"],
                     help="decode (default): mla_decode_partial; qprep: mla_query_prep on the "
-                         "workload's query rows and heads; upproj: mla_up_project of its latent output")
+                         "workload's query rows and heads; upproj: mla_up_project of its latent output; "
+                         "gather: mla_gather_cache of each request's first 2048 cache tokens")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -340,6 +411,8 @@ def main(argv=None) -> int:
         return bench_query_prep(args)
     if args.op == "upproj":
         return bench_up_project(args)
+    if args.op == "gather":
+        return bench_gather(args)
 
     import torch
     import mla_latent_decode_absorbed_amd as mla

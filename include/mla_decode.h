@@ -213,6 +213,46 @@ typedef struct mla_up_project_desc {
 int mla_up_project(const mla_up_project_desc* desc, const void* o_lat, const void* w_uv,
                    void* out, void* stream);
 
+/* Gather the latent cache rows of each request's context chunk into one
+ * contiguous bf16 buffer, dequantising an e4m3 cache (page 4, "与非 DCP 的流程对比":
+ * each prefill chunk's context is taken out of the paged cache by
+ * gather_and_maybe_dequant_cache; page 2, "实现拆解" items 3 and 4: the
+ * gather whose requests start at seq_starts).  Output row cu_lens[b] + i is
+ * token seq_starts[b] + i of request b (row t % 64 of page
+ * block_table[b][t / 64]), for i < cu_lens[b + 1] - cu_lens[b]:
+ *   bf16 cache:  copied;
+ *   e4m3 cache:  bf16(fp32(value) * kv_scale), the fp32 product rounded to
+ *                nearest even.
+ *   kv_cache     device [num_pages][64][576] of kv_dtype, 16-byte aligned
+ *   kv_scale     device float[1] for MLA_FP8_E4M3 (NULL for MLA_BF16)
+ *   block_table  device int32 [batch][max_pages_per_seq]
+ *   seq_starts   device int32 [batch], >= 0
+ *   cu_lens      device int32 [batch + 1], non-decreasing, cu_lens[0] = 0
+ *   total_rows   rows to write (normally cu_lens[batch], which the host passes
+ *                because it sizes the launch); rows past cu_lens[batch] are zeros
+ *   out          device bf16 [total_rows][576], 16-byte aligned
+ * A row whose token lies past the block table or whose page id is outside
+ * [0, num_pages) is written as zeros. */
+int mla_gather_cache(const void* kv_cache, int32_t kv_dtype, const float* kv_scale,
+                     const int32_t* block_table, int32_t batch, int32_t num_pages,
+                     int32_t max_pages_per_seq, const int32_t* seq_starts, const int32_t* cu_lens,
+                     int64_t total_rows, void* out, void* stream);
+
+/* merge_attn_states of a prefix and a suffix partial result (page 4,
+ * "Chunked Prefill 与 LSE Merge"): per row, with w_i = exp(lse_i - max),
+ *   out = (w_p prefix + w_s suffix) / (w_p + w_s),  lse = max + ln(w_p + w_s);
+ * a -inf LSE marks an empty partial; two empty inputs give out = 0, lse = -inf.
+ * LSE values must be finite or -inf.
+ *   prefix_out, suffix_out  device [rows][head_dim] of in_dtype (MLA_F32 or MLA_BF16)
+ *   prefix_lse, suffix_lse  device float [rows]
+ *   out                     device [rows][head_dim] of out_dtype (MLA_F32 or MLA_BF16)
+ *   lse                     device float [rows], or NULL when not wanted
+ * head_dim: a multiple of 4 in 4 .. 4096; every pointer 16-byte aligned.  out
+ * may not overlap the inputs. */
+int mla_merge_two_states(int32_t rows, int32_t head_dim, int32_t in_dtype, int32_t out_dtype,
+                         const void* prefix_out, const float* prefix_lse, const void* suffix_out,
+                         const float* suffix_lse, void* out, float* lse, void* stream);
+
 /* Human-readable text of a status code (static storage; never NULL). */
 const char* mla_status_string(int status);
 

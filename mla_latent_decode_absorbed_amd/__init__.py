@@ -11,6 +11,8 @@ and the current stream.  The entry points mirror include/mla_decode.h:
     merge_states(outs, lses, n, rows, out, lse, out_dtype=F32, stream=None)
     query_prep(q_nope, q_pe, w_uk, q_out, q_scale=None, stream=None)
     up_project(o_lat, w_uv, out, stream=None)
+    gather_cache(kv_cache, block_table, seq_starts, cu_lens, total_rows, out, kv_scale=None, stream=None)
+    merge_two_states(prefix_out, prefix_lse, suffix_out, suffix_lse, out, lse=None, stream=None)
 
 plus ``Decoder``, which owns a workspace and allocates outputs.
 
@@ -45,6 +47,8 @@ EXPORTS = (
     "mla_merge_states",
     "mla_query_prep",
     "mla_up_project",
+    "mla_gather_cache",
+    "mla_merge_two_states",
     "mla_status_string",
 )
 
@@ -115,6 +119,10 @@ def _load():
     lib.mla_query_prep.restype = ctypes.c_int
     lib.mla_up_project.argtypes = [ctypes.POINTER(UpProjectDesc), vp, vp, vp, vp]
     lib.mla_up_project.restype = ctypes.c_int
+    lib.mla_gather_cache.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp, ctypes.c_int64, vp, vp]
+    lib.mla_gather_cache.restype = ctypes.c_int
+    lib.mla_merge_two_states.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.mla_merge_two_states.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     return lib
@@ -276,6 +284,50 @@ def up_project(o_lat, w_uv, out, stream=None) -> None:
     st = lib.mla_up_project(ctypes.byref(desc), _ptr(o_lat), _ptr(w_uv), _ptr(out), _stream(stream))
     if st != OK:
         raise MlaError(st, "mla_up_project")
+
+
+def gather_cache(kv_cache, block_table, seq_starts, cu_lens, total_rows: int, out, kv_scale=None,
+                 stream=None) -> None:
+    """Enqueue mla_gather_cache: rows seq_starts[b] .. of each request's chunk
+    (cu_lens [B + 1] output offsets) out of the paged cache [P][64][576]
+    (bf16, or e4m3 codes with kv_scale) into out [total_rows][576] bf16."""
+    if kv_cache.dim() != 3 or tuple(kv_cache.shape[1:]) != (PAGE_SIZE, QK_DIM):
+        raise ValueError(f"kv_cache must be [pages][64][576], got {tuple(kv_cache.shape)}")
+    fp8 = kv_cache.element_size() == 1
+    if fp8 != (kv_scale is not None):
+        raise ValueError("kv_scale is required for an e4m3 cache and must be None for bf16")
+    B, maxp = block_table.shape
+    _need("block_table", block_table, B * maxp * 4, 4)
+    _need("seq_starts", seq_starts, B * 4, 4)
+    _need("cu_lens", cu_lens, (B + 1) * 4, 4)
+    _need("out", out, int(total_rows) * QK_DIM * 2, 2)
+    if kv_scale is not None:
+        _need("kv_scale", kv_scale, 4, 4)
+    st = lib.mla_gather_cache(_ptr(kv_cache), FP8_E4M3 if fp8 else BF16, _ptr(kv_scale), _ptr(block_table),
+                              int(B), int(kv_cache.shape[0]), int(maxp), _ptr(seq_starts), _ptr(cu_lens),
+                              ctypes.c_int64(int(total_rows)), _ptr(out), _stream(stream))
+    if st != OK:
+        raise MlaError(st, "mla_gather_cache")
+
+
+def merge_two_states(prefix_out, prefix_lse, suffix_out, suffix_lse, out, lse=None, stream=None) -> None:
+    """Enqueue mla_merge_two_states: [rows][head_dim] prefix and suffix partials
+    (fp32 or bf16) and their LSEs -> out (fp32 or bf16) and optionally lse."""
+    rows, hd = prefix_out.shape[0], prefix_out.shape[-1]
+    if prefix_out.numel() != rows * hd or tuple(suffix_out.shape) != tuple(prefix_out.shape):
+        raise ValueError("prefix and suffix outputs must both be [rows][head_dim]")
+    if prefix_out.dtype != suffix_out.dtype or prefix_out.element_size() not in (2, 4):
+        raise ValueError("prefix and suffix outputs must share an fp32 or bf16 dtype")
+    for name, x in (("prefix_lse", prefix_lse), ("suffix_lse", suffix_lse)) + ((("lse", lse),) if lse is not None else ()):
+        _need(name, x, rows * 4, 4)
+    _need("prefix_out", prefix_out, rows * hd * prefix_out.element_size())
+    _need("suffix_out", suffix_out, rows * hd * suffix_out.element_size())
+    _need("out", out, rows * hd * out.element_size())
+    st = lib.mla_merge_two_states(int(rows), int(hd), F32 if prefix_out.element_size() == 4 else BF16,
+                                  F32 if out.element_size() == 4 else BF16, _ptr(prefix_out), _ptr(prefix_lse),
+                                  _ptr(suffix_out), _ptr(suffix_lse), _ptr(out), _ptr(lse), _stream(stream))
+    if st != OK:
+        raise MlaError(st, "mla_merge_two_states")
 
 
 class Decoder:

@@ -4,6 +4,7 @@
 #include "mla_internal.h"
 #include "mla_qprep.h"
 #include "mla_upproj.h"
+#include "mla_gather.h"
 
 #include <atomic>
 #include <math.h>
@@ -250,6 +251,62 @@ int mla_up_project(const mla_up_project_desc* d, const void* o_lat, const void* 
     p.in_f32 = d->in_dtype == MLA_F32;
     p.out_f32 = d->out_dtype == MLA_F32;
     if (mla::launch_up_project(p, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+int mla_gather_cache(const void* kv_cache, int32_t kv_dtype, const float* kv_scale,
+                     const int32_t* block_table, int32_t batch, int32_t num_pages,
+                     int32_t max_pages_per_seq, const int32_t* seq_starts, const int32_t* cu_lens,
+                     int64_t total_rows, void* out, void* stream) {
+    if (kv_dtype != MLA_BF16 && kv_dtype != MLA_FP8_E4M3) return MLA_ERR_INVALID_ARG;
+    if (batch < 1 || num_pages < 1 || max_pages_per_seq < 1 || total_rows < 0) return MLA_ERR_INVALID_ARG;
+    if ((kv_dtype == MLA_FP8_E4M3) != (kv_scale != nullptr)) return MLA_ERR_INVALID_ARG;
+    if ((int64_t)batch * max_pages_per_seq > INT32_MAX || total_rows > ((int64_t)1 << 34)) return MLA_ERR_UNSUPPORTED;
+    if (total_rows == 0) return MLA_OK;
+    if (!kv_cache || !block_table || !seq_starts || !cu_lens || !out) return MLA_ERR_INVALID_ARG;
+    if (!aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(block_table, 4) || !aligned(seq_starts, 4) ||
+        !aligned(cu_lens, 4) || (kv_scale && !aligned(kv_scale, 4)))
+        return MLA_ERR_INVALID_ARG;
+    mla::GatherParams p;
+    p.kv = kv_cache;
+    p.kv_scale = kv_scale;
+    p.block_table = block_table;
+    p.seq_starts = seq_starts;
+    p.cu_lens = cu_lens;
+    p.out = out;
+    p.total_rows = total_rows;
+    p.batch = batch;
+    p.num_pages = num_pages;
+    p.max_pages = max_pages_per_seq;
+    p.fp8 = kv_dtype == MLA_FP8_E4M3;
+    if (mla::launch_gather_cache(p, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+int mla_merge_two_states(int32_t rows, int32_t head_dim, int32_t in_dtype, int32_t out_dtype,
+                         const void* prefix_out, const float* prefix_lse, const void* suffix_out,
+                         const float* suffix_lse, void* out, float* lse, void* stream) {
+    if (rows < 0 || head_dim < 4 || head_dim > 4096 || head_dim % 4 != 0) return MLA_ERR_INVALID_ARG;
+    if ((in_dtype != MLA_F32 && in_dtype != MLA_BF16) || (out_dtype != MLA_F32 && out_dtype != MLA_BF16))
+        return MLA_ERR_INVALID_ARG;
+    if ((int64_t)rows * head_dim > ((int64_t)1 << 32)) return MLA_ERR_UNSUPPORTED;
+    if (rows == 0) return MLA_OK;
+    if (!prefix_out || !prefix_lse || !suffix_out || !suffix_lse || !out) return MLA_ERR_INVALID_ARG;
+    if (!aligned(prefix_out, 16) || !aligned(suffix_out, 16) || !aligned(out, 16) || !aligned(prefix_lse, 4) ||
+        !aligned(suffix_lse, 4) || (lse && !aligned(lse, 4)))
+        return MLA_ERR_INVALID_ARG;
+    mla::MergeTwoParams p;
+    p.prefix_out = prefix_out;
+    p.prefix_lse = prefix_lse;
+    p.suffix_out = suffix_out;
+    p.suffix_lse = suffix_lse;
+    p.out = out;
+    p.lse = lse;
+    p.rows = rows;
+    p.head_dim = head_dim;
+    p.in_f32 = in_dtype == MLA_F32;
+    p.out_f32 = out_dtype == MLA_F32;
+    if (mla::launch_merge_two(p, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }
 

@@ -942,8 +942,42 @@ void decode_bf16_kernel(DecodeParams p) {
                         (f32x4){ot[dq][4 * q4], ot[dq][4 * q4 + 1], ot[dq][4 * q4 + 2], ot[dq][4 * q4 + 3]} * inv;
         }
     };
+    if (w.nsplit > 1 || !p.out_bf16) {
+        // fp32 rows leave through the idle ring: per half (64 rows) every wave
+        // writes its dims of the rows (scaled by 1 / l) into rows of 2064
+        // bytes, then the workgroup stores whole contiguous row pieces
+        constexpr int kStRow = 4 * kV + 16;
+        float* gbase = w.nsplit > 1 ? p.ws_o + (size_t)blockIdx.x * kMTile * kV
+                                    : (float*)p.out + ((size_t)b * p.rows + (size_t)w.mt * kMTile) * kV;
+        for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) store_tile(o[t], w.mt * kMTile + 32 * t + lr, abuf[t * 64]);
+            for (int tt = 0; tt < 2; ++tt) {
+                const int t = 2 * hf + tt;
+                const float lt = abuf[t * 64];
+                const float inv = lt > 0.f ? 1.f / lt : 0.f;
+                lds_u8* srow = ring + (32 * tt + lr) * kStRow + 4 * dim0;
+#pragma unroll
+                for (int dq = 0; dq < 4; ++dq)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        *(__attribute__((address_space(3))) f32x4*)(srow + 4 * (32 * dq + 8 * q4)) =
+                            (f32x4){o[t][dq][4 * q4], o[t][dq][4 * q4 + 1], o[t][dq][4 * q4 + 2], o[t][dq][4 * q4 + 3]} * inv;
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int k = 0; k < 32; ++k) {
+                const int i = k * 256 + (int)threadIdx.x;
+                const int rl = i >> 7, c = i & 127;
+                if (w.mt * kMTile + 64 * hf + rl < p.rows)
+                    *(f32x4*)(gbase + (size_t)(64 * hf + rl) * kV + 4 * c) =
+                        *(const __attribute__((address_space(3))) f32x4*)(ring + rl * kStRow + 16 * c);
+            }
+            __syncthreads();
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) store_tile(o[t], w.mt * kMTile + 32 * t + lr, abuf[t * 64]);
+    }
     if (row_ok && G == 0) {
         const float lse = l_own > 0.f ? (m + __log2f(l_own)) * kLn2 : -INFINITY;
         if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;

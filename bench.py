@@ -384,6 +384,79 @@ def bench_gather(args) -> int:
     return 0
 
 
+def bench_merge_up_project(args) -> int:
+    """mla_merge_up_project on one DCP rank's shape: 4 shard partials of 32
+    tokens x 512 heads (fp32 [4][16384][512] + LSEs) merged and mapped through
+    W_UV (v_head_dim 128, bf16 out), against mla_merge_states followed by
+    mla_up_project on the same inputs.  Prints ONE JSON line."""
+    import torch
+    import mla_latent_decode_absorbed_amd as mla
+    import workloads
+
+    dev = torch.device("cuda:0")
+    n, R, H, Vd = 4, 32, 512, 128
+    g = torch.Generator(device=dev).manual_seed(args.seed or 3)
+    outs = torch.randn((n, R, H, 512), generator=g, device=dev)
+    lses = torch.randn((n, R, H), generator=g, device=dev)
+    w = workloads.make_up_project_inputs(1, H, Vd, seed=args.seed or 3, device=dev).w_uv
+    ws = [w] + [w.clone() for _ in range(4)]                   # 5 x 67 MB of weights rotated
+    out = torch.empty((R, H, Vd), dtype=torch.bfloat16, device=dev)
+    merged = torch.empty((R * H, 512), dtype=torch.float32, device=dev)
+    mlse = torch.empty(R * H, dtype=torch.float32, device=dev)
+    alg = n * R * H * (512 * 4 + 4) + H * Vd * 512 * 2 + R * H * Vd * 2
+    mla.merge_up_project(outs, lses, n, w, out)                 # checked once through the binding
+    desc = mla.UpProjectDesc(R, H, Vd, mla.F32, mla.BF16)
+    stream = torch.cuda.current_stream().cuda_stream
+    fused_args = [(outs.data_ptr(), lses.data_ptr(), n, ctypes.byref(desc), x.data_ptr(), out.data_ptr(), None,
+                   stream) for x in ws]
+
+    def fused(i):
+        if mla.lib.mla_merge_up_project(*fused_args[i % len(ws)]) != mla.OK:
+            raise RuntimeError("mla_merge_up_project failed")
+
+    def unfused(i):
+        mla.merge_states(outs.view(n, R * H, 512), lses.view(n, R * H), n, R * H, merged, mlse)
+        mla.up_project(merged.view(R, H, 512), ws[i % len(ws)], out)
+
+    ms, kern_ms, n_warm = _time_launches(fused, args)
+    ms_u, kern_u, _ = _time_launches(unfused, args)
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    res = {
+        "metric": "MLA DCP merge + W_UV up-projection GB/s (fraction of MI355X HBM roofline)",
+        "value": round(alg / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) fp32 partials and LSEs, N(0,1/512) W_UV, bf16)",
+        "config": {"workload": f"one DCP rank's merge: {n} shard partials of {R} tokens x {H} heads, "
+                               f"v_head_dim {Vd}, bf16 out", "partials": n, "rows": R, "heads": H,
+                   "v_head_dim": Vd, "weight_copies_rotated": len(ws)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel_ms": round(kern_ms, 5),
+                     "algorithmic_bytes_per_launch": alg},
+        "unfused": {"what": "mla_merge_states then mla_up_project (the merged latent through HBM)",
+                    "ms_events": round(kern_u, 5), "ms_per_step": round(ms_u, 5)},
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        from oracle import bf16_bits_to_f64, merge_ref, up_project_ref
+        o64 = outs.double().cpu().numpy().reshape(n, R * H, 512)
+        l64 = lses.double().cpu().numpy().reshape(n, R * H)
+        w64 = bf16_bits_to_f64(w.view(torch.int16).cpu().numpy())
+        done, spent = 0, 0.0
+        while done < R and spent < 20.0:
+            t = time.perf_counter()
+            om, _ = merge_ref(o64[:, done * H:(done + 1) * H], l64[:, done * H:(done + 1) * H])
+            up_project_ref(om.reshape(1, H, 512), w64)
+            spent += time.perf_counter() - t
+            done += 1
+        per_row = H * (n * (512 * 4 + 4) + Vd * 2)
+        res["cpu_baseline"] = {"value": round((H * Vd * 512 * 2 * done / R + per_row * done) / spent / 1e9, 4),
+                               "unit": "GB/s", "cores": int(os.cpu_count() or 1), "kind": "oracle",
+                               "sample": f"{done} of {R} tokens (all heads), {spent:.2f} s of fp64 numpy"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -396,10 +469,11 @@ def main(argv=None) -> int:
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--op", default="decode", choices=["decode", "qprep", "upproj", "gather"],
+    ap.add_argument("--op", default="decode", choices=["decode", "qprep", "upproj", "gather", "mergeup"],
                     help="decode (default): mla_decode_partial; qprep: mla_query_prep on the "
                          "workload's query rows and heads; upproj: mla_up_project of its latent output; "
-                         "gather: mla_gather_cache of each request's first 2048 cache tokens")
+                         "gather: mla_gather_cache of each request's first 2048 cache tokens; "
+                         "mergeup: mla_merge_up_project of 4 DCP shard partials (one DCP rank's shape)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -413,6 +487,8 @@ def main(argv=None) -> int:
         return bench_up_project(args)
     if args.op == "gather":
         return bench_gather(args)
+    if args.op == "mergeup":
+        return bench_merge_up_project(args)
 
     import torch
     import mla_latent_decode_absorbed_amd as mla

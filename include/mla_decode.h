@@ -213,6 +213,22 @@ typedef struct mla_up_project_desc {
 int mla_up_project(const mla_up_project_desc* desc, const void* o_lat, const void* w_uv,
                    void* out, void* stream);
 
+/* mla_merge_states fused in front of mla_up_project: the latent input of row
+ * (r, h) is the LSE merge of n fp32 partials (DCP shard results; page 4, "DCP
+ * 在 Prefill 与 Decode 中的不同角色": per-rank partials merged with LSE
+ * weights), and is mapped through W_UV without going through memory:
+ *     o_lat = sum_i exp(lse_i - lse) * outs_i,  lse = ln sum_i exp(lse_i),
+ *     out[r][h][v] = sum_l W_UV[h][v][l] * o_lat[l]
+ *   outs   device float [n][R * H][512], 16-byte aligned (rows ordered (r, h))
+ *   lses   device float [n][R * H]; -inf marks an empty partial (never read)
+ *   desc   as for mla_up_project, with in_dtype = MLA_F32
+ *   out    device [R][H][Vd] of desc->out_dtype, 16-byte aligned
+ *   lse    device float [R * H] receives the merged LSE, or NULL
+ * n in 1 .. 16.  A row whose partials are all empty gets out = 0, lse = -inf. */
+int mla_merge_up_project(const float* outs, const float* lses, int32_t n,
+                         const mla_up_project_desc* desc, const void* w_uv, void* out, float* lse,
+                         void* stream);
+
 /* Gather the latent cache rows of each request's context chunk into one
  * contiguous bf16 buffer, dequantising an e4m3 cache (page 4, "与非 DCP 的流程对比":
  * each prefill chunk's context is taken out of the paged cache by

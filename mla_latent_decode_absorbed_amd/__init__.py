@@ -11,6 +11,7 @@ and the current stream.  The entry points mirror include/mla_decode.h:
     merge_states(outs, lses, n, rows, out, lse, out_dtype=F32, stream=None)
     query_prep(q_nope, q_pe, w_uk, q_out, q_scale=None, stream=None)
     up_project(o_lat, w_uv, out, stream=None)
+    merge_up_project(outs, lses, n, w_uv, out, lse=None, stream=None)
     gather_cache(kv_cache, block_table, seq_starts, cu_lens, total_rows, out, kv_scale=None, stream=None)
     merge_two_states(prefix_out, prefix_lse, suffix_out, suffix_lse, out, lse=None, stream=None)
 
@@ -47,6 +48,7 @@ EXPORTS = (
     "mla_merge_states",
     "mla_query_prep",
     "mla_up_project",
+    "mla_merge_up_project",
     "mla_gather_cache",
     "mla_merge_two_states",
     "mla_status_string",
@@ -119,6 +121,8 @@ def _load():
     lib.mla_query_prep.restype = ctypes.c_int
     lib.mla_up_project.argtypes = [ctypes.POINTER(UpProjectDesc), vp, vp, vp, vp]
     lib.mla_up_project.restype = ctypes.c_int
+    lib.mla_merge_up_project.argtypes = [vp, vp, i32, ctypes.POINTER(UpProjectDesc), vp, vp, vp, vp]
+    lib.mla_merge_up_project.restype = ctypes.c_int
     lib.mla_gather_cache.argtypes = [vp, i32, vp, vp, i32, i32, i32, vp, vp, ctypes.c_int64, vp, vp]
     lib.mla_gather_cache.restype = ctypes.c_int
     lib.mla_merge_two_states.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -284,6 +288,29 @@ def up_project(o_lat, w_uv, out, stream=None) -> None:
     st = lib.mla_up_project(ctypes.byref(desc), _ptr(o_lat), _ptr(w_uv), _ptr(out), _stream(stream))
     if st != OK:
         raise MlaError(st, "mla_up_project")
+
+
+def merge_up_project(outs, lses, n: int, w_uv, out, lse=None, stream=None) -> None:
+    """Enqueue mla_merge_up_project: n fp32 partials outs [n][R][H][512] with
+    lses [n][R][H] -> out [R][H][Vd] (fp32 or bf16 by element size) through
+    W_UV [H][Vd][512], and optionally the merged lse [R][H]."""
+    if outs.dim() != 4 or outs.shape[0] != n or outs.shape[-1] != LATENT_DIM:
+        raise ValueError(f"outs must be [n][R][H][512], got {tuple(outs.shape)}")
+    _, R, H, _ = outs.shape
+    Vd = w_uv.shape[1]
+    if tuple(w_uv.shape) != (H, Vd, LATENT_DIM):
+        raise ValueError(f"w_uv {tuple(w_uv.shape)} does not match {H} heads")
+    _need("outs", outs, n * R * H * LATENT_DIM * 4, 4)
+    _need("lses", lses, n * R * H * 4, 4)
+    _need("w_uv", w_uv, H * Vd * LATENT_DIM * 2, 2)
+    _need("out", out, R * H * Vd * out.element_size())
+    if lse is not None:
+        _need("lse", lse, R * H * 4, 4)
+    desc = UpProjectDesc(int(R), int(H), int(Vd), F32, F32 if out.element_size() == 4 else BF16)
+    st = lib.mla_merge_up_project(_ptr(outs), _ptr(lses), int(n), ctypes.byref(desc), _ptr(w_uv), _ptr(out),
+                                  _ptr(lse), _stream(stream))
+    if st != OK:
+        raise MlaError(st, "mla_merge_up_project")
 
 
 def gather_cache(kv_cache, block_table, seq_starts, cu_lens, total_rows: int, out, kv_scale=None,

@@ -243,6 +243,8 @@ int mla_up_project(const mla_up_project_desc* d, const void* o_lat, const void* 
     if (!aligned(o_lat, 16) || !aligned(w_uv, 16) || !aligned(out, 16)) return MLA_ERR_INVALID_ARG;
     mla::UpProjParams p;
     p.o_lat = o_lat;
+    p.lses = nullptr;
+    p.lse_out = nullptr;
     p.w_uv = w_uv;
     p.out = out;
     p.rows = d->rows;
@@ -250,6 +252,35 @@ int mla_up_project(const mla_up_project_desc* d, const void* o_lat, const void* 
     p.vdim = d->v_head_dim;
     p.in_f32 = d->in_dtype == MLA_F32;
     p.out_f32 = d->out_dtype == MLA_F32;
+    p.n_merge = 0;
+    if (mla::launch_up_project(p, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+int mla_merge_up_project(const float* outs, const float* lses, int32_t n, const mla_up_project_desc* d,
+                         const void* w_uv, void* out, float* lse, void* stream) {
+    if (!d) return MLA_ERR_INVALID_ARG;
+    if (n < 1 || n > mla::kMaxMergeUp) return MLA_ERR_INVALID_ARG;
+    if (d->rows < 0 || d->num_heads < 1 || d->in_dtype != MLA_F32) return MLA_ERR_INVALID_ARG;
+    if (d->out_dtype != MLA_F32 && d->out_dtype != MLA_BF16) return MLA_ERR_INVALID_ARG;
+    if (d->v_head_dim < 32 || d->v_head_dim > 512 || d->v_head_dim % 32 != 0) return MLA_ERR_UNSUPPORTED;
+    if (d->num_heads > (1 << 16) || (int64_t)d->rows * d->num_heads > (int64_t)1 << 26) return MLA_ERR_UNSUPPORTED;
+    if (d->rows == 0) return MLA_OK;
+    if (!outs || !lses || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+    if (!aligned(outs, 16) || !aligned(w_uv, 16) || !aligned(out, 16) || !aligned(lses, 4) || (lse && !aligned(lse, 4)))
+        return MLA_ERR_INVALID_ARG;
+    mla::UpProjParams p;
+    p.o_lat = outs;
+    p.lses = lses;
+    p.lse_out = lse;
+    p.w_uv = w_uv;
+    p.out = out;
+    p.rows = d->rows;
+    p.heads = d->num_heads;
+    p.vdim = d->v_head_dim;
+    p.in_f32 = 1;
+    p.out_f32 = d->out_dtype == MLA_F32;
+    p.n_merge = n;
     if (mla::launch_up_project(p, (hipStream_t)stream) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }

@@ -14,6 +14,7 @@
 #include "mla_upproj.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace mla {
@@ -40,8 +41,14 @@ constexpr int kPad = 2 * kKc + 16;   // LDS row stride of a bf16 K-chunk row (27
 // on consecutive 16 bytes, in rows padded by 16 bytes (16 consecutive rows
 // start on distinct bank groups).  Workgroups that share a weight block (same h, vc; other
 // row tiles) run on one XCD, so the block comes from that XCD's L2.
-template <bool IN_F32>
+// MODE 0: bf16 latent input; 1: fp32 latent input; 2: the latent input is the
+// LSE merge of n_merge fp32 partials (mla_merge_states fused in front: each
+// row's weights exp(lse_i - max) / sum come first, then every K chunk of the
+// row tile is the weighted sum of the partials' chunks, so the merged latent
+// never goes through HBM).
+template <int MODE>
 __global__ __launch_bounds__(256) void up_project_kernel(UpProjParams p) {
+    constexpr bool IN_F32 = MODE != 0;
     __shared__ __attribute__((aligned(16))) uint8_t w_lds[kVc * kPad];
     __shared__ __attribute__((aligned(16))) uint8_t hi_lds[32 * kPad];
     __shared__ __attribute__((aligned(16))) uint8_t lo_lds[IN_F32 ? 32 * kPad : 16];
@@ -62,6 +69,32 @@ __global__ __launch_bounds__(256) void up_project_kernel(UpProjParams p) {
     const bool wave_on = 32 * wave < vrows;
     const size_t H = (size_t)p.heads;
 
+    // merge weights of the tile's rows (MODE 2): row li's weight of partial i
+    // at mw[li][i]; a row whose partials are all empty gets weights 0 (out 0,
+    // LSE -inf)
+    __shared__ float mw[MODE == 2 ? 32 : 1][MODE == 2 ? kMaxMergeUp : 1];
+    const size_t rows_all = (size_t)p.rows * H;
+    if (MODE == 2) {
+        if (tid < 32) {
+            const int m = min(m0 + tid, p.rows - 1);
+            const size_t row = (size_t)m * H + h;
+            float mx = -INFINITY;
+            for (int i = 0; i < p.n_merge; ++i) mx = fmaxf(mx, p.lses[i * rows_all + row]);
+            float sum = 0.f;
+            for (int i = 0; i < p.n_merge; ++i) {
+                const float li = p.lses[i * rows_all + row];
+                const float wgt = (mx == -INFINITY || li == -INFINITY) ? 0.f : expf(li - mx);
+                mw[tid][i] = wgt;
+                sum += wgt;
+            }
+            const float inv = sum > 0.f ? 1.f / sum : 0.f;
+            for (int i = 0; i < p.n_merge; ++i) mw[tid][i] *= inv;
+            if (p.lse_out && vc == 0 && m0 + tid < p.rows)
+                p.lse_out[row] = mx == -INFINITY ? -INFINITY : mx + logf(sum);
+        }
+        __syncthreads();
+    }
+
     // K chunk kc: weight piece i = tid + 256 j is (v row i / 16, 16 B piece
     // i % 16); row-tile piece i is fp32 (row i / 32, 4 floats i % 32) or bf16
     // (row i / 16, 8 values i % 16).  Each chunk's loads live in registers only
@@ -81,13 +114,50 @@ __global__ __launch_bounds__(256) void up_project_kernel(UpProjParams p) {
             const int r = min(i >> 4, vrows - 1), pc = i & 15;
             wv[j] = *((const uint4*)((const __bf16*)p.w_uv + ((size_t)h * p.vdim + kVc * vc + r) * kLat + kKc * kc) + pc);
         }
+        if (MODE != 2) {
 #pragma unroll
-        for (int j = 0; j < kOLoads; ++j) {
-            const int i = tid + 256 * j;
-            const int r = IN_F32 ? i >> 5 : i >> 4, pc = IN_F32 ? i & 31 : i & 15;
-            const int mr = min(m0 + r, p.rows - 1);
-            const uint8_t* row = (const uint8_t*)p.o_lat + ((size_t)mr * H + h) * kLat * kEl;
-            ov[j] = *((const uint4*)(row + kKc * kc * kEl) + pc);
+            for (int j = 0; j < kOLoads; ++j) {
+                const int i = tid + 256 * j;
+                const int r = IN_F32 ? i >> 5 : i >> 4, pc = IN_F32 ? i & 31 : i & 15;
+                const int mr = min(m0 + r, p.rows - 1);
+                const uint8_t* row = (const uint8_t*)p.o_lat + ((size_t)mr * H + h) * kLat * kEl;
+                ov[j] = *((const uint4*)(row + kKc * kc * kEl) + pc);
+            }
+        } else {
+            // weighted sum of the partials' pieces, four partials' loads in
+            // flight at a time; a zero weight (an empty partial) is never read
+            float4 acc4[kOLoads];
+#pragma unroll
+            for (int j = 0; j < kOLoads; ++j) acc4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int i0 = 0; i0 < p.n_merge; i0 += 4) {
+                uint4 pv[4][kOLoads];
+                float wv[4][kOLoads];
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int j = 0; j < kOLoads; ++j) {
+                        const int i = tid + 256 * j;
+                        const int r = i >> 5, pc = i & 31;
+                        const int mr = min(m0 + r, p.rows - 1);
+                        wv[k][j] = i0 + k < p.n_merge ? mw[r][i0 + k] : 0.f;
+                        const float* row = (const float*)p.o_lat + ((size_t)(i0 + k) * rows_all + (size_t)mr * H + h) * kLat;
+                        pv[k][j] = wv[k][j] != 0.f ? *((const uint4*)(row + kKc * kc) + pc) : make_uint4(0, 0, 0, 0);
+                    }
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+#pragma unroll
+                    for (int j = 0; j < kOLoads; ++j) {
+                        const float wgt = wv[k][j];
+                        acc4[j].x += wgt * __uint_as_float(pv[k][j].x);
+                        acc4[j].y += wgt * __uint_as_float(pv[k][j].y);
+                        acc4[j].z += wgt * __uint_as_float(pv[k][j].z);
+                        acc4[j].w += wgt * __uint_as_float(pv[k][j].w);
+                    }
+            }
+#pragma unroll
+            for (int j = 0; j < kOLoads; ++j)
+                ov[j] = make_uint4(__float_as_uint(acc4[j].x), __float_as_uint(acc4[j].y),
+                                   __float_as_uint(acc4[j].z), __float_as_uint(acc4[j].w));
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -160,8 +230,9 @@ hipError_t launch_up_project(const UpProjParams& p, hipStream_t stream) {
     const int mtiles = (p.rows + 31) / 32;
     const int groups = (p.heads * vchunks + 7) / 8;
     const dim3 grid((unsigned)(groups * 8 * mtiles));
-    if (p.in_f32) hipLaunchKernelGGL(up_project_kernel<true>, grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(up_project_kernel<false>, grid, dim3(256), 0, stream, p);
+    if (p.n_merge > 0) hipLaunchKernelGGL(up_project_kernel<2>, grid, dim3(256), 0, stream, p);
+    else if (p.in_f32) hipLaunchKernelGGL(up_project_kernel<1>, grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(up_project_kernel<0>, grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

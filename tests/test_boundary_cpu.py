@@ -267,3 +267,15 @@ def test_up_project_pointer_rules():
     assert mla.lib.mla_up_project(ctypes.byref(d), None, 16, 16, None) == mla.ERR_INVALID_ARG
     assert mla.lib.mla_up_project(ctypes.byref(d), 16, 16, 8, None) == mla.ERR_INVALID_ARG
     assert mla.lib.mla_up_project(ctypes.byref(_udesc(rows=0)), None, None, None, None) == mla.OK
+
+
+def test_merge_up_project_argument_rules():
+    d = _udesc(in_dtype=mla.F32)
+    assert mla.lib.mla_merge_up_project(16, 16, 0, ctypes.byref(d), 16, 16, None, None) == mla.ERR_INVALID_ARG
+    assert mla.lib.mla_merge_up_project(16, 16, 17, ctypes.byref(d), 16, 16, None, None) == mla.ERR_INVALID_ARG
+    assert mla.lib.mla_merge_up_project(16, 16, 4, ctypes.byref(_udesc(in_dtype=mla.BF16)), 16, 16, None,
+                                        None) == mla.ERR_INVALID_ARG
+    assert mla.lib.mla_merge_up_project(16, 16, 4, ctypes.byref(_udesc(v_head_dim=48)), 16, 16, None,
+                                        None) == mla.ERR_UNSUPPORTED
+    assert mla.lib.mla_merge_up_project(None, 16, 4, ctypes.byref(d), 16, 16, None, None) == mla.ERR_INVALID_ARG
+    assert mla.lib.mla_merge_up_project(None, None, 4, ctypes.byref(_udesc(rows=0)), None, None, None, None) == mla.OK

@@ -99,3 +99,74 @@ def test_decode_then_up_project():
     ref = up_project_ref(o_ref.reshape(R, g.heads, 512), w64)
     bar = 1e-2 * np.abs(w64).sum(axis=-1).max()
     assert np.abs(out.double().cpu().numpy() - ref).max() <= bar
+
+
+def _merge_inputs(n, R, H, seed):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    outs = torch.randn((n, R, H, 512), generator=g)
+    lses = torch.randn((n, R, H), generator=g) * 2
+    if n > 1:
+        lses[0, ::3] = -float("inf")                  # empty partials ...
+        outs[0, ::3] = float("nan")                   # ... whose data must never be read
+    lses[:, 1, 0] = -float("inf")                     # one row with every partial empty
+    return outs, lses
+
+
+@pytest.mark.parametrize("n,R,H,vdim", [(1, 5, 3, 128), (2, 37, 2, 128), (4, 33, 4, 96), (7, 3, 2, 160),
+                                        (16, 2, 2, 64)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_merge_up_project_matches_oracle(n, R, H, vdim, out_dtype):
+    """mla_merge_up_project = the oracle's LSE merge followed by its up-projection."""
+    import mla_latent_decode_absorbed_amd as mla
+    from oracle import merge_ref
+    say(f"merge_up_project n={n} R={R} H={H} vdim={vdim} {out_dtype}")
+    outs, lses = _merge_inputs(n, R, H, seed=n * 100 + R)
+    w = workloads.make_up_project_inputs(1, H, vdim, seed=n, device=DEV).w_uv
+    out = torch.empty((R, H, vdim), dtype=out_dtype, device=DEV)
+    lse = torch.empty((R, H), dtype=torch.float32, device=DEV)
+    mla.merge_up_project(outs.to(DEV), lses.to(DEV), n, w, out, lse)
+    torch.cuda.synchronize()
+    o_m, l_m = merge_ref(np.nan_to_num(outs.double().numpy().reshape(n, R * H, 512), nan=0.0),
+                         lses.double().numpy().reshape(n, R * H))
+    w64 = _f64(w)
+    exact = up_project_ref(o_m.reshape(R, H, 512), w64)
+    absdot = up_project_ref(np.abs(o_m).reshape(R, H, 512), np.abs(w64))
+    spread = up_project_ref(np.nan_to_num(np.abs(outs.double().numpy())).sum(axis=0), np.abs(w64))
+    delta = (2.0 ** -16 + 2.0 ** -13) * absdot + 2.0 ** -20 * spread
+    got = out.double().cpu().numpy()
+    assert np.isfinite(got).all()
+    if out_dtype == torch.float32:
+        assert (np.abs(got - exact) <= delta + 1e-30).all()
+    else:
+        codes = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        lo = bf16_bits_to_f64(bf16_encode(exact - delta))
+        hi = bf16_bits_to_f64(bf16_encode(exact + delta))
+        assert ((got >= lo) & (got <= hi)).all()
+    gl, rl = lse.double().cpu().numpy().reshape(-1), l_m
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+    fin = np.isfinite(rl)
+    assert (np.abs(gl[fin] - rl[fin]) <= 1e-5).all()
+    assert (got[1, 0] == 0).all()                      # all partials empty -> 0
+
+
+def test_merge_up_project_matches_unfused_full_size():
+    """The one-DCP-rank shape: 4 shard partials of 32 tokens x 512 heads, fused
+    against mla_merge_states followed by mla_up_project."""
+    import mla_latent_decode_absorbed_amd as mla
+    say("merge_up_project full size, 4 x (32 x 512)")
+    n, R, H = 4, 32, 512
+    outs, lses = _merge_inputs(n, R, H, seed=5)
+    outs, lses = outs.to(DEV), lses.to(DEV)
+    w = workloads.make_up_project_inputs(1, H, 128, seed=6, device=DEV).w_uv
+    fused = torch.empty((R, H, 128), dtype=torch.float32, device=DEV)
+    mla.merge_up_project(outs, lses, n, w, fused)
+    merged = torch.empty((R * H, 512), dtype=torch.float32, device=DEV)
+    ml = torch.empty(R * H, dtype=torch.float32, device=DEV)
+    mla.merge_states(outs.reshape(n, R * H, 512).contiguous(), lses.reshape(n, R * H).contiguous(), n, R * H,
+                     merged, ml)
+    unfused = torch.empty((R, H, 128), dtype=torch.float32, device=DEV)
+    mla.up_project(merged.view(R, H, 512), w, unfused)
+    torch.cuda.synchronize()
+    ref = unfused.double().cpu().numpy()
+    scale = np.abs(ref).max()
+    assert np.abs(fused.double().cpu().numpy() - ref).max() <= 1e-4 * scale

@@ -543,6 +543,7 @@ def main(argv=None) -> int:
 
     ms_per_step = wall * 1e3 / args.steps
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
+
     kv_gbs = acc["kv_bytes"] / (ms_per_step * 1e-3) / 1e9
     tflops = acc["flops"] / (ms_per_step * 1e-3) / 1e12
     total_gbs = (acc["kv_bytes"] + acc["q_bytes"] + acc["bt_bytes"] + acc["out_bytes"]) / (ms_per_step * 1e-3) / 1e9

@@ -384,6 +384,53 @@ def bench_gather(args) -> int:
     return 0
 
 
+def probe_peaks() -> int:
+    """Achievable figures of this GPU next to the published peaks the rooflines
+    use: a 4 GiB device-to-device copy (HBM read + write), a 4 GiB reduction
+    (HBM read), and 8192^3 dense GEMMs in bf16 and (when torch offers it) fp8
+    through hipBLASLt."""
+    import torch
+
+    dev = torch.device("cuda:0")
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    res = {"probe": "achievable peaks", "published": {"hbm_gbs": HBM_PEAK_GBS, "mfma_tflops": MFMA_PEAK_TFLOPS}}
+    src = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t = timed(lambda: dst.copy_(src), 10)
+    res["hbm_copy_gbs"] = round(2 * src.numel() / t / 1e9, 1)        # bytes read + written
+    del dst
+    f = src.view(torch.float32)
+    t = timed(lambda: f.sum(), 10)
+    res["hbm_read_gbs"] = round(src.numel() / t / 1e9, 1)              # a 4 GiB reduction: reads only
+    del src, f
+    n = 8192
+    a = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), device=dev).to(torch.bfloat16)
+    t = timed(lambda: torch.mm(a, b), 20)
+    res["bf16_gemm_tflops"] = round(2 * n ** 3 / t / 1e12, 1)
+    try:
+        a8, b8 = a.to(torch.float8_e4m3fn), b.t().contiguous().to(torch.float8_e4m3fn).t()
+        one = torch.ones((), device=dev)
+        t = timed(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16), 20)
+        res["fp8_gemm_tflops"] = round(2 * n ** 3 / t / 1e12, 1)
+    except Exception as exc:                                              # not offered by this torch build
+        res["fp8_gemm_tflops"] = None
+        res["fp8_note"] = f"torch._scaled_mm unavailable: {type(exc).__name__}"
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_merge_up_project(args) -> int:
     """mla_merge_up_project on one DCP rank's shape: 4 shard partials of 32
     tokens x 512 heads (fp32 [4][16384][512] + LSEs) merged and mapped through
@@ -469,6 +516,9 @@ def main(argv=None) -> int:
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--probe-peaks", action="store_true",
+                    help="print achievable HBM copy bandwidth and dense bf16/fp8 GEMM rates of this "
+                         "GPU (torch's copy kernel and hipBLASLt) as one JSON line, and exit")
     ap.add_argument("--op", default="decode", choices=["decode", "qprep", "upproj", "gather", "mergeup"],
                     help="decode (default): mla_decode_partial; qprep: mla_query_prep on the "
                          "workload's query rows and heads; upproj: mla_up_project of its latent output; "
@@ -481,6 +531,8 @@ def main(argv=None) -> int:
               "DCP shards are materialised on one device, so run with --gpus 1.", file=sys.stderr)
         return 2
 
+    if args.probe_peaks:
+        return probe_peaks()
     if args.op == "qprep":
         return bench_query_prep(args)
     if args.op == "upproj":

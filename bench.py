@@ -651,10 +651,58 @@ def main(argv=None) -> int:
         "roofline": roof,
         "setup_s": round(setup_s, 2),
     }
+    if args.config == "c3" and args.num_splits == 0:
+        res["dcp_rank_merge"] = dcp_merge_timings(args, inp, dec, out, lse, stream)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def dcp_merge_timings(args, inp0, dec, out0, lse0, stream) -> dict:
+    """One DCP rank's share, 4 shards: the LSE merge of the 4 shard partials
+    (mla_merge_states, n = 4, 16,384 rows) alone, and all 4 shard decodes plus
+    that merge, for information.  The other 3 shards are built like shard 0."""
+    import torch
+    import mla_latent_decode_absorbed_amd as mla
+    import workloads
+
+    dev = inp0.q.device
+    shards = [inp0] + [workloads.make_config("c3", seed=args.seed, device=dev, poison=False, extra_pages=0,
+                                             shard_only=r) for r in (1, 2, 3)]
+    rows = inp0.batch * inp0.q_len * inp0.heads
+    outs = torch.empty((4, rows, 512), dtype=torch.float32, device=dev)
+    lses = torch.empty((4, rows), dtype=torch.float32, device=dev)
+    mo = torch.empty((rows, 512), dtype=torch.float32, device=dev)
+    ml = torch.empty(rows, dtype=torch.float32, device=dev)
+
+    def all_shards():
+        for r, sh in enumerate(shards):
+            dec(sh.q, sh.kv_cache, sh.block_table, sh.seq_lens, sh.scale, out=outs[r].view_as(out0),
+                lse=lses[r].view_as(lse0), stream=stream)
+        mla.merge_states(outs, lses, 4, rows, mo, ml, stream=stream)
+
+    def merge_only():
+        mla.merge_states(outs, lses, 4, rows, mo, ml, stream=stream)
+
+    all_shards()
+    torch.cuda.synchronize()
+    res = {}
+    for name, fn, reps in (("merge_ms", merge_only, max(args.steps, 20)), ("four_shards_and_merge_ms", all_shards, 10)):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        res[name] = round(a.elapsed_time(b) / reps, 5)
+    merge_bytes = 4 * rows * 2052 + rows * 2052
+    res["merge_gbs"] = round(merge_bytes / (res["merge_ms"] * 1e-3) / 1e9, 1)
+    res["what"] = ("mla_merge_states of the 4 shard partials (n = 4, 16,384 rows; 4 x 2052 B in and 2052 B "
+                   "out per row), and the 4 shard decodes plus that merge")
+    return res
 
 
 if __name__ == "__main__":

@@ -28,6 +28,11 @@ if ROOT not in sys.path:
 
 METRIC = "MLA decode KV-cache GB/s + TFLOP/s (fraction of MI355X HBM/MFMA roofline)"
 HBM_PEAK_GBS = 8000.0
+# HIP events bracket the measured kernel in every EVENT_EVERY-th timed step:
+# a timing event pair costs ~5.8 us of every step it brackets (DeepSeek-V3
+# shape: 110.7 us per step with events on every step, 104.9 without, 106.6
+# with every fourth), which the wall-clock step time should not carry.
+EVENT_EVERY = 4
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 FLOP_PER_ROW_TOKEN = 2 * (576 + 512)
 KERNEL_SRC = os.path.join(ROOT, "mla_latent_decode_absorbed_amd", "csrc", "mla_kernels.hip")
@@ -177,23 +182,7 @@ def bench_query_prep(args) -> int:
         if call(*args_of[i % n_w]) != mla.OK:
             raise RuntimeError("mla_query_prep failed")
 
-    step(0)
-    torch.cuda.synchronize()
-    n_warm, t_w = 1, time.perf_counter()
-    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
-        step(n_warm)
-        n_warm += 1
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        evs[i][0].record()
-        step(i)
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
-    ms = wall * 1e3 / args.steps
+    ms, kern_ms, n_warm = _time_launches(step, args)
     achieved = alg / (kern_ms * 1e-3) / 1e9
     res = {
         "metric": "MLA query preparation GB/s (fraction of MI355X HBM roofline)",
@@ -240,15 +229,19 @@ def _time_launches(step, args):
         step(n_warm)
         n_warm += 1
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(0, args.steps, EVENT_EVERY)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        evs[i][0].record()
+        timed = i % EVENT_EVERY == 0
+        if timed:
+            evs[i // EVENT_EVERY][0].record()
         step(i)
-        evs[i][1].record()
+        if timed:
+            evs[i // EVENT_EVERY][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall * 1e3 / args.steps, sum(a.elapsed_time(b) for a, b in evs) / args.steps, n_warm
+    return wall * 1e3 / args.steps, sum(a.elapsed_time(b) for a, b in evs) / len(evs), n_warm
 
 
 def bench_up_project(args) -> int:
@@ -565,7 +558,7 @@ def main(argv=None) -> int:
     setup_s = time.perf_counter() - t_setup
 
     hev = HipEvents()
-    evs = [(hev.create(), hev.create()) for _ in range(args.steps)]
+    evs = [(hev.create(), hev.create()) for _ in range(0, args.steps, EVENT_EVERY)]
     stream = torch.cuda.current_stream()
 
     def step(i, events=None):
@@ -585,7 +578,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, events=evs[i])
+        step(i, events=evs[i // EVENT_EVERY] if i % EVENT_EVERY == 0 else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = [hev.elapsed_ms(a, b) for a, b in evs]
@@ -651,12 +644,42 @@ def main(argv=None) -> int:
         "roofline": roof,
         "setup_s": round(setup_s, 2),
     }
+    res["plan_reuse"] = plan_reuse_timings(args, inp, dec, copies, out, lse, stream)
     if args.config == "c3" and args.num_splits == 0:
         res["dcp_rank_merge"] = dcp_merge_timings(args, inp, dec, out, lse, stream)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def plan_reuse_timings(args, inp, dec, copies, out, lse, stream) -> dict:
+    """The same decode with the split plan made once per step and reused by
+    every layer: mla_decode_plan alone, and one layer's decode on the stored
+    plan (mla_decode_partial_planned: decode + combine, no planning), each
+    averaged over back-to-back launches, for information."""
+    import torch
+
+    def plan():
+        dec.plan(inp.seq_lens, stream=stream)
+
+    def layer(i):
+        dec.planned(inp.q, copies[i % len(copies)], inp.block_table, inp.seq_lens, inp.scale,
+                    kv_scale=inp.kv_scale, out=out, lse=lse, stream=stream)
+
+    res = {}
+    for name, fn, reps in (("plan_ms", lambda i: plan(), 50), ("layer_decode_on_stored_plan_ms", layer, args.steps)):
+        for i in range(5):
+            fn(i)
+        plan()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        res[name] = round(a.elapsed_time(b) / reps, 5)
+    return res
 
 
 def dcp_merge_timings(args, inp0, dec, out0, lse0, stream) -> dict:

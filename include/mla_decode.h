@@ -139,6 +139,32 @@ int mla_decode_partial_timed(const mla_decode_desc* desc, const void* q, const v
                              void* workspace, size_t workspace_bytes, void* stream,
                              void* event_before_decode, void* event_after_decode);
 
+/* The split plan of a decode step alone, for reuse by every layer's decode of
+ * that step (page 2, the flashmla.py _build_decode excerpt: the scheduler
+ * metadata comes from seq_lens and q tokens x heads in the backend's per-step
+ * metadata build, apart from the attention calls that consume it).
+ *   desc, seq_lens, workspace: as for mla_decode_partial.
+ * Enqueues one planner kernel on `stream` that writes the per-request split
+ * counts and the work list into the workspace; nothing else of the workspace
+ * is touched.  Returns MLA_OK or a negative mla_status (before any device work
+ * on a bad argument). */
+int mla_decode_plan(const mla_decode_desc* desc, const int32_t* seq_lens, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* mla_decode_partial without the planning step: the split-KV decode and the
+ * combine follow the plan that mla_decode_plan left in `workspace`.  Arguments
+ * and results are those of mla_decode_partial.  The workspace must hold the
+ * plan for the same descriptor and the same seq_lens values, made earlier in
+ * stream order; the plan stays valid across calls (each call only rewrites
+ * the split partials), so the calls of one step on one workspace must not
+ * overlap.  A work item or split count that does not fit the descriptor is
+ * skipped rather than followed (its rows are then not written); a plan for
+ * other seq_lens gives wrong results but no access outside the arguments. */
+int mla_decode_partial_planned(const mla_decode_desc* desc, const void* q, const void* kv_cache,
+                               const float* kv_scale, const int32_t* block_table,
+                               const int32_t* seq_lens, float scale, void* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* LSE merge of n partial results per row (page 4, "Chunked Prefill 与 LSE
  * Merge": merge_attn_states' elementwise LSE rescaling; "DCP 在 Prefill 与
  * Decode 中的不同角色": DCP decode merges per-rank partials with LSE weights).

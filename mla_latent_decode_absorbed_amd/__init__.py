@@ -45,6 +45,8 @@ EXPORTS = (
     "mla_decode_workspace_size",
     "mla_decode_partial",
     "mla_decode_partial_timed",
+    "mla_decode_plan",
+    "mla_decode_partial_planned",
     "mla_merge_states",
     "mla_query_prep",
     "mla_up_project",
@@ -115,6 +117,10 @@ def _load():
     lib.mla_decode_partial.restype = ctypes.c_int
     lib.mla_decode_partial_timed.argtypes = dec_args + [vp, vp]
     lib.mla_decode_partial_timed.restype = ctypes.c_int
+    lib.mla_decode_plan.argtypes = [pdesc, vp, vp, sz, vp]
+    lib.mla_decode_plan.restype = ctypes.c_int
+    lib.mla_decode_partial_planned.argtypes = dec_args
+    lib.mla_decode_partial_planned.restype = ctypes.c_int
     lib.mla_merge_states.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp]
     lib.mla_merge_states.restype = ctypes.c_int
     lib.mla_query_prep.argtypes = [ctypes.POINTER(QueryPrepDesc), vp, vp, vp, vp, vp, vp]
@@ -230,6 +236,34 @@ def decode_partial(desc: DecodeDesc, q, kv_cache, kv_scale, block_table, seq_len
         st = lib.mla_decode_partial_timed(*args, events[0], events[1])
     if st != OK:
         raise MlaError(st, "mla_decode_partial")
+
+
+def decode_plan(desc: DecodeDesc, seq_lens, workspace, workspace_bytes: int | None = None, stream=None) -> None:
+    """Enqueue mla_decode_plan: the split plan of seq_lens into ``workspace``,
+    for the decodes of every layer of one step (decode_partial_planned)."""
+    if seq_lens.numel() != desc.batch or seq_lens.element_size() != 4:
+        raise ValueError(f"seq_lens: expected {desc.batch} int32 values")
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib.mla_decode_plan(ctypes.byref(desc), _ptr(seq_lens), _ptr(workspace), ctypes.c_size_t(workspace_bytes),
+                             _stream(stream))
+    if st != OK:
+        raise MlaError(st, "mla_decode_plan")
+
+
+def decode_partial_planned(desc: DecodeDesc, q, kv_cache, kv_scale, block_table, seq_lens, scale: float,
+                           out, lse, workspace, workspace_bytes: int | None = None, stream=None) -> None:
+    """Enqueue mla_decode_partial_planned: decode_partial following the plan an
+    earlier decode_plan left in ``workspace`` (same descriptor and seq_lens)."""
+    check_decode_buffers(desc, q, kv_cache, kv_scale, block_table, seq_lens, out, lse)
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib.mla_decode_partial_planned(ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(kv_scale),
+                                        _ptr(block_table), _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
+                                        _ptr(lse), _ptr(workspace), ctypes.c_size_t(workspace_bytes),
+                                        _stream(stream))
+    if st != OK:
+        raise MlaError(st, "mla_decode_partial_planned")
 
 
 def merge_states(outs, lses, n: int, rows: int, out, lse, out_dtype: int = F32, stream=None) -> None:
@@ -379,4 +413,23 @@ class Decoder:
         assert out.numel() == d.batch * rows * LATENT_DIM and lse.numel() == d.batch * rows
         decode_partial(d, q, kv_cache, kv_scale, block_table, seq_lens, scale, out, lse,
                        self.workspace, self.ws_bytes, stream=stream, events=events)
+        return out, lse
+
+    def plan(self, seq_lens, stream=None) -> None:
+        """Plan the splits of one step once (mla_decode_plan); then call
+        ``planned`` for each layer's decode with the same seq_lens."""
+        decode_plan(self.desc, seq_lens, self.workspace, self.ws_bytes, stream=stream)
+
+    def planned(self, q, kv_cache, block_table, seq_lens, scale: float, kv_scale=None, out=None, lse=None,
+                stream=None):
+        """One layer's decode on the plan of the last ``plan`` call."""
+        import torch
+        d = self.desc
+        if out is None:
+            dt = torch.float32 if d.out_dtype == F32 else torch.bfloat16
+            out = torch.empty((d.batch, d.q_len, d.num_heads, LATENT_DIM), dtype=dt, device=q.device)
+        if lse is None:
+            lse = torch.empty((d.batch, d.q_len, d.num_heads), dtype=torch.float32, device=q.device)
+        decode_partial_planned(d, q, kv_cache, kv_scale, block_table, seq_lens, scale, out, lse,
+                               self.workspace, self.ws_bytes, stream=stream)
         return out, lse

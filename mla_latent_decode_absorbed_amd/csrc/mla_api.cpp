@@ -75,10 +75,42 @@ WorkspaceLayout layout_for(const mla_decode_desc* d) {
     return L;
 }
 
+// The planner's inputs for one descriptor.
+mla::PlanParams plan_params(const mla_decode_desc* d, const WorkspaceLayout& L) {
+    mla::PlanParams pp;
+    pp.batch = d->batch;
+    pp.rows = d->q_len * d->num_heads;
+    pp.m_tiles = L.m_tiles;
+    pp.max_pages = d->max_pages_per_seq;
+    pp.num_splits = d->num_splits;
+    pp.target_units = target_units_for_current_device();
+    pp.min_chunk = mla::kMinChunkPages;
+    pp.units_max = (int32_t)L.units_max;
+    return pp;
+}
+
+int plan_impl(const mla_decode_desc* d, const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
+              void* stream) {
+    int st = check_desc(d);
+    if (st != MLA_OK) return st;
+    if (!seq_lens || !aligned(seq_lens, 4)) return MLA_ERR_INVALID_ARG;
+    const WorkspaceLayout L = layout_for(d);
+    if (!workspace || !aligned(workspace, kAlign)) return MLA_ERR_WORKSPACE;
+    if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+    if (L.units_max > INT32_MAX / mla::kMTile) return MLA_ERR_UNSUPPORTED;
+    uint8_t* ws = (uint8_t*)workspace;
+    if (mla::launch_plan(plan_params(d, L), seq_lens, (int32_t*)(ws + L.req_info),
+                         (mla::WorkItem*)(ws + L.work), (hipStream_t)stream) != hipSuccess)
+        return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+// planned: the work list and split counts already sit in the workspace (an
+// earlier mla_decode_plan); otherwise this call plans them itself.
 int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const float* kv_scale,
                 const int32_t* block_table, const int32_t* seq_lens, float scale, void* out,
                 float* lse, void* workspace, size_t workspace_bytes, void* stream, void* ev0,
-                void* ev1) {
+                void* ev1, bool planned = false) {
     int st = check_desc(d);
     if (st != MLA_OK) return st;
     if (!q || !kv || !block_table || !seq_lens || !out || !lse) return MLA_ERR_INVALID_ARG;
@@ -99,19 +131,13 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     mla::WorkItem* work = (mla::WorkItem*)(ws + L.work);
     const int rows = d->q_len * d->num_heads;
 
-    mla::PlanParams pp;
-    pp.batch = d->batch;
-    pp.rows = rows;
-    pp.m_tiles = L.m_tiles;
-    pp.max_pages = d->max_pages_per_seq;
-    pp.num_splits = d->num_splits;
-    pp.target_units = target_units_for_current_device();
-    pp.min_chunk = mla::kMinChunkPages;
-    pp.units_max = (int32_t)L.units_max;
+    const mla::PlanParams pp = plan_params(d, L);
     // small batches: every decode workgroup plans the splits itself (one
-    // launch fewer); larger ones: one planner workgroup writes the work list
-    const bool fused_plan = d->batch <= mla::kFusedPlanMax;
-    if (!fused_plan && mla::launch_plan(pp, seq_lens, req_info, work, s) != hipSuccess) return MLA_ERR_HIP;
+    // launch fewer); larger ones: one planner workgroup writes the work list;
+    // planned calls read the list an earlier planner run left
+    const bool fused_plan = !planned && d->batch <= mla::kFusedPlanMax;
+    if (!planned && !fused_plan && mla::launch_plan(pp, seq_lens, req_info, work, s) != hipSuccess)
+        return MLA_ERR_HIP;
 
     mla::DecodeParams dp;
     dp.q = q;
@@ -150,6 +176,7 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     cp.rows = rows;
     cp.m_tiles = L.m_tiles;
     cp.out_bf16 = dp.out_bf16;
+    cp.units_max = (int32_t)L.units_max;
     if (mla::launch_combine(cp, s) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }
@@ -181,6 +208,19 @@ int mla_decode_partial_timed(const mla_decode_desc* desc, const void* q, const v
                              void* event_before_decode, void* event_after_decode) {
     return decode_impl(desc, q, kv_cache, kv_scale, block_table, seq_lens, scale, out, lse,
                        workspace, workspace_bytes, stream, event_before_decode, event_after_decode);
+}
+
+int mla_decode_plan(const mla_decode_desc* desc, const int32_t* seq_lens, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    return plan_impl(desc, seq_lens, workspace, workspace_bytes, stream);
+}
+
+int mla_decode_partial_planned(const mla_decode_desc* desc, const void* q, const void* kv_cache,
+                               const float* kv_scale, const int32_t* block_table, const int32_t* seq_lens,
+                               float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    return decode_impl(desc, q, kv_cache, kv_scale, block_table, seq_lens, scale, out, lse,
+                       workspace, workspace_bytes, stream, nullptr, nullptr, true);
 }
 
 int mla_merge_states(const float* outs, const float* lses, int32_t n, int32_t rows, void* out,

@@ -35,7 +35,8 @@ struct DecodeParams {
     WorkItem* work_out;         // the same list (written when fused_plan == 1, one item per workgroup)
     int32_t* req_info;          // [B][2] (written by workgroup 0 when fused_plan == 1)
     PlanParams plan;            // the planner's inputs (fused_plan == 1)
-    int32_t fused_plan;         // 1: every workgroup plans the splits itself (batch <= kFusedPlanMax)
+    int32_t fused_plan;         // 1: every workgroup plans the splits itself (batch <= kFusedPlanMax);
+                                // 0: work[] comes from the planner kernel, of this call or an earlier one
     void* out;                  // [B][M][512] of out_dtype
     float* lse;                 // [B][M]
     float* ws_o;                // [units_max][kMTile][512]
@@ -56,6 +57,7 @@ struct CombineParams {
     void* out;
     float* lse;
     int32_t batch, rows, m_tiles, out_bf16;
+    int32_t units_max;          // slots in ws_o / ws_lse (a split list that needs more is skipped)
 };
 
 struct MergeParams {

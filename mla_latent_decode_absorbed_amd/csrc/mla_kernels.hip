@@ -327,7 +327,17 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
 // per-request (splits, first kv-unit) the combine reads.  The item is the
 // same value in every lane; readfirstlane makes that visible to the compiler.
 __device__ __forceinline__ WorkItem decode_work_item(const DecodeParams& p, uint8_t* lds) {
-    if (!p.fused_plan) return p.work[blockIdx.x];
+    if (!p.fused_plan) {
+        // A stored work list may come from an earlier planner run: an item
+        // that does not fit this call's descriptor (a list planned for
+        // another one, or never written) is skipped rather than followed.
+        WorkItem w = p.work[blockIdx.x];
+        if (w.b >= p.plan.batch || w.mt < 0 || w.mt >= p.plan.m_tiles || w.page_begin < 0 ||
+            w.page_begin > w.page_end || w.page_end > p.max_pages || w.nsplit < 1 || w.split < 0 ||
+            w.split >= w.nsplit)
+            w.b = -1;
+        return w;
+    }
     lds_u8* l8 = (lds_u8*)lds;
     constexpr int kOff = 8 * kFusedPlanMax;
     const PlanScratch L{(lds_int*)l8, (lds_int*)(l8 + 4 * kFusedPlanMax), (lds_int*)(l8 + kOff),
@@ -1593,9 +1603,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     const int r = (int)(grow - (long long)b * p.rows);
     const int S = p.req_info[2 * b];
     if (S <= 1) return;   // a single split wrote the result directly
+    const int first = p.req_info[2 * b + 1];
     const int k_total = p.req_info[2 * (p.batch - 1)] + p.req_info[2 * (p.batch - 1) + 1];
-    SplitPartials at{p.ws_o, p.ws_lse, p.req_info[2 * b + 1], r / kMTile, p.m_tiles, (k_total + 7) / 8,
-                     r % kMTile};
+    const int per_xcd = (k_total + 7) / 8;
+    // (a split list that does not fit the workspace, e.g. one stored for
+    // another descriptor, is not followed: every slot index stays below units_max)
+    if (first < 0 || first > k_total - S || per_xcd < 1 || (long long)per_xcd * p.m_tiles * 8 > p.units_max) return;
+    SplitPartials at{p.ws_o, p.ws_lse, first, r / kMTile, p.m_tiles, per_xcd, r % kMTile};
     merge_row(S, at, p.out, p.lse, (size_t)grow, p.out_bf16);
 }
 

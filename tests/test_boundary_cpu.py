@@ -109,6 +109,46 @@ def test_workspace_checks():
     assert _call(d, ws_bytes=need - 1) == mla.ERR_WORKSPACE
 
 
+def test_plan_argument_checks():
+    """mla_decode_plan: the descriptor, seq_lens and workspace rules of mla_decode_partial."""
+    d = good_desc()
+    need = mla.workspace_size(d)
+
+    def plan(desc, sl=4096, ws=4096, ws_bytes=1 << 34):
+        return mla.lib.mla_decode_plan(ctypes.byref(desc), sl, ws, ctypes.c_size_t(ws_bytes), None)
+
+    bad = good_desc()
+    bad.batch = 0
+    assert plan(bad) == mla.ERR_INVALID_ARG
+    assert plan(d, sl=None) == mla.ERR_INVALID_ARG
+    assert plan(d, sl=4096 + 2) == mla.ERR_INVALID_ARG
+    assert plan(d, ws=None) == mla.ERR_WORKSPACE
+    assert plan(d, ws=4096 + 128) == mla.ERR_WORKSPACE
+    assert plan(d, ws_bytes=need - 1) == mla.ERR_WORKSPACE
+
+
+def test_planned_decode_argument_checks():
+    """mla_decode_partial_planned validates exactly like mla_decode_partial."""
+    d = good_desc()
+    need = mla.workspace_size(d)
+
+    def call(**kw):
+        a = dict(q=4096, kv=4096, kv_scale=None, bt=4096, sl=4096, scale=0.1, out=4096, lse=4096, ws=4096,
+                 ws_bytes=1 << 34)
+        a.update(kw)
+        return mla.lib.mla_decode_partial_planned(ctypes.byref(d), a["q"], a["kv"], a["kv_scale"], a["bt"],
+                                                  a["sl"], ctypes.c_float(a["scale"]), a["out"], a["lse"],
+                                                  a["ws"], ctypes.c_size_t(a["ws_bytes"]), None)
+
+    assert call(q=None) == mla.ERR_INVALID_ARG
+    assert call(sl=None) == mla.ERR_INVALID_ARG
+    assert call(out=4096 + 4) == mla.ERR_INVALID_ARG
+    assert call(scale=0.0) == mla.ERR_INVALID_ARG
+    assert call(kv_scale=4096) == mla.ERR_INVALID_ARG
+    assert call(ws=None) == mla.ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == mla.ERR_WORKSPACE
+
+
 def test_fp8_requires_kv_scale():
     d = good_desc(kv_dtype=mla.FP8_E4M3)
     n = ctypes.c_size_t(0)

@@ -57,3 +57,46 @@ def test_decode_and_merge_graph_replays_match_eager(cfg):
         torch.cuda.synchronize()
         for got, want in zip((out, lse, mo, ml), ref):
             assert torch.equal(got, want), f"replay {rep} differs"
+
+
+def test_plan_once_three_layers_graph_replays_match_eager():
+    """One decode step as a serving loop would capture it: mla_decode_plan once,
+    then three layers' mla_decode_partial_planned on that plan (each layer its
+    own query and cache); every replay reproduces the eager outputs bit for bit."""
+    import mla_latent_decode_absorbed_amd as mla
+    say("graph capture: plan once, three planned layers")
+    base = workloads.make_decode_inputs(5, 1, 128, [700, 2100, 64, 1, 1300], "bf16", seed=71, device=DEV)
+    gen = torch.Generator(device="cpu").manual_seed(72)
+    layers = [(torch.randn(base.q.shape, generator=gen).to(torch.bfloat16).to(DEV),
+               torch.randn(base.kv_cache.shape, generator=gen).to(torch.bfloat16).to(DEV)) for _ in range(3)]
+    desc = mla.make_desc(base.batch, base.q_len, base.heads, base.kv_cache.shape[0], base.block_table.shape[1])
+    dec = mla.Decoder(desc, device=DEV)
+    outs = [torch.empty((base.batch, 1, base.heads, 512), dtype=torch.float32, device=DEV) for _ in layers]
+    lses = [torch.empty((base.batch, 1, base.heads), dtype=torch.float32, device=DEV) for _ in layers]
+
+    def step():
+        dec.plan(base.seq_lens)
+        for (q, kv), o, l in zip(layers, outs, lses):
+            dec.planned(q, kv, base.block_table, base.seq_lens, base.scale, out=o, lse=l)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs + lses]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(4):
+        for t in outs + lses:
+            t.fill_(float("nan"))
+        dec.workspace.fill_(0xAB)                        # the plan too is remade by every replay
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs + lses, ref):
+            assert torch.equal(got, want), f"replay {rep} differs"

@@ -10,7 +10,7 @@ rotates over several copies so that repeated steps do not re-read it from the
 Default workload: the DeepSeek-V3-shape decode (batch 64, q_len 1, 128 heads,
 576/512 latent dims, seq_len 4096, bf16, 64-token pages).  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config c2] [--num-splits 0]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 5] [--config c2] [--num-splits 0]
 """
 from __future__ import annotations
 
@@ -500,7 +500,7 @@ def bench_merge_up_project(args) -> int:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="minimum wall time of the untimed warm-up (clocks settle)")

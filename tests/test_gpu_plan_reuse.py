@@ -7,7 +7,9 @@
 * one plan serves several layers (other queries and caches, the same block
   table and seq_lens), each layer within the bars of the oracle;
 * a workspace that holds no plan (never written: every work item and split
-  count out of range) is skipped, not followed: out and lse stay untouched.
+  count out of range) is skipped, not followed: out and lse stay untouched;
+* past 256 requests (planner kernel instead of in-kernel planning) every row
+  matches the oracle.
 """
 import dataclasses
 
@@ -103,3 +105,26 @@ def test_workspace_without_a_plan_is_not_followed():
     o_ref, l_ref = run_oracle(inp)
     compare(out, lse, o_ref, l_ref, what="after planning")
     assert np.isfinite(lse.cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_batch_past_the_fused_planner_matches_oracle(dtype):
+    """300 requests (more than the decode kernel plans for itself): the planner
+    kernel writes the split list, the decode follows it.  Every row against the
+    oracle; ragged lengths 0..400 with empty requests; the stored-plan call
+    gives the same bytes."""
+    say(f"batch 300 through the planner kernel, {dtype}")
+    rng = np.random.default_rng(66)
+    lens = rng.integers(0, 401, size=300)
+    lens[rng.choice(300, size=9, replace=False)] = 0
+    inp = workloads.make_decode_inputs(300, 1, 16, lens.tolist(), dtype, seed=67, device=dev())
+    d = decoder(inp)
+    out, lse = d(inp.q, inp.kv_cache, inp.block_table, inp.seq_lens, inp.scale, kv_scale=inp.kv_scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = run_oracle(inp)
+    compare(out, lse, o_ref, l_ref, dtype=dtype, what=f"batch 300 {dtype}")
+    d.plan(inp.seq_lens)
+    out2, lse2 = d.planned(inp.q, inp.kv_cache, inp.block_table, inp.seq_lens, inp.scale, kv_scale=inp.kv_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))

@@ -424,34 +424,6 @@ def probe_peaks() -> int:
     return 0
 
 
-def probe_lds() -> int:
-    """LDS read rate per CU (libmla_probe.so, built next to the decode library):
-    median bytes per core clock per workgroup for 1, 4, 8 and 16 waves per CU,
-    16- and 8-byte conflict-free reads, 8 or 15 reads in flight."""
-    import torch
-
-    torch.cuda.init()                      # the probe library runs on torch's HIP runtime
-    path = os.path.join(ROOT, "mla_latent_decode_absorbed_amd", "libmla_probe.so")
-    if not os.path.exists(path):
-        raise SystemExit(f"{path} is not built (build() of __graft_entry__)")
-    lib = ctypes.CDLL(path)
-    lib.mla_probe_lds_read_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                            ctypes.POINTER(ctypes.c_double)]
-    lib.mla_probe_lds_read_rate.restype = ctypes.c_int
-    rows = []
-    for wide in (1, 0):
-        for threads in (64, 256, 512, 1024):
-            for unroll in (8, 15):
-                v = ctypes.c_double(0.0)
-                st = lib.mla_probe_lds_read_rate(threads, unroll, wide, ctypes.byref(v))
-                if st != 0:
-                    raise SystemExit(f"probe failed ({st}) at threads {threads} unroll {unroll} wide {wide}")
-                rows.append({"read_bytes": 16 if wide else 8, "waves_per_cu": threads // 64,
-                             "reads_in_flight": unroll, "bytes_per_clk": round(v.value, 1)})
-    print(json.dumps({"probe": "LDS read rate per CU", "rows": rows}), flush=True)
-    return 0
-
-
 def bench_merge_up_project(args) -> int:
     """mla_merge_up_project on one DCP rank's shape: 4 shard partials of 32
     tokens x 512 heads (fp32 [4][16384][512] + LSEs) merged and mapped through
@@ -537,8 +509,6 @@ def main(argv=None) -> int:
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over the steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--probe-lds", action="store_true",
-                    help="print the LDS read rate per CU for 1-16 waves (libmla_probe.so) and exit")
     ap.add_argument("--probe-peaks", action="store_true",
                     help="print achievable HBM copy bandwidth and dense bf16/fp8 GEMM rates of this "
                          "GPU (torch's copy kernel and hipBLASLt) as one JSON line, and exit")
@@ -556,8 +526,6 @@ def main(argv=None) -> int:
 
     if args.probe_peaks:
         return probe_peaks()
-    if args.probe_lds:
-        return probe_lds()
     if args.op == "qprep":
         return bench_query_prep(args)
     if args.op == "upproj":

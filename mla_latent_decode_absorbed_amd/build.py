@@ -17,7 +17,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_decode.so")
-PROBE_LIB = os.path.join(PKG, "libmla_probe.so")   # measurement tool only (bench.py --probe-lds)
 SOURCES = [os.path.join(CSRC, "mla_kernels.hip"), os.path.join(CSRC, "mla_qprep.hip"),
            os.path.join(CSRC, "mla_upproj.hip"), os.path.join(CSRC, "mla_gather.hip"),
            os.path.join(CSRC, "mla_api.cpp")]
@@ -73,23 +72,7 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with status {res.returncode}")
     os.replace(tmp, LIB)
-    build_probe(verbose)
     return LIB
-
-
-def build_probe(verbose: bool = False) -> str:
-    """Compile the LDS read-rate probe (a measurement tool, not part of the
-    decode library) into the package's libmla_probe.so."""
-    tmp = PROBE_LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, os.path.join(CSRC, "probe_lds.hip")]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with status {res.returncode} (probe)")
-    os.replace(tmp, PROBE_LIB)
-    return PROBE_LIB
 
 
 if __name__ == "__main__":

@@ -32,10 +32,13 @@
  *    are valid once the stream has reached the call.
  *  - Host-checkable argument errors are reported by the return value BEFORE
  *    any device work is enqueued (see mla_status).  A failed kernel launch
- *    returns MLA_ERR_HIP.  Contract violations that only the device could see
- *    (a live block-table entry outside [0, num_pages), a seq_len beyond
- *    max_pages_per_seq * page_size) are not checked: seq_lens are clamped to
- *    the block-table capacity, and a bad page id is undefined behaviour.
+ *    returns MLA_ERR_HIP.  Contract violations that only the device can see
+ *    never make a kernel access memory outside its arguments, but give
+ *    meaningless results for the rows concerned: a seq_len beyond
+ *    max_pages_per_seq * page_size (or below 0) is clamped into
+ *    [0, max_pages_per_seq * page_size]; a live block-table entry outside
+ *    [0, num_pages) is clamped into the pool (a negative or too large id
+ *    reads page num_pages - 1).
  *  - Layouts are dense, row-major, with no padding unless stated.  Query and
  *    output rows of a request are ordered (query token t, head h).
  */
@@ -129,15 +132,6 @@ int mla_decode_partial(const mla_decode_desc* desc, const void* q, const void* k
                        const float* kv_scale, const int32_t* block_table,
                        const int32_t* seq_lens, float scale, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
-
-/* Same as mla_decode_partial; additionally records the two hipEvent_t
- * (passed as void*, either may be NULL) on `stream` immediately before and
- * after the split-KV decode kernel, so a caller can time that kernel alone. */
-int mla_decode_partial_timed(const mla_decode_desc* desc, const void* q, const void* kv_cache,
-                             const float* kv_scale, const int32_t* block_table,
-                             const int32_t* seq_lens, float scale, void* out, float* lse,
-                             void* workspace, size_t workspace_bytes, void* stream,
-                             void* event_before_decode, void* event_after_decode);
 
 /* The split plan of a decode step alone, for reuse by every layer's decode of
  * that step (page 2, the flashmla.py _build_decode excerpt: the scheduler

@@ -1,6 +1,7 @@
 // C ABI of the gfx950 MLA decode library: argument validation, workspace
 // layout and kernel launches.  Declarations and contracts: include/mla_decode.h.
 #include "mla_decode.h"
+#include "mla_decode_timing.h"
 #include "mla_internal.h"
 #include "mla_qprep.h"
 #include "mla_upproj.h"
@@ -75,6 +76,17 @@ WorkspaceLayout layout_for(const mla_decode_desc* d) {
     return L;
 }
 
+// The descriptor's checks and its workspace layout: every decode entry point
+// rejects a descriptor the same way, before looking at any pointer.
+int check_layout(const mla_decode_desc* d, WorkspaceLayout* L) {
+    const int st = check_desc(d);
+    if (st != MLA_OK) return st;
+    *L = layout_for(d);
+    // work-list slots are 32-bit indices, and each holds kMTile partial rows
+    if (L->units_max > INT32_MAX / mla::kMTile) return MLA_ERR_UNSUPPORTED;
+    return MLA_OK;
+}
+
 // The planner's inputs for one descriptor.
 mla::PlanParams plan_params(const mla_decode_desc* d, const WorkspaceLayout& L) {
     mla::PlanParams pp;
@@ -91,13 +103,12 @@ mla::PlanParams plan_params(const mla_decode_desc* d, const WorkspaceLayout& L) 
 
 int plan_impl(const mla_decode_desc* d, const int32_t* seq_lens, void* workspace, size_t workspace_bytes,
               void* stream) {
-    int st = check_desc(d);
+    WorkspaceLayout L;
+    const int st = check_layout(d, &L);
     if (st != MLA_OK) return st;
     if (!seq_lens || !aligned(seq_lens, 4)) return MLA_ERR_INVALID_ARG;
-    const WorkspaceLayout L = layout_for(d);
     if (!workspace || !aligned(workspace, kAlign)) return MLA_ERR_WORKSPACE;
     if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
-    if (L.units_max > INT32_MAX / mla::kMTile) return MLA_ERR_UNSUPPORTED;
     uint8_t* ws = (uint8_t*)workspace;
     if (mla::launch_plan(plan_params(d, L), seq_lens, (int32_t*)(ws + L.req_info),
                          (mla::WorkItem*)(ws + L.work), (hipStream_t)stream) != hipSuccess)
@@ -111,7 +122,8 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
                 const int32_t* block_table, const int32_t* seq_lens, float scale, void* out,
                 float* lse, void* workspace, size_t workspace_bytes, void* stream, void* ev0,
                 void* ev1, bool planned = false) {
-    int st = check_desc(d);
+    WorkspaceLayout L;
+    const int st = check_layout(d, &L);
     if (st != MLA_OK) return st;
     if (!q || !kv || !block_table || !seq_lens || !out || !lse) return MLA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(lse, 4) ||
@@ -120,10 +132,8 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     if (d->kv_dtype == MLA_FP8_E4M3 ? (kv_scale == nullptr) : (kv_scale != nullptr))
         return MLA_ERR_INVALID_ARG;
     if (!isfinite(scale) || !(scale > 0.f)) return MLA_ERR_INVALID_ARG;
-    const WorkspaceLayout L = layout_for(d);
     if (!workspace || !aligned(workspace, kAlign)) return MLA_ERR_WORKSPACE;
     if (workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
-    if (L.units_max > INT32_MAX / mla::kMTile) return MLA_ERR_UNSUPPORTED;
 
     hipStream_t s = (hipStream_t)stream;
     uint8_t* ws = (uint8_t*)workspace;
@@ -160,6 +170,7 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     dp.q_len = d->q_len;
     dp.causal = d->q_len > 1 ? d->causal : 0;
     dp.max_pages = d->max_pages_per_seq;
+    dp.num_pages = d->num_pages;
     dp.out_bf16 = d->out_dtype == MLA_BF16;
     const hipError_t de = d->kv_dtype == MLA_FP8_E4M3
                               ? mla::launch_decode_fp8(dp, (int)L.units_max, s, (hipEvent_t)ev0, (hipEvent_t)ev1)
@@ -187,9 +198,10 @@ extern "C" {
 
 int mla_decode_workspace_size(const mla_decode_desc* desc, size_t* bytes) {
     if (!bytes) return MLA_ERR_INVALID_ARG;
-    const int st = check_desc(desc);
+    WorkspaceLayout L;
+    const int st = check_layout(desc, &L);
     if (st != MLA_OK) return st;
-    *bytes = layout_for(desc).total;
+    *bytes = L.total;
     return MLA_OK;
 }
 

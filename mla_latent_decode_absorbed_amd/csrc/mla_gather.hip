@@ -161,7 +161,11 @@ __global__ __launch_bounds__(256) void merge_two_kernel(MergeTwoParams p) {
 
 }  // namespace
 
+// Each launcher reads hipGetLastError() once before its launch, so that a
+// stale error left by an unrelated earlier HIP call is not reported as this
+// launch's failure, and once after it for the launch's own status.
 hipError_t launch_gather_cache(const GatherParams& p, hipStream_t stream) {
+    (void)hipGetLastError();
     if (p.fp8) {
         const int64_t groups = (p.total_rows + kRowsPerWgFp8 - 1) / kRowsPerWgFp8;
         hipLaunchKernelGGL(gather_cache_kernel<kRowsPerWgFp8>, dim3((unsigned)groups), dim3(256), 0, stream, p);
@@ -174,6 +178,7 @@ hipError_t launch_gather_cache(const GatherParams& p, hipStream_t stream) {
 
 hipError_t launch_merge_two(const MergeTwoParams& p, hipStream_t stream) {
     const int64_t threads = (int64_t)p.rows * (p.head_dim / 4);
+    (void)hipGetLastError();
     hipLaunchKernelGGL(merge_two_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p);
     return hipGetLastError();
 }

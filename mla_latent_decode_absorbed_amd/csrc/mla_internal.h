@@ -47,8 +47,17 @@ struct DecodeParams {
     int32_t q_len;
     int32_t causal;
     int32_t max_pages;
+    int32_t num_pages;          // pages in the cache pool: every page id is clamped into [0, num_pages)
     int32_t out_bf16;
 };
+
+// A block-table entry as a page index that stays inside the pool: one
+// unsigned minimum maps a negative or too large id to the last page, so a bad
+// entry reads a wrong (but existing) page instead of faulting.
+__host__ __device__ inline int clamp_page(int pid, int num_pages) {
+    const unsigned int last = (unsigned int)num_pages - 1u;
+    return (int)((unsigned int)pid < last ? (unsigned int)pid : last);
+}
 
 struct CombineParams {
     const int32_t* req_info;    // [B][2]: splits, first kv-unit index

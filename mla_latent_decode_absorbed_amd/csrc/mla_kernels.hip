@@ -506,7 +506,7 @@ void decode_bf16_kernel(DecodeParams p) {
     // waits for the HBM -> LDS copies in flight, which vmcnt counts.  Callers
     // pass half pages inside [half_begin, half_end).
     const __attribute__((address_space(4))) int32_t* bt_s = (const __attribute__((address_space(4))) int32_t*)bt;
-    auto page_id = [&](int k) { return bt_s[k >> 1]; };
+    auto page_id = [&](int k) { return clamp_page(bt_s[k >> 1], p.num_pages); };
     auto half_src_of = [&](int pid, int k) { return kvbase + (size_t)pid * kPageBytes + (k & 1) * kSlotBytes; };
     auto half_src = [&](int k) { return half_src_of(page_id(k), k); };
     auto slot_addr = [&](int k) { return ring_addr + ((k - half_begin) & 3) * kSlotBytes; };
@@ -1110,16 +1110,16 @@ void decode_fp8_kernel(DecodeParams p) {
     // pages inside [pg_begin, pg_end)
     const __attribute__((address_space(4))) int32_t* bt_s = (const __attribute__((address_space(4))) int32_t*)bt;
     auto page_src_of = [&](int pid) { return kvbase + (size_t)pid * kPageBytes8; };
-    auto page_src = [&](int k) { return page_src_of(bt_s[k]); };
+    auto page_id = [&](int k) { return clamp_page(bt_s[k], p.num_pages); };
     auto slot_addr = [&](int k) { return ring_addr + ((k - pg_begin) & 3) * kSlotBytes; };
     auto slot_ptr = [&](int k) { return ring + ((k - pg_begin) & 3) * kSlotBytes; };
     // prologue: the first page, the query, then two more pages; loads retire
     // in issue order, so the first QK^T (which needs the first page and the
     // query) does not wait for the other two.  The three page ids are loaded
     // together up front.
-    const int pid0 = pg_begin < pg_end ? bt_s[pg_begin] : 0;
-    const int pid1 = pg_begin + 1 < pg_end ? bt_s[pg_begin + 1] : 0;
-    const int pid2 = pg_begin + 2 < pg_end ? bt_s[pg_begin + 2] : 0;
+    const int pid0 = pg_begin < pg_end ? page_id(pg_begin) : 0;
+    const int pid1 = pg_begin + 1 < pg_end ? page_id(pg_begin + 1) : 0;
+    const int pid2 = pg_begin + 2 < pg_end ? page_id(pg_begin + 2) : 0;
     auto issue_page = [&](int j3) {
         if (pg_begin + j3 < pg_end) {
             const uint8_t* src = page_src_of(j3 == 0 ? pid0 : j3 == 1 ? pid1 : pid2) + wave * 16 * kRowBytes8;
@@ -1409,7 +1409,7 @@ void decode_fp8_kernel(DecodeParams p) {
         int pid_copy;
         auto enter_sync = [&](int k) {
             wait_copies(k + 2 < pg_end ? 1 : 0);
-            pid_copy = bt_s[copy_page(k)];
+            pid_copy = page_id(copy_page(k));
             lds_sync();
         };
         auto enter = [&](int k) {

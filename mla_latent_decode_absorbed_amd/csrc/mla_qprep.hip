@@ -199,6 +199,7 @@ static void launch_ks(const QueryPrepParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_query_prep(const QueryPrepParams& p, hipStream_t stream) {
+    (void)hipGetLastError();   // a stale error of an earlier, unrelated HIP call is not this launch's
     switch (p.nope_dim / 16) {
         case 1: launch_ks<1>(p, stream); break;
         case 2: launch_ks<2>(p, stream); break;

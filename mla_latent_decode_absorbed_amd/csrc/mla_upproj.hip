@@ -230,6 +230,7 @@ hipError_t launch_up_project(const UpProjParams& p, hipStream_t stream) {
     const int mtiles = (p.rows + 31) / 32;
     const int groups = (p.heads * vchunks + 7) / 8;
     const dim3 grid((unsigned)(groups * 8 * mtiles));
+    (void)hipGetLastError();   // a stale error of an earlier, unrelated HIP call is not this launch's
     if (p.n_merge > 0) hipLaunchKernelGGL(up_project_kernel<2>, grid, dim3(256), 0, stream, p);
     else if (p.in_f32) hipLaunchKernelGGL(up_project_kernel<1>, grid, dim3(256), 0, stream, p);
     else hipLaunchKernelGGL(up_project_kernel<0>, grid, dim3(256), 0, stream, p);

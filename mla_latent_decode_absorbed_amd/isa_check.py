@@ -13,6 +13,21 @@ verifies the final instruction stream instead of trusting that:
 
 where `s_nop N` counts N + 1 wait states and every other instruction one.
 Used by build.py on the device assembly of the kernels source.
+
+Limits of the check (what it does not prove):
+  * it scans each function's text straight backwards from an instruction and
+    ignores control flow, so a hazard across a branch or a loop back edge
+    (a read at the top of a loop of a result written at its bottom) is not
+    seen;
+  * it treats only VALU instructions (v_* other than MFMAs) as readers of an
+    MFMA result: DS / buffer / global stores that read an MFMA destination,
+    and write-after-read / write-after-write hazards on an MFMA's srcC or
+    vdst, are not modelled;
+  * it applies one threshold (18) to every MFMA, including the 16-pass
+    v_mfma_f32_32x32x64_f8f6f4.
+The kernels therefore do not rely on it alone: every inline-assembly MFMA
+chain ends with explicit s_nop drains of 24 wait states before any other
+instruction can read its results, on every path.
 """
 from __future__ import annotations
 

@@ -1,10 +1,11 @@
-"""The C-ABI library loads, exports every symbol include/mla_decode.h declares,
+"""The C-ABI library loads, exports every symbol the headers under include/ declare,
 and rejects bad arguments with the documented status before any device work.
 
 No GPU is needed: every call here fails host-side validation (or only sizes the
 workspace), so nothing is enqueued.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -14,13 +15,16 @@ import mla_latent_decode_absorbed_amd as mla
 
 pytestmark = pytest.mark.cpu
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mla_decode.h")
+HEADERS = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                        "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(mla_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:int|const char\*)\s+(mla_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_binding_exports():

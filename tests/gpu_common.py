@@ -9,8 +9,11 @@ import torch
 
 from oracle import bf16_bits_to_f64, decode_partial_ref, e4m3_bits_to_f64, merge_ref
 
-#: max-abs-error bars (bf16: out 1e-2, lse 1e-3; fp8 cache: out 3e-2)
-TOL = {"bf16": (1e-2, 1e-3), "fp8": (3e-2, 1e-2)}
+#: max-abs-error bars: bf16 out 1e-2 and lse 1e-3; fp8 cache out 3e-2 and lse
+#: 1e-3 (the fp8 LSE bar is not fixed by the method's statement; 1e-3 is the
+#: bf16 bar, which the fp8 path meets: its logits are exact products of e4m3
+#: codes summed in fp32, like the bf16 path's)
+TOL = {"bf16": (1e-2, 1e-3), "fp8": (3e-2, 1e-3)}
 
 
 def say(msg: str) -> None:

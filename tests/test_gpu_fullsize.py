@@ -44,7 +44,7 @@ def test_dcp_rank_share_and_four_shard_merge():
     """One DCP rank's share (batch 32, 512 heads, 8192 local tokens), then the
     merge of all 4 ranks' partials (16384 rows, n = 4) on the device."""
     import mla_latent_decode_absorbed_amd as mla
-    req = sample(32, 4, 303)
+    req = sample(32, 8, 303)
     outs, lses, refs = [], [], []
     for r in range(4):
         say(f"full-size DCP rank {r}/4: batch32 H512 local 8192 bf16")

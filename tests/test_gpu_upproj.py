@@ -112,13 +112,47 @@ def _merge_inputs(n, R, H, seed):
     return outs, lses
 
 
+def check_merge_up(outs, lses, w, out, lse, tokens=None):
+    """The device's fused merge + up-projection against the oracle's LSE merge
+    followed by its up-projection, on every token or on the sampled ``tokens``
+    (all heads of each), within the bound derived in the module docstring plus
+    2^-20 of the partials' spread (the fp32 weighted sum of the merge)."""
+    from oracle import merge_ref
+    n, R, H, _ = outs.shape
+    vdim = w.shape[1]
+    sel = list(range(R)) if tokens is None else list(tokens)
+    T = len(sel)
+    o64 = np.nan_to_num(outs[:, sel].double().cpu().numpy(), nan=0.0)
+    l64 = lses[:, sel].double().cpu().numpy()
+    o_m, l_m = merge_ref(o64.reshape(n, T * H, 512), l64.reshape(n, T * H))
+    w64 = _f64(w)
+    exact = up_project_ref(o_m.reshape(T, H, 512), w64)
+    absdot = up_project_ref(np.abs(o_m).reshape(T, H, 512), np.abs(w64))
+    spread = up_project_ref(np.abs(o64).sum(axis=0), np.abs(w64))
+    delta = (2.0 ** -16 + 2.0 ** -13) * absdot + 2.0 ** -20 * spread
+    got = out[sel].double().cpu().numpy()
+    assert got.shape == (T, H, vdim)
+    assert np.isfinite(got).all()
+    if out.dtype == torch.float32:
+        assert (np.abs(got - exact) <= delta + 1e-30).all(), float((np.abs(got - exact) - delta).max())
+    else:
+        lo = bf16_bits_to_f64(bf16_encode(exact - delta))
+        hi = bf16_bits_to_f64(bf16_encode(exact + delta))
+        assert ((got >= lo) & (got <= hi)).all()
+    if lse is not None:
+        gl, rl = lse[sel].double().cpu().numpy().reshape(-1), l_m
+        assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+        fin = np.isfinite(rl)
+        assert (np.abs(gl[fin] - rl[fin]) <= 1e-5).all()
+    return got
+
+
 @pytest.mark.parametrize("n,R,H,vdim", [(1, 5, 3, 128), (2, 37, 2, 128), (4, 33, 4, 96), (7, 3, 2, 160),
                                         (16, 2, 2, 64)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_merge_up_project_matches_oracle(n, R, H, vdim, out_dtype):
     """mla_merge_up_project = the oracle's LSE merge followed by its up-projection."""
     import mla_latent_decode_absorbed_amd as mla
-    from oracle import merge_ref
     say(f"merge_up_project n={n} R={R} H={H} vdim={vdim} {out_dtype}")
     outs, lses = _merge_inputs(n, R, H, seed=n * 100 + R)
     w = workloads.make_up_project_inputs(1, H, vdim, seed=n, device=DEV).w_uv
@@ -126,27 +160,30 @@ def test_merge_up_project_matches_oracle(n, R, H, vdim, out_dtype):
     lse = torch.empty((R, H), dtype=torch.float32, device=DEV)
     mla.merge_up_project(outs.to(DEV), lses.to(DEV), n, w, out, lse)
     torch.cuda.synchronize()
-    o_m, l_m = merge_ref(np.nan_to_num(outs.double().numpy().reshape(n, R * H, 512), nan=0.0),
-                         lses.double().numpy().reshape(n, R * H))
-    w64 = _f64(w)
-    exact = up_project_ref(o_m.reshape(R, H, 512), w64)
-    absdot = up_project_ref(np.abs(o_m).reshape(R, H, 512), np.abs(w64))
-    spread = up_project_ref(np.nan_to_num(np.abs(outs.double().numpy())).sum(axis=0), np.abs(w64))
-    delta = (2.0 ** -16 + 2.0 ** -13) * absdot + 2.0 ** -20 * spread
-    got = out.double().cpu().numpy()
-    assert np.isfinite(got).all()
-    if out_dtype == torch.float32:
-        assert (np.abs(got - exact) <= delta + 1e-30).all()
-    else:
-        codes = out.view(torch.int16).cpu().numpy().view(np.uint16)
-        lo = bf16_bits_to_f64(bf16_encode(exact - delta))
-        hi = bf16_bits_to_f64(bf16_encode(exact + delta))
-        assert ((got >= lo) & (got <= hi)).all()
-    gl, rl = lse.double().cpu().numpy().reshape(-1), l_m
-    assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
-    fin = np.isfinite(rl)
-    assert (np.abs(gl[fin] - rl[fin]) <= 1e-5).all()
+    got = check_merge_up(outs, lses, w, out, lse)
     assert (got[1, 0] == 0).all()                      # all partials empty -> 0
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_merge_up_project_full_size_sampled(out_dtype):
+    """The one-DCP-rank shape (4 shard partials of 32 tokens x 512 heads, v_head_dim
+    128) against the oracle's merge + up-projection on a seeded sample of 8
+    tokens with every head; the all-empty row (token 1, head 0) is in the sample."""
+    import mla_latent_decode_absorbed_amd as mla
+    say(f"merge_up_project full size 4 x (32 x 512), 8 sampled tokens vs oracle, {out_dtype}")
+    n, R, H = 4, 32, 512
+    outs, lses = _merge_inputs(n, R, H, seed=11)
+    w = workloads.make_up_project_inputs(1, H, 128, seed=12, device=DEV).w_uv
+    out = torch.empty((R, H, 128), dtype=out_dtype, device=DEV)
+    lse = torch.empty((R, H), dtype=torch.float32, device=DEV)
+    mla.merge_up_project(outs.to(DEV), lses.to(DEV), n, w, out, lse)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    tokens = sorted(set(rng.choice(R, size=7, replace=False).tolist()) | {1})
+    while len(tokens) < 8:
+        tokens = sorted(set(tokens) | {int(rng.integers(R))})
+    got = check_merge_up(outs, lses, w, out, lse, tokens=tokens)
+    assert (got[tokens.index(1), 0] == 0).all()
 
 
 def test_merge_up_project_matches_unfused_full_size():

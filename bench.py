@@ -7,10 +7,18 @@ synthetic and already resident in HBM when the timed region starts; the cache
 rotates over several copies so that repeated steps do not re-read it from the
 256 MB Infinity Cache.
 
-Default workload: the DeepSeek-V3-shape decode (batch 64, q_len 1, 128 heads,
-576/512 latent dims, seq_len 4096, bf16, 64-token pages).  Prints ONE JSON line.
+Headline workload (default): the long-context, low-concurrency decode (batch
+4, q_len 2 causal, 128 heads, 576/512 latent dims, seq_len 131072, bf16,
+64-token pages, automatic split-KV).  The same JSON line carries keyed
+sub-records for the fp8-cache decode (batch 128, ragged 1k-16k), one DCP
+rank's share (batch 32, 512 heads, 8192 local tokens, plus the merge of its 4
+shard partials), the DeepSeek-V3-shape decode (batch 64, 128 heads, 4096) and
+the long-context decode at 256 and 64 splits per sequence.  Each record has
+its decode kernel's roofline (median of >= 50 event-timed launches, separate
+from the timed steps) and the fp64 oracle timed on the host's cores.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 5] [--config c2] [--num-splits 0]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config c5] [--num-splits 0]
+                    [--no-sub-records] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -28,18 +36,15 @@ if ROOT not in sys.path:
 
 METRIC = "MLA decode KV-cache GB/s + TFLOP/s (fraction of MI355X HBM/MFMA roofline)"
 HBM_PEAK_GBS = 8000.0
-# HIP events bracket the measured kernel in every EVENT_EVERY-th timed step:
-# a timing event pair costs ~5.8 us of every step it brackets (DeepSeek-V3
-# shape: 110.7 us per step with events on every step, 104.9 without, 106.6
-# with every fourth), which the wall-clock step time should not carry.
-EVENT_EVERY = 4
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 FLOP_PER_ROW_TOKEN = 2 * (576 + 512)
 KERNEL_SRC = os.path.join(ROOT, "mla_latent_decode_absorbed_amd", "csrc", "mla_kernels.hip")
 # rocprofv3 counter summaries (HBM traffic, MFMA/LDS utilisation) of the decode
 # kernel on a workload, used while the kernel sources hash to the profiled ones
 PMC_FILES = {"c2": os.path.join(ROOT, "profiles", "decode_kernel_c2_pmc.json"),
-             "c4": os.path.join(ROOT, "profiles", "decode_fp8_kernel_c4_pmc.json")}
+             "c3": os.path.join(ROOT, "profiles", "decode_kernel_c3_pmc.json"),
+             "c4": os.path.join(ROOT, "profiles", "decode_fp8_kernel_c4_pmc.json"),
+             "c5": os.path.join(ROOT, "profiles", "decode_kernel_c5_pmc.json")}
 
 WORKLOAD_NAMES = {
     "c2": "DeepSeek-V3-shape decode on one unsharded cache: batch 64, q_len 1, 128 heads, "
@@ -107,23 +112,28 @@ def workload_accounting(inp) -> dict:
                 flops=flops, rows=rows, tokens=tokens)
 
 
+def oracle_threads() -> int:
+    """Threads the oracle's BLAS runs on (threadpoolctl's view), else the host's CPUs."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count()]))
+    except Exception:
+        return int(os.cpu_count() or 1)
+
+
 def cpu_baseline(inp, budget_s: float = 20.0) -> dict:
     """The fp64 oracle on this host's cores over whole requests of the same workload
     (as many as fit a ~budget_s time box, at least one)."""
     import numpy as np
     import torch
     from oracle import bf16_bits_to_f64, decode_partial_ref, e4m3_bits_to_f64
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count()])
-    except Exception:
-        threads = os.cpu_count()
     bt_all = inp.block_table.cpu().numpy()
     sl_all = inp.seq_lens.cpu().numpy()
     dec = bf16_bits_to_f64 if inp.dtype == "bf16" else e4m3_bits_to_f64
     view = (lambda x: x.view(torch.int16)) if inp.dtype == "bf16" else (lambda x: x)
-    done_bytes, done_req, spent = 0, 0, 0.0
+    done_bytes, done_flops, done_req, spent = 0, 0, 0, 0.0
     e = 2 if inp.dtype == "bf16" else 1
+    T = inp.q_len
     for b in range(inp.batch):
         n = int(sl_all[b])
         pages = bt_all[b][: (n + 63) // 64]
@@ -136,10 +146,13 @@ def cpu_baseline(inp, budget_s: float = 20.0) -> dict:
                            kv_scale=inp.kv_scale_value, causal=inp.causal)
         spent += time.perf_counter() - t0
         done_bytes += n * 576 * e
+        vis = sum(max(n - (T - 1 - t), 0) for t in range(T)) if inp.causal and T > 1 else n * T
+        done_flops += vis * inp.heads * FLOP_PER_ROW_TOKEN
         done_req += 1
         if spent >= budget_s:
             break
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s",
+            "tflops": round(done_flops / spent / 1e12, 5), "cores": oracle_threads(), "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": f"{done_req} of {inp.batch} requests (whole requests, all heads), "
                       f"{done_bytes / 1e6:.1f} MB of KV, {spent:.2f} s of fp64 numpy on the host"}
@@ -211,16 +224,18 @@ def bench_query_prep(args) -> int:
             done += 1
         per_row = (H * P * 2 + H * 64 * 2 + H * 576 * e)
         res["cpu_baseline"] = {"value": round((w_bytes * done / R + per_row * done) / spent / 1e9, 4),
-                               "unit": "GB/s", "cores": int(os.cpu_count() or 1), "kind": "oracle",
+                               "unit": "GB/s", "cores": oracle_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                                "sample": f"{done} of {R} rows (all heads), {spent:.2f} s of fp64 numpy"}
     print(json.dumps(res), flush=True)
     return 0
 
 
 def _time_launches(step, args):
-    """Warm-up (at least W calls and --warmup-seconds), then K timed calls with
-    torch events around each; returns (ms per call by the wall clock, average
-    event-timed ms, warm-up calls run)."""
+    """Warm-up (at least W calls and --warmup-seconds), then K calls timed by
+    the wall clock between synchronisations, then a separate loop of
+    --event-launches (>= 50) calls each bracketed by torch events on the
+    current stream; returns (ms per call by the wall clock, median event-timed
+    ms, warm-up calls run)."""
     import torch
     step(0)
     torch.cuda.synchronize()
@@ -229,19 +244,19 @@ def _time_launches(step, args):
         step(n_warm)
         n_warm += 1
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(0, args.steps, EVENT_EVERY)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        timed = i % EVENT_EVERY == 0
-        if timed:
-            evs[i // EVENT_EVERY][0].record()
         step(i)
-        if timed:
-            evs[i // EVENT_EVERY][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall * 1e3 / args.steps, sum(a.elapsed_time(b) for a, b in evs) / len(evs), n_warm
+    n_ev = max(args.event_launches, 50)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        step(i)
+        b.record()
+    torch.cuda.synchronize()
+    return wall * 1e3 / args.steps, median([a.elapsed_time(b) for a, b in evs]), n_warm
 
 
 def bench_up_project(args) -> int:
@@ -301,7 +316,7 @@ def bench_up_project(args) -> int:
             done += 1
         per_row = H * 512 * 4 + H * Vd * 2
         res["cpu_baseline"] = {"value": round((w_bytes * done / R + per_row * done) / spent / 1e9, 4),
-                               "unit": "GB/s", "cores": int(os.cpu_count() or 1), "kind": "oracle",
+                               "unit": "GB/s", "cores": oracle_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                                "sample": f"{done} of {R} rows (all heads), {spent:.2f} s of fp64 numpy"}
     print(json.dumps(res), flush=True)
     return 0
@@ -491,8 +506,321 @@ def bench_merge_up_project(args) -> int:
             done += 1
         per_row = H * (n * (512 * 4 + 4) + Vd * 2)
         res["cpu_baseline"] = {"value": round((H * Vd * 512 * 2 * done / R + per_row * done) / spent / 1e9, 4),
-                               "unit": "GB/s", "cores": int(os.cpu_count() or 1), "kind": "oracle",
+                               "unit": "GB/s", "cores": oracle_threads(), "cpu_model": cpu_model(), "kind": "oracle",
                                "sample": f"{done} of {R} tokens (all heads), {spent:.2f} s of fp64 numpy"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_model() -> str | None:
+    """The host CPU's model name (first /proc/cpuinfo entry), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def make_workload(name: str, seed, dev):
+    import workloads
+    kw = dict(shard_only=0) if name == "c3" else {}
+    return workloads.make_config(name, seed=seed, device=dev, poison=False, extra_pages=0, **kw)
+
+
+def decode_roofline(acc, dtype: str, kern_ms: float) -> dict:
+    """The decode kernel's roofline: the binding roof of the workload's
+    arithmetic intensity (FLOP per byte of KV + q against the peaks' ratio),
+    the algorithmic bytes or flops per launch over the kernel's time."""
+    peak_tf = MFMA_PEAK_TFLOPS[dtype]
+    ai = acc["flops"] / (acc["kv_bytes"] + acc["q_bytes"])
+    k_bytes = acc["kv_bytes"] + acc["q_bytes"] + acc["bt_bytes"]
+    if ai < peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9):
+        achieved = k_bytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = acc["flops"] / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(achieved / peak_tf, 4)}
+    roof["kernel_ms"] = round(kern_ms, 5)
+    roof["algorithmic_bytes_per_launch"] = k_bytes
+    roof["algorithmic_flops_per_launch"] = acc["flops"]
+    return roof
+
+
+def stored_counters(name: str, num_splits: int, seed) -> tuple:
+    """(HBM bytes per launch, utilisation counters) of the decode kernel on a
+    workload from its rocprofv3 summary, while the kernel sources hash to the
+    profiled ones; (None, None) otherwise."""
+    pmc_file = PMC_FILES.get(name)
+    if not pmc_file or not os.path.exists(pmc_file) or num_splits != 0 or seed is not None:
+        return None, None
+    pmc = json.load(open(pmc_file))
+    if pmc.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None, None
+    return pmc.get("hbm_bytes_per_launch"), {k: pmc.get(k) for k in (
+        "MfmaUtil_percent", "LdsUtil_percent", "LdsBankConflict_per_access", "mfma_flops_per_launch")}
+
+
+def decode_record(name: str, inp, args, hev, num_splits: int, steps: int, cpu_budget: float) -> dict:
+    """One workload through mla_decode_partial: warm-up, `steps` whole steps
+    timed by the wall clock between synchronisations, then a separate loop of
+    `--event-launches` calls whose decode kernel is bracketed by HIP events on
+    the stream it runs on (median duration).  Inputs are resident in HBM; the
+    cache rotates over `--copies` copies."""
+    import torch
+    import mla_latent_decode_absorbed_amd as mla
+
+    dev = inp.q.device
+    acc = workload_accounting(inp)
+    desc = mla.make_desc(inp.batch, inp.q_len, inp.heads, inp.kv_cache.shape[0], inp.block_table.shape[1],
+                         kv_dtype=mla.BF16 if inp.dtype == "bf16" else mla.FP8_E4M3,
+                         causal=1 if inp.causal else 0, num_splits=num_splits)
+    dec = mla.Decoder(desc, device=dev)
+    copies = [inp.kv_cache] + [inp.kv_cache.clone() for _ in range(max(args.copies, 1) - 1)]
+    out = torch.empty((inp.batch, inp.q_len, inp.heads, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((inp.batch, inp.q_len, inp.heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        dec(inp.q, copies[i % len(copies)], inp.block_table, inp.seq_lens, inp.scale,
+            kv_scale=inp.kv_scale, out=out, lse=lse, stream=stream, events=events)
+
+    # warm-up: at least W steps and at least --warmup-seconds of back-to-back
+    # work (the first call, module load and first touch, excluded), so that
+    # clocks have settled before the timed region
+    step(0)
+    torch.cuda.synchronize()
+    n_warm, t_w = 1, time.perf_counter()
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
+        step(n_warm)
+        n_warm += 1
+        if n_warm % 64 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / steps
+
+    n_ev = max(args.event_launches, 50)
+    evs = [(hev.create(), hev.create()) for _ in range(n_ev)]
+    for i in range(n_ev):
+        step(i, events=evs[i])
+    torch.cuda.synchronize()
+    kern = [hev.elapsed_ms(a, b) for a, b in evs]
+    for a, b in evs:
+        hev.destroy(a)
+        hev.destroy(b)
+    kern_ms = median(kern)
+
+    # split counts the planner chose (the workspace's first 2 B int32: splits, first kv-unit)
+    info = dec.workspace[: 8 * inp.batch].view(torch.int32).view(inp.batch, 2)[:, 0].cpu()
+    partial_rows = int(sum(int(sp) for sp in info.tolist() if sp > 1) * inp.q_len * inp.heads)
+    partial_bytes = partial_rows * (512 * 4 + 4)
+
+    peak_tf = MFMA_PEAK_TFLOPS[inp.dtype]
+    kv_gbs = acc["kv_bytes"] / (ms_per_step * 1e-3) / 1e9
+    tflops = acc["flops"] / (ms_per_step * 1e-3) / 1e12
+    total_gbs = (acc["kv_bytes"] + acc["q_bytes"] + acc["bt_bytes"] + acc["out_bytes"]) / (ms_per_step * 1e-3) / 1e9
+    roof = decode_roofline(acc, inp.dtype, kern_ms)
+    traffic, counters = stored_counters(name, num_splits, args.seed)
+    roof["traffic"] = traffic
+    roof["counters"] = counters
+    roof["kernel_ms_min_max"] = [round(min(kern), 5), round(max(kern), 5)]
+    roof["event_timed_launches"] = n_ev
+    rec = {
+        "workload": f"{name}: {WORKLOAD_NAMES[name]}",
+        "num_splits": num_splits or "auto",
+        "value": round(kv_gbs, 2), "unit": "GB/s", "steps": steps, "warmup_steps_run": n_warm,
+        "ms_per_step": round(ms_per_step, 5), "dtype": inp.dtype,
+        "tflops": round(tflops, 2),
+        "fractions": {"hbm_kv_only": round(kv_gbs / HBM_PEAK_GBS, 4),
+                      "hbm_all_algorithmic_bytes": round(total_gbs / HBM_PEAK_GBS, 4),
+                      "mfma": round(tflops / peak_tf, 4),
+                      "binding_roof": round(max(acc["kv_bytes"] / (HBM_PEAK_GBS * 1e9),
+                                                acc["flops"] / (peak_tf * 1e12)) / (ms_per_step * 1e-3), 4)},
+        "roofline": roof,
+        "split_partials": {"splits_per_request_min_max": [int(info.min()), int(info.max())],
+                           "partial_bytes_written_and_read": 2 * partial_bytes,
+                           "overhead_vs_kv_bytes": round(2 * partial_bytes / acc["kv_bytes"], 4)},
+        "shape": {"batch": inp.batch, "q_len": inp.q_len, "heads": inp.heads,
+                  "seq_lens_total": acc["tokens"], "cache_copies_rotated": len(copies)},
+    }
+    if cpu_budget > 0:
+        rec["cpu_baseline"] = cpu_baseline(inp, budget_s=cpu_budget)
+    rec["_decoder"] = (dec, out, lse, stream, copies)
+    return rec
+
+
+def dcp_merge_record(args, inp0, rec0, cpu_budget: float) -> dict:
+    """One DCP rank's share, 4 shards: mla_merge_states of the 4 shard partials
+    (n = 4, 16,384 rows) with its own roofline (HBM: 4 x 2052 B in and 2052 B
+    out per row; median of >= 50 event-timed calls), and all 4 shard decodes
+    plus that merge, for information.  Shards 1-3 are built like shard 0."""
+    import numpy as np
+    import torch
+    import mla_latent_decode_absorbed_amd as mla
+    import workloads
+
+    dev = inp0.q.device
+    dec, out0, lse0, stream, _ = rec0["_decoder"]
+    shards = [inp0] + [workloads.make_config("c3", seed=args.seed, device=dev, poison=False, extra_pages=0,
+                                             shard_only=r) for r in (1, 2, 3)]
+    rows = inp0.batch * inp0.q_len * inp0.heads
+    outs = torch.empty((4, rows, 512), dtype=torch.float32, device=dev)
+    lses = torch.empty((4, rows), dtype=torch.float32, device=dev)
+    mo = torch.empty((rows, 512), dtype=torch.float32, device=dev)
+    ml = torch.empty(rows, dtype=torch.float32, device=dev)
+
+    def all_shards():
+        for r, sh in enumerate(shards):
+            dec(sh.q, sh.kv_cache, sh.block_table, sh.seq_lens, sh.scale, out=outs[r].view_as(out0),
+                lse=lses[r].view_as(lse0), stream=stream)
+        mla.merge_states(outs, lses, 4, rows, mo, ml, stream=stream)
+
+    def merge_only():
+        mla.merge_states(outs, lses, 4, rows, mo, ml, stream=stream)
+
+    all_shards()
+    torch.cuda.synchronize()
+    for _ in range(5):
+        merge_only()
+    n_ev = max(args.event_launches, 50)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for a, b in evs:
+        a.record(stream)
+        merge_only()
+        b.record(stream)
+    torch.cuda.synchronize()
+    merge_ms = median([a.elapsed_time(b) for a, b in evs])
+    for _ in range(2):
+        all_shards()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(10):
+        all_shards()
+    b.record(stream)
+    torch.cuda.synchronize()
+    merge_bytes = 4 * rows * 2052 + rows * 2052
+    achieved = merge_bytes / (merge_ms * 1e-3) / 1e9
+    res = {"what": "mla_merge_states of the 4 shard partials (n = 4, 16,384 rows; 4 x 2052 B in and 2052 B "
+                   "out per row); and the 4 shard decodes plus that merge",
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel_ms": round(merge_ms, 5),
+                        "algorithmic_bytes_per_launch": merge_bytes, "event_timed_launches": n_ev},
+           "four_shards_and_merge_ms": round(a.elapsed_time(b) / 10, 5)}
+    if cpu_budget > 0:
+        from oracle import merge_ref
+        o64 = outs.double().cpu().numpy()
+        l64 = lses.double().cpu().numpy()
+        done, spent = 0, 0.0
+        while done < rows and spent < cpu_budget:
+            t = time.perf_counter()
+            merge_ref(o64[:, done:done + 512], l64[:, done:done + 512])
+            spent += time.perf_counter() - t
+            done += 512
+        res["cpu_baseline"] = {"value": round(done * 2052 * 5 / spent / 1e9, 4), "unit": "GB/s",
+                               "cores": oracle_threads(), "cpu_model": cpu_model(), "kind": "oracle",
+                               "sample": f"{done} of {rows} rows (blocks of 512), {spent:.2f} s of fp64 numpy"}
+    return res
+
+
+def plan_reuse_timings(args, inp, rec) -> dict:
+    """The same decode with the split plan made once per step and reused by
+    every layer: mla_decode_plan alone, and one layer's decode on the stored
+    plan (mla_decode_partial_planned: decode + combine, no planning), each
+    averaged over back-to-back launches, for information."""
+    import torch
+    dec, out, lse, stream, copies = rec["_decoder"]
+
+    def plan():
+        dec.plan(inp.seq_lens, stream=stream)
+
+    def layer(i):
+        dec.planned(inp.q, copies[i % len(copies)], inp.block_table, inp.seq_lens, inp.scale,
+                    kv_scale=inp.kv_scale, out=out, lse=lse, stream=stream)
+
+    res = {}
+    for name, fn, reps in (("plan_ms", lambda i: plan(), 50), ("layer_decode_on_stored_plan_ms", layer, 50)):
+        for i in range(5):
+            fn(i)
+        plan()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        res[name] = round(a.elapsed_time(b) / reps, 5)
+    return res
+
+
+def bench_decode(args) -> int:
+    """The headline line: mla_decode_partial on the --config workload (default:
+    the long-context bf16 decode), with keyed sub-records for the fp8 cache
+    decode, one DCP rank's share (plus its 4-shard merge), the DeepSeek-V3-shape
+    decode and the long-context decode at 256 and 64 splits per sequence."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    hev = HipEvents()
+    t_setup = time.perf_counter()
+    inp = make_workload(args.config, args.seed, dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    head = decode_record(args.config, inp, args, hev, args.num_splits, args.steps,
+                         0.0 if args.no_cpu_baseline else 20.0)
+    res = {
+        "metric": METRIC,
+        "value": head["value"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "warmup_steps_run": head["warmup_steps_run"], "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"],
+        "data": "synthetic (seeded N(0,1) query and latent cache, shuffled 64-token pages)",
+        "config": {"workload": head["workload"], "batch": inp.batch, "q_len": inp.q_len, "heads": inp.heads,
+                   "seq_lens_total": head["shape"]["seq_lens_total"], "num_splits": head["num_splits"],
+                   "cache_copies_rotated": head["shape"]["cache_copies_rotated"]},
+        "tflops": head["tflops"], "fractions": head["fractions"], "roofline": head["roofline"],
+        "split_partials": head["split_partials"], "setup_s": round(setup_s, 2),
+    }
+    res["plan_reuse"] = plan_reuse_timings(args, inp, head)
+    if "cpu_baseline" in head:
+        res["cpu_baseline"] = head["cpu_baseline"]
+    if args.config == "c3" and args.num_splits == 0:
+        res["dcp_rank_merge"] = dcp_merge_record(args, inp, head, 0.0 if args.no_cpu_baseline else 5.0)
+    del head["_decoder"]
+    del inp
+    torch.cuda.empty_cache()
+
+    if not args.no_sub_records:
+        subs = {}
+        plan = [("c4", "c4", 0), ("c3", "c3", 0), ("c2", "c2", 0)]
+        if args.config == "c5":
+            plan += [("c5_splits256", "c5", 256), ("c5_splits64", "c5", 64)]
+        for key, name, ns in plan:
+            if name == args.config and ns == args.num_splits:
+                continue
+            sub_inp = make_workload(name, args.seed, dev)
+            rec = decode_record(name, sub_inp, args, hev, ns, args.sub_steps,
+                                0.0 if (args.no_cpu_baseline or ns) else 5.0)
+            if name == "c3" and ns == 0:
+                rec["dcp_rank_merge"] = dcp_merge_record(args, sub_inp, rec, 0.0 if args.no_cpu_baseline else 3.0)
+            del rec["_decoder"]
+            subs[key] = rec
+            del sub_inp
+            torch.cuda.empty_cache()
+        res["sub_records"] = subs
     print(json.dumps(res), flush=True)
     return 0
 
@@ -500,13 +828,19 @@ def bench_merge_up_project(args) -> int:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--warmup-seconds", type=float, default=1.0,
                     help="minimum wall time of the untimed warm-up (clocks settle)")
-    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--config", default="c5", choices=sorted(WORKLOAD_NAMES),
+                    help="headline workload (default c5, the long-context bf16 decode)")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--copies", type=int, default=3, help="cache copies rotated over the steps")
+    ap.add_argument("--event-launches", type=int, default=60,
+                    help="event-timed decode launches per workload (median; at least 50)")
+    ap.add_argument("--sub-steps", type=int, default=50, help="whole steps timed per sub-record")
+    ap.add_argument("--no-sub-records", action="store_true",
+                    help="only the headline workload (no fp8 / DCP-rank / DeepSeek-V3-shape / split records)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--probe-peaks", action="store_true",
@@ -535,197 +869,7 @@ def main(argv=None) -> int:
     if args.op == "mergeup":
         return bench_merge_up_project(args)
 
-    import torch
-    import mla_latent_decode_absorbed_amd as mla
-    import workloads
-
-    dev = torch.device("cuda:0")
-    t_setup = time.perf_counter()
-    if args.config == "c3":
-        inp = workloads.make_config("c3", seed=args.seed, device=dev, poison=False, extra_pages=0,
-                                    shard_only=0)
-    else:
-        inp = workloads.make_config(args.config, seed=args.seed, device=dev, poison=False, extra_pages=0)
-    acc = workload_accounting(inp)
-    desc = mla.make_desc(inp.batch, inp.q_len, inp.heads, inp.kv_cache.shape[0], inp.block_table.shape[1],
-                         kv_dtype=mla.BF16 if inp.dtype == "bf16" else mla.FP8_E4M3,
-                         causal=1 if inp.causal else 0, num_splits=args.num_splits)
-    dec = mla.Decoder(desc, device=dev)
-    copies = [inp.kv_cache] + [inp.kv_cache.clone() for _ in range(max(args.copies, 1) - 1)]
-    out = torch.empty((inp.batch, inp.q_len, inp.heads, 512), dtype=torch.float32, device=dev)
-    lse = torch.empty((inp.batch, inp.q_len, inp.heads), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-    setup_s = time.perf_counter() - t_setup
-
-    hev = HipEvents()
-    evs = [(hev.create(), hev.create()) for _ in range(0, args.steps, EVENT_EVERY)]
-    stream = torch.cuda.current_stream()
-
-    def step(i, events=None):
-        dec(inp.q, copies[i % len(copies)], inp.block_table, inp.seq_lens, inp.scale,
-            kv_scale=inp.kv_scale, out=out, lse=lse, stream=stream, events=events)
-
-    # warm-up: at least W steps and at least --warmup-seconds of back-to-back
-    # work, so that the clocks have settled before the timed region
-    step(0)                      # first call: module load and first-touch costs
-    torch.cuda.synchronize()
-    n_warm, t_w = 1, time.perf_counter()
-    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_seconds:
-        step(n_warm)
-        n_warm += 1
-        if n_warm % 64 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, events=evs[i // EVENT_EVERY] if i % EVENT_EVERY == 0 else None)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [hev.elapsed_ms(a, b) for a, b in evs]
-    for a, b in evs:
-        hev.destroy(a)
-        hev.destroy(b)
-
-    ms_per_step = wall * 1e3 / args.steps
-    kern_avg_ms = sum(kern_ms) / len(kern_ms)
-
-    kv_gbs = acc["kv_bytes"] / (ms_per_step * 1e-3) / 1e9
-    tflops = acc["flops"] / (ms_per_step * 1e-3) / 1e12
-    total_gbs = (acc["kv_bytes"] + acc["q_bytes"] + acc["bt_bytes"] + acc["out_bytes"]) / (ms_per_step * 1e-3) / 1e9
-    peak_tf = MFMA_PEAK_TFLOPS[inp.dtype]
-    ai = acc["flops"] / (acc["kv_bytes"] + acc["q_bytes"])
-    bound = "hbm" if ai < peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9) else "mfma"
-    # dominant kernel: the split-KV decode kernel; its algorithmic reads are KV + q + live block-table rows
-    k_bytes = acc["kv_bytes"] + acc["q_bytes"] + acc["bt_bytes"]
-    if bound == "hbm":
-        achieved = k_bytes / (kern_avg_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        achieved = acc["flops"] / (kern_avg_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf, "unit": "TFLOP/s",
-                "frac": round(achieved / peak_tf, 4)}
-    traffic, counters = None, None
-    pmc_file = PMC_FILES.get(args.config)
-    if pmc_file and os.path.exists(pmc_file) and args.num_splits == 0 and args.seed is None:
-        pmc = json.load(open(pmc_file))
-        if pmc.get("kernel_source_sha256_16") == kernel_source_hash():
-            traffic = pmc.get("hbm_bytes_per_launch")
-            counters = {k: pmc.get(k) for k in ("MfmaUtil_percent", "LdsUtil_percent",
-                                                "LdsBankConflict_per_access", "mfma_flops_per_launch")}
-    roof["traffic"] = traffic
-    roof["counters"] = counters
-    roof["kernel_ms"] = round(kern_avg_ms, 5)
-    roof["algorithmic_bytes_per_launch"] = k_bytes
-
-    res = {
-        "metric": METRIC,
-        "value": round(kv_gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "warmup_steps_run": n_warm,
-        "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": inp.dtype,
-        "data": "synthetic (seeded N(0,1) query and latent cache, shuffled 64-token pages)",
-        "config": {"workload": f"{args.config}: {WORKLOAD_NAMES[args.config]}", "batch": inp.batch,
-                   "q_len": inp.q_len, "heads": inp.heads, "seq_lens_total": acc["tokens"],
-                   "num_splits": args.num_splits or "auto", "cache_copies_rotated": len(copies)},
-        "tflops": round(tflops, 2),
-        "fractions": {"hbm_kv_only": round(kv_gbs / HBM_PEAK_GBS, 4),
-                      "hbm_all_algorithmic_bytes": round(total_gbs / HBM_PEAK_GBS, 4),
-                      "mfma": round(tflops / peak_tf, 4),
-                      "binding_roof": round(max(acc["kv_bytes"] / (HBM_PEAK_GBS * 1e9),
-                                                acc["flops"] / (peak_tf * 1e12)) / (ms_per_step * 1e-3), 4)},
-        "roofline": roof,
-        "setup_s": round(setup_s, 2),
-    }
-    res["plan_reuse"] = plan_reuse_timings(args, inp, dec, copies, out, lse, stream)
-    if args.config == "c3" and args.num_splits == 0:
-        res["dcp_rank_merge"] = dcp_merge_timings(args, inp, dec, out, lse, stream)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp)
-    print(json.dumps(res), flush=True)
-    return 0
-
-
-def plan_reuse_timings(args, inp, dec, copies, out, lse, stream) -> dict:
-    """The same decode with the split plan made once per step and reused by
-    every layer: mla_decode_plan alone, and one layer's decode on the stored
-    plan (mla_decode_partial_planned: decode + combine, no planning), each
-    averaged over back-to-back launches, for information."""
-    import torch
-
-    def plan():
-        dec.plan(inp.seq_lens, stream=stream)
-
-    def layer(i):
-        dec.planned(inp.q, copies[i % len(copies)], inp.block_table, inp.seq_lens, inp.scale,
-                    kv_scale=inp.kv_scale, out=out, lse=lse, stream=stream)
-
-    res = {}
-    for name, fn, reps in (("plan_ms", lambda i: plan(), 50), ("layer_decode_on_stored_plan_ms", layer, args.steps)):
-        for i in range(5):
-            fn(i)
-        plan()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(reps):
-            fn(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        res[name] = round(a.elapsed_time(b) / reps, 5)
-    return res
-
-
-def dcp_merge_timings(args, inp0, dec, out0, lse0, stream) -> dict:
-    """One DCP rank's share, 4 shards: the LSE merge of the 4 shard partials
-    (mla_merge_states, n = 4, 16,384 rows) alone, and all 4 shard decodes plus
-    that merge, for information.  The other 3 shards are built like shard 0."""
-    import torch
-    import mla_latent_decode_absorbed_amd as mla
-    import workloads
-
-    dev = inp0.q.device
-    shards = [inp0] + [workloads.make_config("c3", seed=args.seed, device=dev, poison=False, extra_pages=0,
-                                             shard_only=r) for r in (1, 2, 3)]
-    rows = inp0.batch * inp0.q_len * inp0.heads
-    outs = torch.empty((4, rows, 512), dtype=torch.float32, device=dev)
-    lses = torch.empty((4, rows), dtype=torch.float32, device=dev)
-    mo = torch.empty((rows, 512), dtype=torch.float32, device=dev)
-    ml = torch.empty(rows, dtype=torch.float32, device=dev)
-
-    def all_shards():
-        for r, sh in enumerate(shards):
-            dec(sh.q, sh.kv_cache, sh.block_table, sh.seq_lens, sh.scale, out=outs[r].view_as(out0),
-                lse=lses[r].view_as(lse0), stream=stream)
-        mla.merge_states(outs, lses, 4, rows, mo, ml, stream=stream)
-
-    def merge_only():
-        mla.merge_states(outs, lses, 4, rows, mo, ml, stream=stream)
-
-    all_shards()
-    torch.cuda.synchronize()
-    res = {}
-    for name, fn, reps in (("merge_ms", merge_only, max(args.steps, 20)), ("four_shards_and_merge_ms", all_shards, 10)):
-        for _ in range(3):
-            fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        res[name] = round(a.elapsed_time(b) / reps, 5)
-    merge_bytes = 4 * rows * 2052 + rows * 2052
-    res["merge_gbs"] = round(merge_bytes / (res["merge_ms"] * 1e-3) / 1e9, 1)
-    res["what"] = ("mla_merge_states of the 4 shard partials (n = 4, 16,384 rows; 4 x 2052 B in and 2052 B "
-                   "out per row), and the 4 shard decodes plus that merge")
-    return res
+    return bench_decode(args)
 
 
 if __name__ == "__main__":

@@ -251,3 +251,28 @@ def test_three_row_tiles_partial_last(dtype):
     out, lse = run_hip(inp, num_splits=2)
     o_ref, l_ref = run_oracle(inp)
     compare(out, lse, o_ref, l_ref, dtype=dtype, what=f"300 rows {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_out_of_pool_page_ids_are_clamped(dtype):
+    """Live block-table entries outside [0, num_pages) (-1, num_pages, a large id)
+    read page num_pages - 1 instead of memory outside the cache: the result
+    equals the oracle's on the table with those entries replaced by
+    num_pages - 1, and the requests with valid tables are unaffected."""
+    import dataclasses
+    say(f"out-of-pool page ids clamped, {dtype}")
+    # (no NaN poison here: page num_pages - 1 may be an unused pool page)
+    inp = workloads.make_decode_inputs(4, 1, 128, [200, 129, 64, 300], dtype, seed=31, device=dev(),
+                                       poison=False)
+    P = inp.kv_cache.shape[0]
+    bt = inp.block_table.clone()
+    clamped = bt.clone()
+    for (b, j, bad_id) in ((0, 1, -1), (1, 0, P), (3, 4, 1 << 30)):   # live entries of requests 0, 1, 3
+        bt[b, j] = bad_id
+        clamped[b, j] = P - 1
+    bad = dataclasses.replace(inp, block_table=bt)
+    out, lse = run_hip(bad, num_splits=2)
+    o_ref, l_ref = run_oracle(dataclasses.replace(inp, block_table=clamped))
+    compare(out, lse, o_ref, l_ref, dtype=dtype, what=f"clamped page ids {dtype}")
+    o_ok, l_ok = run_oracle(inp)
+    compare(out[2:3], lse[2:3], o_ok[2:3], l_ok[2:3], dtype=dtype, what="valid-table request untouched")

@@ -65,7 +65,9 @@ typedef enum {
     MLA_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or shape */
     MLA_ERR_UNSUPPORTED = -2,  /* valid but not supported combination */
     MLA_ERR_WORKSPACE = -3,    /* workspace missing or too small */
-    MLA_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed */
+    MLA_ERR_HIP = -4,          /* a HIP runtime call or kernel launch failed */
+    MLA_ERR_SCRATCH_LIMIT = -5 /* mla_decode_partial_noalloc: the descriptor needs more
+                                  workspace than the static scratch holds */
 } mla_status;
 
 /* Fixed model dimensions of the latent cache (page 4: 512 + 64 = 576). */
@@ -132,6 +134,37 @@ int mla_decode_partial(const mla_decode_desc* desc, const void* q, const void* k
                        const float* kv_scale, const int32_t* block_table,
                        const int32_t* seq_lens, float scale, void* out, float* lse,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the library's static device scratch on each GPU (the workspace of
+ * mla_decode_partial_noalloc). */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* mla_decode_partial for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same decode, with the library's own static device scratch
+ * in place of a caller workspace.  Arguments, results, validation and errors
+ * are those of mla_decode_partial, minus the workspace.
+ *  - The scratch is a file-scope device array of MLA_NOALLOC_SCRATCH_BYTES
+ *    (128 MiB), one per GPU the library runs on, held from library load until
+ *    the process ends.  Its address on the current device is looked up on the
+ *    first call on that device (make that first call outside graph capture).
+ *  - A descriptor whose workspace (mla_decode_workspace_size) exceeds the
+ *    scratch returns MLA_ERR_SCRATCH_LIMIT before any device work.  The
+ *    workspace holds 262,688 bytes per work unit, and the automatic split of
+ *    B requests of T 128-row tiles sizes for ceil((256 / T + B) / 8) * 8 * T
+ *    units: up to 504 units fit (for example B = 128 with 128 heads, or
+ *    B = 32 with 512 heads); 256 fixed splits of a long sequence do not.
+ *  - The call allocates and frees nothing: no hipMalloc or hipFree and no
+ *    allocating library routine.
+ *  - Every call on a GPU shares that GPU's scratch, which keeps the last
+ *    call's contents; nothing in it needs to start at zero (each call writes
+ *    its split plan before reading it).  Calls that overlap in time on one GPU
+ *    (on different streams, or from threads without ordering) race on the
+ *    scratch and give wrong results: order them on one stream. */
+int mla_decode_partial_noalloc(const mla_decode_desc* desc, const void* q, const void* kv_cache,
+                               const float* kv_scale, const int32_t* block_table,
+                               const int32_t* seq_lens, float scale, void* out, float* lse,
+                               void* stream);
 
 /* The split plan of a decode step alone, for reuse by every layer's decode of
  * that step (page 2, the flashmla.py _build_decode excerpt: the scheduler

@@ -8,6 +8,8 @@ and the current stream.  The entry points mirror include/mla_decode.h:
     workspace_size(desc) -> int
     decode_partial(desc, q, kv_cache, kv_scale, block_table, seq_lens, scale,
                    out, lse, workspace, stream=None)
+    decode_partial_noalloc(desc, q, kv_cache, kv_scale, block_table, seq_lens, scale,
+                           out, lse, stream=None)
     merge_states(outs, lses, n, rows, out, lse, out_dtype=F32, stream=None)
     query_prep(q_nope, q_pe, w_uk, q_out, q_scale=None, stream=None)
     up_project(o_lat, w_uv, out, stream=None)
@@ -37,7 +39,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmla_decode.so")
 
 BF16, FP8_E4M3, F32 = 0, 1, 2
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH_LIMIT = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 128 << 20
 LATENT_DIM, ROPE_DIM, QK_DIM, PAGE_SIZE = 512, 64, 576, 64
 
 #: every symbol include/mla_decode.h declares
@@ -47,6 +50,7 @@ EXPORTS = (
     "mla_decode_partial_timed",
     "mla_decode_plan",
     "mla_decode_partial_planned",
+    "mla_decode_partial_noalloc",
     "mla_merge_states",
     "mla_query_prep",
     "mla_up_project",
@@ -121,6 +125,8 @@ def _load():
     lib.mla_decode_plan.restype = ctypes.c_int
     lib.mla_decode_partial_planned.argtypes = dec_args
     lib.mla_decode_partial_planned.restype = ctypes.c_int
+    lib.mla_decode_partial_noalloc.argtypes = [pdesc, vp, vp, vp, vp, vp, f32, vp, vp, vp]
+    lib.mla_decode_partial_noalloc.restype = ctypes.c_int
     lib.mla_merge_states.argtypes = [vp, vp, i32, i32, vp, vp, i32, vp]
     lib.mla_merge_states.restype = ctypes.c_int
     lib.mla_query_prep.argtypes = [ctypes.POINTER(QueryPrepDesc), vp, vp, vp, vp, vp, vp]
@@ -264,6 +270,19 @@ def decode_partial_planned(desc: DecodeDesc, q, kv_cache, kv_scale, block_table,
                                         _stream(stream))
     if st != OK:
         raise MlaError(st, "mla_decode_partial_planned")
+
+
+def decode_partial_noalloc(desc: DecodeDesc, q, kv_cache, kv_scale, block_table, seq_lens, scale: float,
+                           out, lse, stream=None) -> None:
+    """Enqueue mla_decode_partial_noalloc: decode_partial on the library's static
+    device scratch (no workspace argument, no allocation).  Calls on one GPU
+    share that scratch and must not overlap in time."""
+    check_decode_buffers(desc, q, kv_cache, kv_scale, block_table, seq_lens, out, lse)
+    st = lib.mla_decode_partial_noalloc(ctypes.byref(desc), _ptr(q), _ptr(kv_cache), _ptr(kv_scale),
+                                        _ptr(block_table), _ptr(seq_lens), ctypes.c_float(scale), _ptr(out),
+                                        _ptr(lse), _stream(stream))
+    if st != OK:
+        raise MlaError(st, "mla_decode_partial_noalloc")
 
 
 def merge_states(outs, lses, n: int, rows: int, out, lse, out_dtype: int = F32, stream=None) -> None:

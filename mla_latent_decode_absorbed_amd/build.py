@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla_decode.so")
 SOURCES = [os.path.join(CSRC, "mla_kernels.hip"), os.path.join(CSRC, "mla_qprep.hip"),
            os.path.join(CSRC, "mla_upproj.hip"), os.path.join(CSRC, "mla_gather.hip"),
-           os.path.join(CSRC, "mla_api.cpp")]
+           os.path.join(CSRC, "mla_scratch.hip"), os.path.join(CSRC, "mla_api.cpp")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -222,6 +222,20 @@ int mla_decode_partial_timed(const mla_decode_desc* desc, const void* q, const v
                        workspace, workspace_bytes, stream, event_before_decode, event_after_decode);
 }
 
+int mla_decode_partial_noalloc(const mla_decode_desc* desc, const void* q, const void* kv_cache,
+                               const float* kv_scale, const int32_t* block_table, const int32_t* seq_lens,
+                               float scale, void* out, float* lse, void* stream) {
+    static_assert(mla::kNoAllocScratchBytes == MLA_NOALLOC_SCRATCH_BYTES, "scratch size");
+    WorkspaceLayout L;
+    const int st = check_layout(desc, &L);
+    if (st != MLA_OK) return st;
+    if (L.total > mla::kNoAllocScratchBytes) return MLA_ERR_SCRATCH_LIMIT;
+    void* ws = nullptr;
+    if (mla::scratch_for_current_device(&ws) != hipSuccess) return MLA_ERR_HIP;
+    return decode_impl(desc, q, kv_cache, kv_scale, block_table, seq_lens, scale, out, lse, ws,
+                       mla::kNoAllocScratchBytes, stream, nullptr, nullptr);
+}
+
 int mla_decode_plan(const mla_decode_desc* desc, const int32_t* seq_lens, void* workspace,
                     size_t workspace_bytes, void* stream) {
     return plan_impl(desc, seq_lens, workspace, workspace_bytes, stream);
@@ -400,6 +414,9 @@ const char* mla_status_string(int status) {
         case MLA_ERR_UNSUPPORTED: return "unsupported combination (page size, q_len, dtype or size limit)";
         case MLA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case MLA_ERR_HIP: return "HIP runtime error or kernel launch failure";
+        case MLA_ERR_SCRATCH_LIMIT:
+            return "the descriptor needs more workspace than the static scratch (MLA_NOALLOC_SCRATCH_BYTES) "
+                   "holds; use mla_decode_partial with a caller workspace";
         default: return "unknown status";
     }
 }

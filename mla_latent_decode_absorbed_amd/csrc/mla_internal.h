@@ -102,6 +102,14 @@ inline int64_t units_bound(int batch, int m_tiles, int max_pages, int num_splits
     return ((k + 7) / 8) * 8 * m_tiles;
 }
 
+// Bytes of the static device scratch behind mla_decode_partial_noalloc
+// (MLA_NOALLOC_SCRATCH_BYTES of the public header).
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+
+// This device's copy of the static scratch (looked up once per device with
+// hipGetSymbolAddress, then reused); nullptr and the HIP error on failure.
+hipError_t scratch_for_current_device(void** ptr);
+
 hipError_t launch_plan(const PlanParams& p, const int32_t* seq_lens, int32_t* req_info,
                        WorkItem* work, hipStream_t stream);
 hipError_t launch_decode_bf16(const DecodeParams& p, int units, hipStream_t stream,

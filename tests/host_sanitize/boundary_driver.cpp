@@ -181,6 +181,40 @@ void decode_cases() {
     }
 }
 
+// the allocation-free decode: good descriptors run on the static scratch,
+// one that needs more returns MLA_ERR_SCRATCH_LIMIT before any launch
+void noalloc_cases() {
+    const mla_decode_desc fits[] = {desc(64, 1, 128, 4096, 64), desc(128, 1, 128, 17714, 256, MLA_FP8_E4M3),
+                                    desc(32, 1, 512, 4096, 128), desc(4, 2, 128, 8192, 2048, MLA_BF16, MLA_F32, 1),
+                                    desc(240, 1, 128, 600, 2)};
+    for (const auto& g : fits) {
+        DecodeArgs a(g);
+        CHECK(a.ws_bytes <= MLA_NOALLOC_SCRATCH_BYTES);
+        const int b = harness_launches();
+        expect_call(mla_decode_partial_noalloc(&a.d, a.q->p, a.kv->p, a.scale_ptr(), (const int32_t*)a.bt->p,
+                                               (const int32_t*)a.sl->p, 0.1f, a.out->p, (float*)a.lse->p, nullptr),
+                    MLA_OK, b, g.batch > 256 ? 3 : 2);
+    }
+    const mla_decode_desc too_big[] = {desc(4, 2, 128, 8192, 2048, MLA_BF16, MLA_F32, 1, 256),
+                                       desc(512, 1, 128, 4096, 8), desc(300, 1, 128, 600, 2)};
+    for (const auto& g : too_big) {
+        DecodeArgs a(g);
+        CHECK(a.ws_bytes > MLA_NOALLOC_SCRATCH_BYTES);
+        const int b = harness_launches();
+        expect_call(mla_decode_partial_noalloc(&a.d, a.q->p, a.kv->p, a.scale_ptr(), (const int32_t*)a.bt->p,
+                                               (const int32_t*)a.sl->p, 0.1f, a.out->p, (float*)a.lse->p, nullptr),
+                    MLA_ERR_SCRATCH_LIMIT, b, 0);
+    }
+    DecodeArgs a(desc(2, 1, 16, 6, 2));
+    const int b = harness_launches();
+    expect_call(mla_decode_partial_noalloc(&a.d, nullptr, a.kv->p, nullptr, (const int32_t*)a.bt->p,
+                                           (const int32_t*)a.sl->p, 0.1f, a.out->p, (float*)a.lse->p, nullptr),
+                MLA_ERR_INVALID_ARG, b, 0);
+    expect_call(mla_decode_partial_noalloc(nullptr, a.q->p, a.kv->p, nullptr, (const int32_t*)a.bt->p,
+                                           (const int32_t*)a.sl->p, 0.1f, a.out->p, (float*)a.lse->p, nullptr),
+                MLA_ERR_INVALID_ARG, b, 0);
+}
+
 void descriptor_cases() {
     size_t n = 0;
     struct Bad {
@@ -369,7 +403,7 @@ void side_kernel_cases() {
         CHECK(harness_launches() == b);
     }
     harness_clear();
-    for (int s : {0, -1, -2, -3, -4, -5, 1, 12345}) CHECK(mla_status_string(s) != nullptr);
+    for (int s : {0, -1, -2, -3, -4, -5, -6, 1, 12345}) CHECK(mla_status_string(s) != nullptr);
 }
 
 }  // namespace
@@ -391,6 +425,7 @@ int planted_short_workspace() {
 int main(int argc, char** argv) {
     if (argc > 1 && strcmp(argv[1], "--plant-short-workspace") == 0) return planted_short_workspace();
     decode_cases();
+    noalloc_cases();
     descriptor_cases();
     merge_cases();
     side_kernel_cases();

@@ -68,6 +68,15 @@ extern "C" hipError_t hipDeviceGetAttribute(int* value, hipDeviceAttribute_t att
 
 namespace mla {
 
+// the static scratch: a registered host buffer of the same size
+hipError_t scratch_for_current_device(void** ptr) {
+    static uint8_t* buf = nullptr;
+    if (!buf) buf = (uint8_t*)aligned_alloc(256, kNoAllocScratchBytes);
+    harness_register("static scratch", buf, kNoAllocScratchBytes);
+    *ptr = buf;
+    return hipSuccess;
+}
+
 static void check_decode(const char* k, const DecodeParams& p, int units) {
     expect(k, units > 0 && units == p.plan.units_max, "grid size differs from the planner's slot count");
     expect(k, p.plan.m_tiles == (p.rows + kMTile - 1) / kMTile, "row tiles");

@@ -9,6 +9,8 @@
 
 #include <atomic>
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
 
 namespace {
 
@@ -26,6 +28,16 @@ int target_units_for_current_device() {
         cached[dev].store(cus, std::memory_order_relaxed);
     }
     return cus < mla::kTargetUnits ? cus : mla::kTargetUnits;
+}
+
+// The bf16 decode kernel: two waves per SIMD unless MLA_BF16_DECODE_KERNEL=w4
+// selects the one-wave-per-SIMD kernel (same results; kept for measurement).
+int bf16_four_waves() {
+    static const int v = [] {
+        const char* e = getenv("MLA_BF16_DECODE_KERNEL");
+        return e && strcmp(e, "w4") == 0 ? 1 : 0;
+    }();
+    return v;
 }
 
 constexpr size_t kAlign = 256;
@@ -172,6 +184,7 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     dp.max_pages = d->max_pages_per_seq;
     dp.num_pages = d->num_pages;
     dp.out_bf16 = d->out_dtype == MLA_BF16;
+    dp.bf16_four_waves = bf16_four_waves();
     const hipError_t de = d->kv_dtype == MLA_FP8_E4M3
                               ? mla::launch_decode_fp8(dp, (int)L.units_max, s, (hipEvent_t)ev0, (hipEvent_t)ev1)
                               : mla::launch_decode_bf16(dp, (int)L.units_max, s, (hipEvent_t)ev0, (hipEvent_t)ev1);

@@ -326,7 +326,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
 // own item, which it also stores to the work list; workgroup 0 stores the
 // per-request (splits, first kv-unit) the combine reads.  The item is the
 // same value in every lane; readfirstlane makes that visible to the compiler.
+template <int NT = 256>
 __device__ __forceinline__ WorkItem decode_work_item(const DecodeParams& p, uint8_t* lds) {
+    static_assert(NT % 64 == 0 && NT <= 1024, "whole waves, at most 16");
     if (!p.fused_plan) {
         // A stored work list may come from an earlier planner run: an item
         // that does not fit this call's descriptor (a list planned for
@@ -339,12 +341,14 @@ __device__ __forceinline__ WorkItem decode_work_item(const DecodeParams& p, uint
         return w;
     }
     lds_u8* l8 = (lds_u8*)lds;
+    // scratch after the page counts and first kv-units: per-wave sums [3][16],
+    // candidate counts [2][16], wave totals [16], the probed slot's owner [2]
     constexpr int kOff = 8 * kFusedPlanMax;
     const PlanScratch L{(lds_int*)l8, (lds_int*)(l8 + 4 * kFusedPlanMax), (lds_int*)(l8 + kOff),
-                        (lds_uint*)(l8 + kOff + 64), (lds_int*)(l8 + kOff + 192), (lds_int*)(l8 + kOff + 224),
+                        (lds_uint*)(l8 + kOff + 192), (lds_int*)(l8 + kOff + 320), (lds_int*)(l8 + kOff + 384),
                         kFusedPlanMax};
     const int u = blockIdx.x;
-    const PlanResult r = plan_splits<256>(p.plan, p.seq_lens, L, u == 0 ? p.req_info : nullptr, u);
+    const PlanResult r = plan_splits<NT>(p.plan, p.seq_lens, L, u == 0 ? p.req_info : nullptr, u);
     // this slot's item (the layout of plan_item), its request and split
     // written by the thread that owns the request
     const PlanParams& q = p.plan;
@@ -993,6 +997,518 @@ void decode_bf16_kernel(DecodeParams p) {
         if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
         else p.ws_lse[(size_t)blockIdx.x * kMTile + (row - w.mt * kMTile)] = lse;
     }
+}
+
+// ---------------------------------------------------------------------------
+// split-KV decode, bf16 cache, two waves per SIMD with split roles
+//
+// Workgroup = 8 waves over kMTile = 128 query rows (the work items of the
+// one-wave-per-SIMD kernel).  One wave per SIMD can only read about 24 bytes
+// of LDS per clock, while QK^T with Q resident in registers consumes a 1 KB
+// K fragment per 32-clock MFMA; a second wave on each SIMD supplies MFMAs of
+// its own while the first waits on LDS.  The register file decides the
+// split: the 128 rows' O accumulators (256 KB) and query (147 KB) fill 79 % of
+// the CU's 512 KB, so the two waves of a SIMD take different roles:
+//  - wave A of SIMD s owns query rows 32 s .. 32 s + 31: their whole Q^T in
+//    registers (144 VGPRs), QK^T over all 576 dims, the online softmax (exact
+//    row max, reference max in whole log2 units), and publishes P^T of the
+//    tile; it also accumulates O^T for dim tile 4 s (32 dims) of all four row
+//    tiles (64 AGPRs);
+//  - wave B of SIMD s accumulates O^T for dim tiles 4 s + 1 .. 4 s + 3 of all
+//    four row tiles, and issues every page copy.  The split between VGPRs and
+//    AGPRs is one per kernel and would be even, so no accumulator lives in an
+//    AGPR: the MFMAs accumulate in VGPRs, and each wave has 256 of them.
+// Each V^T fragment read from LDS feeds four MFMAs (one per row tile).  Per
+// 32-token step a SIMD runs 36 + 8 MFMAs on wave A and 24 on wave B.
+// Roles follow the hardware SIMD of each wave (HW_ID), read once: the lower
+// wave index of a SIMD is A; if the SIMD ids do not come out two per SIMD,
+// waves 0-3 are A and 4-7 B (same results, only the overlap differs).
+//
+// LDS: a 4-slot ring of half pages (147,456 bytes) and a double-buffered P^T
+// exchange (2 x 8 KB): the whole 160 KB.  The reference max moves in whole
+// log2 units, so every rescale factor is an exact power of two 2^-d; the
+// k-step 0 fragment of a tile carries d in the sign bits of its weights
+// (which are non-negative): element 0 flags a move, elements 1 .. 7 hold d.
+//
+// One step k, one barrier T(k): the copies of half page k + 1 have landed,
+// P(k) is published, and every wave is past its PV of half page k - 1 (so B
+// refills that slot with half page k + 3).  Then A: PV of k, QK^T and softmax
+// of k + 1 (P(k + 1) into the other buffer); B: copies, PV of k.
+// ---------------------------------------------------------------------------
+constexpr int kAbPBufOff = kRingBytes;                 // [2 buffers][4 tiles][2 k-steps][64 lanes] 16 B
+constexpr int kAbLdsBytes = kAbPBufOff + 2 * 8192;     // 163,840 (the whole LDS)
+static_assert(kAbLdsBytes <= 163840, "LDS budget");
+constexpr float kRescaleSlackAb = 8.f;                 // reference max moves when the max grows by > 2^8
+
+// SIMD of the calling wave (HW_ID bits 5:4)
+__device__ __forceinline__ int hw_simd_id() {
+    return (int)(__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3u);
+}
+
+template <bool A>
+__device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const WorkItem& w, uint8_t* lds,
+                                                    const int s) {
+    const int lane = threadIdx.x & 63;
+    const int G = lane >> 5;        // MFMA k-group of this lane
+    const int lr = lane & 31;       // query row (QK^T B operand, PV result) / token (QK^T A operand)
+    const int b = w.b;
+    const int n = min(max(p.seq_lens[b], 0), p.max_pages * kPage);
+    const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
+    const uint8_t* kvbase = (const uint8_t*)p.kv;
+    lds_u8* const ring = (lds_u8*)lds;
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+    lds_u8* const pbase = (lds_u8*)lds + kAbPBufOff + lane * 16;   // + 8192 buf + 2048 tile + 1024 k-step
+
+    const int half_begin = 2 * w.page_begin;
+    const int half_end = min(2 * w.page_end, (n + kHalfTok - 1) / kHalfTok);
+    auto slot_of = [&](int k) { return (k - half_begin) & 3; };
+    auto slot_ptr = [&](int k) { return ring + slot_of(k) * kSlotBytes; };
+    auto pfrag_ptr = [&](int k, int t, int k2) { return pbase + ((k - half_begin) & 1) * 8192 + t * 2048 + k2 * 1024; };
+
+    // ---- page copies (B waves): a half page is 36 blocks of 1 KB (block j
+    // holds LDS chunks 64 j .. 64 j + 63 = (token q / 72, position q % 72),
+    // i.e. global chunk position ^ swz(token)); B wave of SIMD s copies the
+    // blocks 9 s .. 9 s + 8.  Past the last half page a copy re-reads the
+    // last one (a valid page whose data is never used), so that every step
+    // issues the same copies.
+    int cp_off[A ? 1 : 9];
+    if (!A) {
+#pragma unroll
+        for (int j = 0; j < 9; ++j) {
+            const int q = (9 * s + j) * 64 + lane;
+            const int t = q / kRowChunks;
+            const int pc = q - t * kRowChunks;
+            cp_off[j] = t * kRowBytes + ((pc ^ swz(t)) << 4);
+        }
+    }
+    const __attribute__((address_space(4))) int32_t* bt_s = (const __attribute__((address_space(4))) int32_t*)bt;
+    auto page_id = [&](int k) { return clamp_page(bt_s[k >> 1], p.num_pages); };
+    auto copy_src = [&](int k) { return k < half_end ? k : half_end - 1; };
+    auto half_src_of = [&](int pid, int k) { return kvbase + (size_t)pid * kPageBytes + (k & 1) * kSlotBytes; };
+    auto copy_half = [&](int k, int pid) {
+        if (!A) {
+            const uint8_t* src = half_src_of(pid, copy_src(k));
+            const uint32_t dst = ring_addr + slot_of(k) * kSlotBytes + 9 * s * 1024;
+#pragma unroll
+            for (int j = 0; j < 9; ++j) dma16(dst + j * 1024, src, (uint32_t)cp_off[j]);
+        }
+    };
+
+    // ---- this lane's query row (A) and the visible lengths
+    const int row = w.mt * kMTile + s * 32 + lr;
+    const bool row_ok = row < p.rows;
+    const int tq = row / p.heads;
+    const int unit_end = half_end * kHalfTok;
+    const int nvis = min(p.causal ? max(n - (p.q_len - 1 - tq), 0) : n, unit_end);
+    const int nvis_min = min(p.causal ? max(n - (p.q_len - 1), 0) : n, unit_end);
+
+    // ---- query: the 128-row tile through the still empty ring (rows
+    // swizzled like cache rows, 144 blocks of 1 KB, 18 per wave), then each A
+    // wave reads its rows' Q^T fragments: k-step ks covers dims 16 ks .. + 15,
+    // lane (lr, G) holds dims + 8 G .. + 7 of row lr (chunk 2 ks + G)
+    bf16x8_t qf[A ? 36 : 1];
+    {
+        const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const uint8_t* qreq = (const uint8_t*)p.q + (size_t)b * p.rows * kRowBytes;
+#pragma unroll
+        for (int j = 0; j < 18; ++j) {
+            const int qb = 18 * wv + j;
+            const int q = qb * 64 + lane;
+            const int r = q / kRowChunks;
+            const int pc = q - r * kRowChunks;
+            const uint32_t src = (uint32_t)min(w.mt * kMTile + r, p.rows - 1) * kRowBytes + ((pc ^ swz(r)) << 4);
+            dma16(ring_addr + qb * 1024, qreq, src);
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();
+        if (A) {
+            const lds_u8* qrow = ring + (s * 32 + lr) * kRowBytes;
+            int qb4[4];
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) qb4[k4] = (((2 * k4 + G) ^ swz(lr)) & 7) << 4;
+#pragma unroll
+            for (int ks = 0; ks < 36; ++ks) qf[ks] = *(const lds_bf16x8*)(qrow + qb4[ks & 3] + (ks >> 2) * 128);
+        }
+    }
+    __syncthreads();   // the A waves hold their query fragments: the ring is free
+
+    // K fragment offsets within a slot (A): token lr, chunk 2 ks + G at position
+    // (c & ~7) | ((c ^ swz(lr)) & 7); c(ks + 4) = c(ks) + 8, so four bases
+    // cover the 36 k-steps with immediates 128 (ks / 4)
+    int qk_off[A ? 4 : 1];
+    if (A) {
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) qk_off[k4] = lr * kRowBytes + ((((2 * k4 + G) ^ swz(lr)) & 7) << 4);
+    }
+    // V^T transpose reads of dim tile dt = 4 s + j (chunk 4 dt + 2 (bk % 2) +
+    // (lane % 4) / 2 of tokens 4 G + e and + 8): 16 s and 8 (j / 2) lie above
+    // the 3 swizzled chunk bits, 4 (j % 2) inside them
+    int tr_off[2];
+    {
+        const int li = lane & 15, e = li >> 2, cc = li & 3, dhl = (lane >> 4) & 1;
+        const int t = 4 * G + e;
+        const int sw = swz(t);
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+            tr_off[d2] = t * kRowBytes + s * 256 + (((4 * d2 + 2 * dhl + (cc >> 1)) ^ sw) << 4) + (cc & 1) * 8;
+    }
+    auto vfrag = [&](lds_u8* cur, int j, int k2) -> bf16x8_t {
+        const int off = tr_off[j & 1] + (j >> 1) * 128 + k2 * 16 * kRowBytes;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + ((off ^ 32) + 8 * kRowBytes)));
+        return __builtin_bit_cast(bf16x8_t, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
+
+    // O^T accumulators for the rows of tile t over dim tile 4 s + J0 + j (A:
+    // j = 0; B: j = 0 .. 2): oa[t] (j = 0) and ov[j - 1][t], all in VGPRs;
+    // element i is dim + 8 (i / 4) + 4 G + i % 4
+    constexpr int NJ = A ? 1 : 3;
+    constexpr int J0 = A ? 0 : 1;
+    f32x16 oa[4], ov[A ? 1 : 2][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        oa[t] = (f32x16)0.f;
+        asm volatile("" : "+v"(oa[t]));
+    }
+    if (!A) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                ov[j][t] = (f32x16)0.f;
+                asm volatile("" : "+v"(ov[j][t]));
+            }
+    }
+    // O^T[j][t] += V^T . P^T (inline assembly with the accumulator tied to its
+    // registers, so the compiler never moves it)
+    auto mfma_o = [&](int j, int t, const bf16x8_t& a, const bf16x8_t& bp) {
+        if (j == 0) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(oa[t]) : "v"(a), "v"(bp));
+        else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(ov[j - 1][t]) : "v"(a), "v"(bp));
+    };
+    auto o_elem = [&](int j, int t, int i) -> float { return j == 0 ? oa[t][i] : ov[j - 1][t][i]; };
+    // (A) reference max (whole log2 units) and this lane's shares of the row
+    // sum: l of the weights as computed (for the LSE) and lr of the weights as
+    // rounded to bf16, the values the PV multiplies (for normalising O, so that
+    // the output is a weighted mean of V whatever the rounding)
+    float m = -INFINITY, l = 0.f, lr_sum = 0.f;
+    auto pv_drain = [&]() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); };
+    // o *= a for the accumulators of row tile t, in place
+    auto scale_tile = [&](int t, float a) {
+        oa[t] *= a;
+        if (!A) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) ov[j][t] *= a;
+        }
+    };
+
+    // O^T += V^T . P^T over half page k for this wave's dim tiles and the four
+    // row tiles.  The flag bits of the four k-step 0 fragments are read first;
+    // every wave reads the same bits, so when a row of some tile moved its
+    // reference max (rare) the whole workgroup takes the slow path together:
+    // each wave rescales its accumulators of the tile by 2^-d, and after a
+    // barrier the tile's A wave clears the sign bits in LDS (a second barrier
+    // publishes them) before the usual PV.
+    auto pv = [&](int k) {
+        lds_u8* cur = slot_ptr(k);
+        int flag = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) flag |= *(const __attribute__((address_space(3))) int*)pfrag_ptr(k, t, 0);
+        if (__builtin_expect(__any((flag & 0x8000) != 0), 0)) {
+            pv_drain();
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const i32x4 v = *(const __attribute__((address_space(3))) i32x4*)pfrag_ptr(k, t, 0);
+                int d = ((unsigned)v[0]) >> 31;
+#pragma unroll
+                for (int q = 1; q < 4; ++q)
+                    d |= (((v[q] >> 15) & 1) << (2 * q - 1)) | ((((unsigned)v[q]) >> 31) << (2 * q));
+                if (!((v[0] >> 15) & 1)) d = 0;
+                if (__any(d != 0)) scale_tile(t, __builtin_ldexpf(1.f, -d));
+            }
+            __syncthreads();
+            if (A) {
+                __attribute__((address_space(3))) i32x4* f = (__attribute__((address_space(3))) i32x4*)pfrag_ptr(k, s, 0);
+                i32x4 v = *f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v[q] &= 0x7fff7fff;
+                *f = v;
+            }
+            __syncthreads();
+        }
+        if (A) {
+            // one dim tile: each V fragment feeds four MFMAs, P read one tile ahead
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const bf16x8_t a = vfrag(cur, 0, k2);
+                bf16x8_t pc = *(const lds_bf16x8*)pfrag_ptr(k, 0, k2);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    bf16x8_t pn;
+                    if (t < 3) pn = *(const lds_bf16x8*)pfrag_ptr(k, t + 1, k2);
+                    mfma_o(0, t, a, pc);
+                    pc = pn;
+                }
+            }
+        } else {
+            // three dim tiles: the four P fragments of a k-step stay in
+            // registers, each V fragment (read one ahead) feeds four MFMAs
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2) {
+                bf16x8_t pt[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) pt[t] = *(const lds_bf16x8*)pfrag_ptr(k, t, k2);
+                bf16x8_t vc = vfrag(cur, J0, k2);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    bf16x8_t vn;
+                    if (j + 1 < NJ) vn = vfrag(cur, J0 + j + 1, k2);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) mfma_o(j, t, vc, pt[t]);
+                    vc = vn;
+                }
+            }
+        }
+    };
+
+    // (A) S^T of half page k for the wave's 32 rows: all 36 k-steps in one
+    // accumulation chain, K fragments read two ahead (inline-assembly MFMAs
+    // with S tied to VGPRs; wait states before S is read are inserted at the end)
+    auto qk = [&](int k, f32x16& sacc) {
+        lds_u8* cur = slot_ptr(k);
+        constexpr int kKAhead = 2;
+        bf16x8_t kf[kKAhead];
+#pragma unroll
+        for (int ks = 0; ks < kKAhead; ++ks) kf[ks] = *(const lds_bf16x8*)(cur + qk_off[ks & 3] + (ks >> 2) * 128);
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) {
+            const bf16x8_t a = kf[ks % kKAhead];
+            if (ks + kKAhead < 36)
+                kf[ks % kKAhead] = *(const lds_bf16x8*)(cur + qk_off[(ks + kKAhead) & 3] + ((ks + kKAhead) >> 2) * 128);
+            if (ks == 0)
+                asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sacc) : "v"(a), "v"(qf[ks]));
+            else
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(a), "v"(qf[ks]));
+        }
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sacc));
+    };
+    // (A) online softmax of half page k: masks invisible tokens (element i is
+    // token 32 k + 8 (i / 4) + 4 G + i % 4), moves the reference max (whole
+    // log2 units) when the row max exceeds it by more than kRescaleSlackAb,
+    // and publishes both k-step fragments of P^T; the k-step 0 fragment
+    // carries the shift d when some row of the tile moved
+    const float c_log2 = p.scale_log2;
+    auto softmax = [&](int k, f32x16& sacc) {
+        if (k * kHalfTok + kHalfTok > nvis_min) {
+            const int lim = nvis - k * kHalfTok - 4 * G;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[i] = (8 * (i >> 2) + (i & 3)) < lim ? sacc[i] : -INFINITY;
+        }
+        float mx = sacc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+        mx = pair_max(mx) * c_log2;
+        const bool grow = mx > m + kRescaleSlackAb;
+        const float m_new = grow ? __builtin_ceilf(mx) : m;
+        // (nothing has been accumulated while m is still -inf: no rescale)
+        const int d = grow && m != -INFINITY ? (int)fminf(m_new - m, 127.f) : 0;
+        m = m_new;
+        l *= __builtin_ldexpf(1.f, -d);
+        lr_sum *= __builtin_ldexpf(1.f, -d);
+        const float mneg = m == -INFINITY ? 0.f : -m;
+        float sum0 = 0.f, sum1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            sacc[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], c_log2, mneg));
+            if (i & 1) sum1 += sacc[i]; else sum0 += sacc[i];
+        }
+        l += sum0 + sum1;
+        bf16x8_t pf0, pf1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pf0[e] = (__bf16)sacc[e];
+            pf1[e] = (__bf16)sacc[8 + e];
+        }
+        i32x4 v = __builtin_bit_cast(i32x4, pf0);
+        {
+            const i32x4 v1 = __builtin_bit_cast(i32x4, pf1);
+            float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                r0 += __int_as_float(v[q] << 16) + __int_as_float(v[q] & (int)0xffff0000u);
+                r1 += __int_as_float(v1[q] << 16) + __int_as_float(v1[q] & (int)0xffff0000u);
+            }
+            lr_sum += r0 + r1;
+        }
+        if (__builtin_expect(__any(d != 0), 0)) {
+            const int f = d != 0 ? 1 : 0;
+            v[0] |= (f << 15) | ((d & 1) << 31);
+#pragma unroll
+            for (int q = 1; q < 4; ++q) v[q] |= (((d >> (2 * q - 1)) & 1) << 15) | (((d >> (2 * q)) & 1) << 31);
+        }
+        *(__attribute__((address_space(3))) i32x4*)pfrag_ptr(k, s, 0) = v;
+        *(lds_bf16x8*)pfrag_ptr(k, s, 1) = pf1;
+    };
+    // (B) zero the rows of half page k past the sequence end (they may hold
+    // anything, NaN included), so that a zero weight times V stays zero; runs
+    // after the copies of k have landed, and the next barrier orders it before
+    // any PV of k (a concurrent QK^T of k only reads masked tokens there)
+    auto zero_tail = [&](int k) {
+        const int t0 = n - k * kHalfTok;
+        if (t0 >= kHalfTok) return;
+        lds_u8* cur = slot_ptr(k);
+        const int tid = s * 64 + lane;
+        for (int idx = tid; idx < (kHalfTok - t0) * kRowChunks; idx += 256) {
+            const int t = t0 + idx / kRowChunks;
+            const int c = idx % kRowChunks;
+            *(__attribute__((address_space(3))) i32x4*)(cur + t * kRowBytes + c * 16) = (i32x4)0;
+        }
+    };
+
+    if (half_begin < half_end) {
+        // prologue: B copies the first three half pages; T(pre): the first has
+        // landed; A contracts it and publishes P of the first half page
+        int pid_next = 0;
+        if (!A) {
+            const int pid0 = page_id(half_begin);
+            const int pid1 = page_id(copy_src(half_begin + 1));
+            const int pid2 = page_id(copy_src(half_begin + 2));
+            copy_half(half_begin, pid0);
+            copy_half(half_begin + 1, pid1);
+            copy_half(half_begin + 2, pid2);
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));
+            pid_next = page_id(copy_src(half_begin + 3));
+        }
+        lds_sync();
+        // (the first half page's tail is zeroed before the next barrier, and
+        // its PV runs after it)
+        if (!A) zero_tail(half_begin);
+        if (A) {
+            f32x16 sacc;
+            qk(half_begin, sacc);
+            softmax(half_begin, sacc);
+        }
+        for (int k = half_begin;; ++k) {
+            // T(k): the copies of half page k + 1 have landed (B waits for its
+            // own, the barrier makes them everyone's), P(k) is published
+            if (!A) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
+            lds_sync();
+            const bool more = k + 1 < half_end;
+            if (A) {
+                pv(k);
+                if (more) {
+                    f32x16 sacc;
+                    qk(k + 1, sacc);
+                    softmax(k + 1, sacc);
+                }
+            } else {
+                copy_half(k + 3, pid_next);
+                pid_next = page_id(copy_src(k + 4));
+                if (more) zero_tail(k + 1);
+                pv(k);
+            }
+            if (!more) break;
+        }
+    }
+
+    // ---- epilogue: o = O / l for this wave's dim tiles of the four row
+    //      tiles; lse = ln(sum exp) for the A wave's rows.
+    // No copy may still be writing this workgroup's LDS when it is reused.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    pv_drain();
+    const float l_row = pair_sum(l);
+    const float lr_row = pair_sum(lr_sum);
+    __syncthreads();                      // every wave is done with the ring and the P buffers
+    lds_f32* const lbuf = (lds_f32*)(lds + kAbPBufOff);   // [4 tiles][32 rows]: sums of the rounded weights
+    if (A && G == 0) lbuf[s * 32 + lr] = lr_row;
+    __syncthreads();
+    float lt[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) lt[t] = lbuf[t * 32 + lr];
+    if (w.nsplit > 1 || !p.out_bf16) {
+        // fp32 rows leave through the idle ring: per half (64 rows) every wave
+        // writes its dims of the rows (scaled by 1 / l) into rows of 2064
+        // bytes, then the workgroup stores whole contiguous row pieces
+        constexpr int kStRow = 4 * kV + 16;
+        float* gbase = w.nsplit > 1 ? p.ws_o + (size_t)blockIdx.x * kMTile * kV
+                                    : (float*)p.out + ((size_t)b * p.rows + (size_t)w.mt * kMTile) * kV;
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int t = 2 * hf + tt;
+                const float inv = lt[t] > 0.f ? 1.f / lt[t] : 0.f;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    lds_u8* srow = ring + (32 * tt + lr) * kStRow + 4 * (32 * (4 * s + J0 + j) + 4 * G);
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        *(__attribute__((address_space(3))) f32x4*)(srow + 4 * 8 * q4) =
+                            (f32x4){o_elem(j, t, 4 * q4), o_elem(j, t, 4 * q4 + 1), o_elem(j, t, 4 * q4 + 2),
+                                    o_elem(j, t, 4 * q4 + 3)} * inv;
+                }
+            }
+            __syncthreads();
+#pragma unroll 4
+            for (int kk = 0; kk < 16; ++kk) {
+                const int i = kk * 512 + (int)threadIdx.x;
+                const int rl = i >> 7, c = i & 127;
+                if (w.mt * kMTile + 64 * hf + rl < p.rows)
+                    *(f32x4*)(gbase + (size_t)(64 * hf + rl) * kV + 4 * c) =
+                        *(const __attribute__((address_space(3))) f32x4*)(ring + rl * kStRow + 16 * c);
+            }
+            __syncthreads();
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int r = w.mt * kMTile + 32 * t + lr;
+            if (r >= p.rows) continue;
+            const float inv = lt[t] > 0.f ? 1.f / lt[t] : 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                __bf16* dst = (__bf16*)p.out + ((size_t)b * p.rows + r) * kV + 32 * (4 * s + J0 + j) + 4 * G;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    __bf16 __attribute__((ext_vector_type(4))) v;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o_elem(j, t, 4 * q4 + i) * inv);
+                    *(__bf16 __attribute__((ext_vector_type(4)))*)(dst + 8 * q4) = v;
+                }
+            }
+        }
+    }
+    if (A && row_ok && G == 0) {
+        const float lse = l_row > 0.f ? (m + __log2f(l_row)) * kLn2 : -INFINITY;
+        if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
+        else p.ws_lse[(size_t)blockIdx.x * kMTile + (row - w.mt * kMTile)] = lse;
+    }
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void decode_bf16_ab_kernel(DecodeParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kAbLdsBytes];
+    const WorkItem w = decode_work_item<512>(p, lds);
+    if (w.b < 0) return;
+    // roles: each wave posts its SIMD; with two waves on every SIMD the lower
+    // wave index of a SIMD is A and the SIMD id names the row tile and dim
+    // tiles; otherwise waves 0-3 are A (tile = wave) and 4-7 B
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sid = __builtin_amdgcn_readfirstlane(hw_simd_id());
+    lds_int* tab = (lds_int*)lds;
+    if ((threadIdx.x & 63) == 0) tab[wv] = sid;
+    __syncthreads();
+    int cnt0 = 0, cnt1 = 0, cnt2 = 0, cnt3 = 0, lower = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int si = __builtin_amdgcn_readfirstlane(tab[i]);
+        cnt0 += si == 0; cnt1 += si == 1; cnt2 += si == 2; cnt3 += si == 3;
+        lower += (si == sid && i < wv) ? 1 : 0;
+    }
+    __syncthreads();   // the table's LDS is reused for the query
+    const bool by_hw = cnt0 == 2 && cnt1 == 2 && cnt2 == 2 && cnt3 == 2;
+    const bool is_a = by_hw ? lower == 0 : wv < 4;
+    const int s = by_hw ? sid : (wv & 3);
+    if (is_a) decode_bf16_ab_body<true>(p, w, lds, s);
+    else decode_bf16_ab_body<false>(p, w, lds, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1648,7 +2164,8 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int units, hipStream_t stre
         if (e != hipSuccess) return e;
     }
     clear_stale_error();
-    hipLaunchKernelGGL(decode_bf16_kernel, dim3(units), dim3(256), 0, stream, p);
+    if (p.bf16_four_waves) hipLaunchKernelGGL(decode_bf16_kernel, dim3(units), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(decode_bf16_ab_kernel, dim3(units), dim3(512), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_after) return hipEventRecord(ev_after, stream);

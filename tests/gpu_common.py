@@ -74,8 +74,19 @@ def run_oracle(inp, requests=None):
                               causal=inp.causal)
 
 
+def bf16_half_ulp(x):
+    """Half a bf16 unit in the last place at |x| (elementwise): the most a
+    round-to-nearest bf16 store of a value of that magnitude can add."""
+    _, e = np.frexp(np.abs(x))          # |x| in [2^(e-1), 2^e): ulp 2^(e-8)
+    return np.where(x != 0, np.ldexp(1.0, e - 9), 0.0)
+
+
 def compare(out, lse, o_ref, l_ref, dtype="bf16", what=""):
-    """Element-by-element max-abs check of out and lse, -inf rows included."""
+    """Element-by-element max-abs check of out and lse, -inf rows included.
+
+    The bars are on the computed output; a bf16 ``out`` (an optional storage
+    format) is also allowed the half ulp its own round-to-nearest store adds at
+    that magnitude (up to 0.0078 at |o| in [2, 4))."""
     o = out.double().cpu().numpy()
     l = lse.double().cpu().numpy()
     tol_o, tol_l = TOL[dtype]
@@ -83,12 +94,15 @@ def compare(out, lse, o_ref, l_ref, dtype="bf16", what=""):
     ninf_ref = np.isneginf(l_ref)
     assert np.array_equal(np.isneginf(l), ninf_ref), f"{what}: empty-row pattern differs"
     assert np.isfinite(o).all(), f"{what}: non-finite output"
-    err_o = float(np.max(np.abs(o - o_ref))) if o.size else 0.0
+    diff = np.abs(o - o_ref)
+    bound = tol_o + (bf16_half_ulp(np.abs(o_ref) + tol_o) if out.dtype == torch.bfloat16 else 0.0)
+    err_o = float(np.max(diff)) if o.size else 0.0
+    excess = float(np.max(diff - bound)) if o.size else -1.0
     fin = ~ninf_ref
     err_l = float(np.max(np.abs(l[fin] - l_ref[fin]))) if fin.any() else 0.0
-    print(f"  {what}: max|dout| = {err_o:.3e} (bar {tol_o}), max|dlse| = {err_l:.3e} (bar {tol_l})",
-          flush=True)
-    assert err_o <= tol_o, f"{what}: out error {err_o} > {tol_o}"
+    print(f"  {what}: max|dout| = {err_o:.3e} (bar {tol_o}{' + bf16 store' if out.dtype == torch.bfloat16 else ''}), "
+          f"max|dlse| = {err_l:.3e} (bar {tol_l})", flush=True)
+    assert excess <= 0.0, f"{what}: out error {err_o} exceeds the bar by {excess}"
     assert err_l <= tol_l, f"{what}: lse error {err_l} > {tol_l}"
     return err_o, err_l
 

@@ -625,8 +625,12 @@ def decode_record(name: str, inp, args, hev, num_splits: int, steps: int, cpu_bu
         hev.destroy(b)
     kern_ms = median(kern)
 
-    # split counts the planner chose (the workspace's first 2 B int32: splits, first kv-unit)
-    info = dec.workspace[: 8 * inp.batch].view(torch.int32).view(inp.batch, 2)[:, 0].cpu()
+    # pieces per request the planner chose (the workspace's first 4 B int32:
+    # pieces, first piece, first page, 0); a request of more than one piece
+    # goes through fp32 partials
+    req_info = dec.workspace[: 16 * inp.batch].view(torch.int32).view(inp.batch, 4).cpu()
+    info = req_info[:, 0]
+    balanced_plan = bool((req_info[:, 2] != 0).any())
     partial_rows = int(sum(int(sp) for sp in info.tolist() if sp > 1) * inp.q_len * inp.heads)
     partial_bytes = partial_rows * (512 * 4 + 4)
 
@@ -652,7 +656,8 @@ def decode_record(name: str, inp, args, hev, num_splits: int, steps: int, cpu_bu
                       "binding_roof": round(max(acc["kv_bytes"] / (HBM_PEAK_GBS * 1e9),
                                                 acc["flops"] / (peak_tf * 1e12)) / (ms_per_step * 1e-3), 4)},
         "roofline": roof,
-        "split_partials": {"splits_per_request_min_max": [int(info.min()), int(info.max())],
+        "split_partials": {"plan": "balanced page ranges" if balanced_plan else "common chunk",
+                           "splits_per_request_min_max": [int(info.min()), int(info.max())],
                            "partial_bytes_written_and_read": 2 * partial_bytes,
                            "overhead_vs_kv_bytes": round(2 * partial_bytes / acc["kv_bytes"], 4)},
         "shape": {"batch": inp.batch, "q_len": inp.q_len, "heads": inp.heads,

@@ -77,7 +77,7 @@ WorkspaceLayout layout_for(const mla_decode_desc* d) {
     L.units_max = mla::units_bound(d->batch, L.m_tiles, d->max_pages_per_seq, d->num_splits);
     size_t off = 0;
     L.req_info = off;
-    off = align_up(off + sizeof(int32_t) * 2 * (size_t)d->batch);
+    off = align_up(off + sizeof(int32_t) * mla::kReqInfoInts * (size_t)d->batch);
     L.work = off;
     off = align_up(off + sizeof(mla::WorkItem) * (size_t)L.units_max);
     L.ws_lse = off;
@@ -110,6 +110,8 @@ mla::PlanParams plan_params(const mla_decode_desc* d, const WorkspaceLayout& L) 
     pp.target_units = target_units_for_current_device();
     pp.min_chunk = mla::kMinChunkPages;
     pp.units_max = (int32_t)L.units_max;
+    // the fp8 kernel runs multi-piece work items (the balanced plan for ragged batches)
+    pp.balance = d->kv_dtype == MLA_FP8_E4M3 ? 1 : 0;
     return pp;
 }
 

@@ -15,14 +15,34 @@ constexpr int kTargetUnits = 256; // automatic split: at most this many workgrou
 constexpr int kMinChunkPages = 2; // smallest automatic split, in pages
 constexpr int kFusedPlanMax = 256; // batches up to this size are planned inside the decode kernel
 
-// One unit of split-KV work: rows [mt*kMTile, +kMTile) of request b over the
-// pages [page_begin, page_end) of its block table.  b < 0 marks an empty slot.
+// The work of one decode workgroup: rows [mt*kMTile, +kMTile) over npages
+// cache pages, starting at page page_begin of request b.  With chunk == 0 the
+// pages all belong to request b (one piece: a split of the request); with
+// chunk > 0 (the balanced plan) they are the global pages [g0, g0 + npages)
+// of all requests' pages laid end to end, kv-unit g0 / chunk, and run on
+// into the following non-empty requests (one piece per request touched).
+// piece is the partial-result index of the first piece (the following ones
+// count on from it) and nsplit the number of pieces request b is cut into
+// (1: the piece writes the request's result itself).  b < 0 marks an empty slot.
 struct WorkItem {
-    int32_t b, mt, split, page_begin, page_end, nsplit, pad0, pad1;
+    int32_t b, mt, piece, page_begin, npages, nsplit, g0, chunk;
 };
+
+// One piece of a workgroup's work: rows [mt*kMTile, +kMTile) of request b
+// over pages [page_begin, page_end); nsplit == 1 writes out/lse directly,
+// otherwise the partial goes to workspace slot `slot` (= piece * m_tiles + mt).
+struct Piece {
+    int32_t b, mt, page_begin, page_end, nsplit, slot;
+};
+
+// Per-request planner output, int32 [batch][kReqInfoInts]: pieces the request
+// is cut into (0 for an empty request under the balanced plan), index of its
+// first piece, and its first global page (balanced plan; 0 otherwise).
+constexpr int kReqInfoInts = 4;
 
 struct PlanParams {
     int32_t batch, rows, m_tiles, max_pages, num_splits, target_units, min_chunk, units_max;
+    int32_t balance;            // 1: the balanced plan may be chosen (the kernel runs multi-piece items)
 };
 
 struct DecodeParams {
@@ -33,13 +53,13 @@ struct DecodeParams {
     const int32_t* seq_lens;    // [B]
     const WorkItem* work;       // [units_max] (read when fused_plan == 0)
     WorkItem* work_out;         // the same list (written when fused_plan == 1, one item per workgroup)
-    int32_t* req_info;          // [B][2] (written by workgroup 0 when fused_plan == 1)
+    int32_t* req_info;          // [B][kReqInfoInts] (written by workgroup 0 when fused_plan == 1)
     PlanParams plan;            // the planner's inputs (fused_plan == 1)
     int32_t fused_plan;         // 1: every workgroup plans the splits itself (batch <= kFusedPlanMax);
                                 // 0: work[] comes from the planner kernel, of this call or an earlier one
     void* out;                  // [B][M][512] of out_dtype
     float* lse;                 // [B][M]
-    float* ws_o;                // [units_max][kMTile][512]
+    float* ws_o;                // [units_max][kMTile][512], slot piece * m_tiles + mt
     float* ws_lse;              // [units_max][kMTile]
     float scale_log2;           // scale * log2(e)
     int32_t rows;               // M = q_len * H
@@ -61,7 +81,7 @@ __host__ __device__ inline int clamp_page(int pid, int num_pages) {
 }
 
 struct CombineParams {
-    const int32_t* req_info;    // [B][2]: splits, first kv-unit index
+    const int32_t* req_info;    // [B][kReqInfoInts]: pieces, first piece, first page
     const float* ws_o;
     const float* ws_lse;
     void* out;
@@ -78,17 +98,8 @@ struct MergeParams {
     int32_t n, rows, out_bf16;
 };
 
-// Unit (workgroup) index of kv-unit k (one request x split) for M-tile mt,
-// with per_xcd = ceil(kv-units / 8): dispatch deals workgroups to the 8 XCDs
-// round-robin, and XCD x runs the contiguous kv-units x per_xcd .. + per_xcd - 1
-// with all their M-tiles, so the splits of one request (same query rows) and
-// the M-tiles of one kv-unit (same pages) share that XCD's L2.
-__host__ __device__ inline int unit_index(int k, int mt, int m_tiles, int per_xcd) {
-    const int x = k / per_xcd;
-    return ((k - x * per_xcd) * m_tiles + mt) * 8 + x;
-}
-
-// Upper bound on kv-units (request x split) for a descriptor.
+// Upper bound on kv-units (request x split, or equal page ranges under the
+// balanced plan), and on pieces (at most one more per request), for a descriptor.
 inline int64_t kv_units_bound(int batch, int m_tiles, int max_pages, int num_splits) {
     if (num_splits > 0) {
         int64_t per = num_splits < max_pages ? num_splits : max_pages;

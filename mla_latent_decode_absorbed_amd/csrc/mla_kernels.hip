@@ -92,23 +92,36 @@ __device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlan
 
 struct PlanScratch {
     lds_int* pages;      // [cached] page counts
-    lds_int* first;      // [cached] first kv-unit of each request
+    lds_int* first;      // [cached] first piece of each request
+    lds_int* gstart;     // [cached] first global page of each request (balanced plan)
     lds_int* part;       // [3][waves] per-wave page sums (16-bit halves) and longest request
     lds_uint* cnt;       // [2][16] kv-units per candidate chunk, two rounds in turn
-    lds_int* scan;       // [waves] kv-unit totals
-    lds_int* owner;      // [2] request and split of the kv-unit `probe` (when probe >= 0)
-    int cached;          // requests whose page count and first kv-unit stay in LDS
+    lds_int* scan;       // [2][waves] wave totals of the two scans
+    lds_int* owner;      // [4] the probed slot's request, its split or first page, first piece, pieces
+    lds_int* hist;       // [256] requests starting inside each kv-unit (balanced plan)
+    int cached;          // requests whose page count, first piece and first page stay in LDS
 };
 
+constexpr int kPieceCostPages = 2;   // a piece's fixed cost (pipeline fill, epilogue), in pages
+
 struct PlanResult {
-    int chunk;           // pages per split (automatic split)
-    int k_total;         // kv-units (request x split) in all
+    int chunk;           // pages per split (common-chunk plan)
+    int k_total;         // kv-units in all
+    int balanced;        // > 0: the balanced plan, with this many pages per kv-unit
+    int total_pages;     // all requests' pages (balanced plan)
 };
 
 // Runs on all NT threads of the block (every barrier inside is reached by all
-// of them); req_info, if not null, receives (splits, first kv-unit) per
-// request.  probe_slot >= 0 names a work slot whose request and split the
-// thread that owns the request writes to L.owner (see plan_item).
+// of them); req_info, if not null, receives the kReqInfoInts values per
+// request.  probe_slot >= 0 names a work slot whose request the thread that
+// owns the request describes in L.owner (see plan_item).
+//
+// Two plans.  Common chunk: request b of P_b pages is cut into splits of c
+// pages (the smallest c that fits every request's splits into one round of
+// workgroups), one kv-unit per split.  Balanced: when that plan's longest
+// kv-unit is more than 1/8 above the average, the pages of all requests are
+// laid end to end and cut into kv-units of C = ceil(sum P / U) pages; a
+// kv-unit then holds one piece of every request it touches.
 template <int NT>
 __device__ __forceinline__ PlanResult plan_splits(const PlanParams& p, const int32_t* __restrict__ seq_lens,
                                                   const PlanScratch& L, int32_t* __restrict__ req_info,
@@ -154,6 +167,7 @@ __device__ __forceinline__ PlanResult plan_splits(const PlanParams& p, const int
     }
 
     int chunk = 1;
+    int balanced = 0;
     if (p.num_splits <= 0) {
         // The smallest chunk (in pages) for which every request's splits, times
         // the row tiles, fit in one round of target_units workgroups: the
@@ -211,104 +225,215 @@ __device__ __forceinline__ PlanResult plan_splits(const PlanParams& p, const int
             lo = first > 0 ? cand(first - 1) + 1 : lo;
             hi = cand(first);
         }
+        // a candidate for the balanced plan: the common chunk fits one round
+        // but leaves the longest kv-unit more than 1/8 above the averaging
+        // bound (global page indices stay below 2^30)
+        const int c_avg = max((int)min(avg, (long long)INT32_MAX), p.min_chunk);
+        if (p.balance && total_pages > 0 && total_pages < (1ull << 30) && chunk > c_avg + max(1, c_avg / 8) &&
+            (long long)count(chunk) <= units_cap)
+            balanced = c_avg;
     }
 
-    // splits per request, and the first kv-unit of each request (exclusive
-    // scan: a wavefront scan, then the wave totals through LDS)
-    int my_k = 0;
-    for (int b = b0; b < b1; ++b) {
-        const int pages = pages_of(b);
+    // first global page of each request (balanced plan): exclusive scan of
+    // the page counts (a wavefront scan, then the wave totals through LDS)
+    int my_g = 0;
+    if (balanced) {
+        int my_pages = 0;
+        for (int b = b0; b < b1; ++b) my_pages += pages_of(b);
+        const int incl = wave_scan_add(my_pages);
+        if (lane == 63) L.scan[wv] = incl;
+        __syncthreads();
+        int wave_base = 0;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) wave_base += i < wv ? L.scan[i] : 0;
+        my_g = wave_base + incl - my_pages;
+        // Each piece costs a pipeline fill and an epilogue besides its pages
+        // (about kPieceCostPages pages' time): the balanced plan is kept only
+        // if its busiest kv-unit, with one extra piece per request starting
+        // inside it, still beats the common chunk by 1/8.
+        const int A = balanced;
+        const int k_bal = (int)((total_pages + A - 1) / A);
+        for (int i = tid; i < k_bal; i += NT) L.hist[i] = 0;
+        __syncthreads();
+        int g = my_g;
+        for (int b = b0; b < b1; ++b) {
+            const int pages = pages_of(b);
+            if (pages > 0 && g % A != 0) atomicAdd((int*)(L.hist + g / A), 1);
+            g += pages;
+        }
+        __syncthreads();
+        int my_max = 0;
+        for (int i = tid; i < k_bal; i += NT) my_max = max(my_max, (int)L.hist[i]);
+        const int w_max = __builtin_amdgcn_readlane(wave_scan_max(my_max), 63);
+        if (lane == 0) L.scan[wv] = w_max;
+        __syncthreads();
+        int max_extra = 0;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) max_extra = max(max_extra, (int)L.scan[i]);
+        if (A + kPieceCostPages * max_extra + max(1, A / 8) >= chunk) balanced = 0;
+        __syncthreads();   // L.scan is reused below
+    }
+    // pieces per request: splits (common chunk); kv-units touched, none for
+    // an empty request (balanced)
+    auto pieces_of = [&](int pages, int g) {
+        if (balanced) return pages > 0 ? (g + pages - 1) / balanced - g / balanced + 1 : 0;
         const int S = p.num_splits > 0 ? min(p.num_splits, pages) : (pages + chunk - 1) / chunk;
-        my_k += max(S, 1);
+        return max(S, 1);
+    };
+    int my_k = 0;
+    {
+        int g = my_g;
+        for (int b = b0; b < b1; ++b) {
+            const int pages = pages_of(b);
+            my_k += pieces_of(pages, g);
+            g += pages;
+        }
     }
     const int incl = wave_scan_add(my_k);
-    if (lane == 63) L.scan[wv] = incl;
+    if (lane == 63) L.scan[kWaves + wv] = incl;
+    if (probe_slot >= 0 && tid == 0) L.owner[0] = -1;   // (set below by the owning thread)
     __syncthreads();
-    int wave_base = 0, k_total = 0;
+    int wave_base = 0, pieces_total = 0;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) {
-        const int t = L.scan[i];
+        const int t = L.scan[kWaves + i];
         wave_base += i < wv ? t : 0;
-        k_total += t;
+        pieces_total += t;
     }
-    // kv-unit of the probed slot (the layout of plan_item)
+    const int k_total = balanced ? (int)((total_pages + balanced - 1) / balanced) : pieces_total;
+    // the probed slot's kv-unit (the layout of plan_item)
     int probe_k = -1;
     if (probe_slot >= 0) {
         const int per_xcd = (k_total + 7) / 8;
         const int kx = (probe_slot >> 3) / p.m_tiles;
         probe_k = kx < per_xcd ? per_xcd * (probe_slot & 7) + kx : -1;
+        if (probe_k >= k_total) probe_k = -1;
     }
     int base = wave_base + incl - my_k;
+    int g = my_g;
     for (int b = b0; b < b1; ++b) {
         const int pages = pages_of(b);
-        const int S = p.num_splits > 0 ? max(1, min(p.num_splits, pages))
-                                       : max(1, (pages + chunk - 1) / chunk);
+        const int S = pieces_of(pages, g);
         if (req_info) {
-            req_info[2 * b] = S;
-            req_info[2 * b + 1] = base;
+            req_info[kReqInfoInts * b] = S;
+            req_info[kReqInfoInts * b + 1] = base;
+            req_info[kReqInfoInts * b + 2] = balanced ? g : 0;
+            req_info[kReqInfoInts * b + 3] = 0;
         }
-        if (b < L.cached) L.first[b] = base;
-        if (probe_k >= base && probe_k < base + S) {
-            L.owner[0] = b;
-            L.owner[1] = probe_k - base;
+        if (b < L.cached) {
+            L.first[b] = base;
+            L.gstart[b] = g;
+        }
+        if (probe_k >= 0) {
+            // the request holding kv-unit probe_k (common chunk), or the one
+            // holding its first page (balanced)
+            const bool mine = balanced ? (pages > 0 && (long long)probe_k * balanced >= g &&
+                                          (long long)probe_k * balanced < g + pages)
+                                       : (probe_k >= base && probe_k < base + S);
+            if (mine) {
+                L.owner[0] = b;
+                L.owner[1] = balanced ? g : probe_k - base;
+                L.owner[2] = base;
+                L.owner[3] = S;
+            }
         }
         base += S;
+        g += pages;
     }
-    __syncthreads();   // first kv-units of every cached request visible to the block
-    return PlanResult{chunk, k_total};
+    __syncthreads();   // first pieces and pages of every cached request visible to the block
+    return PlanResult{chunk, k_total, balanced, balanced ? (int)total_pages : 0};
 }
 
-// Work item of slot u.  Dispatch deals workgroups to the 8 XCDs round-robin,
-// so slot u runs on XCD u % 8 as its (u / 8)-th workgroup there.  Each XCD
-// takes a contiguous run of C = ceil(kv-units / 8) kv-units with all their
-// row tiles: slot u holds kv-unit k = C (u % 8) + (u / 8) / m_tiles and row
-// tile (u / 8) % m_tiles.  The splits of one request (which read the same
+// Slot u's kv-unit and row tile.  Dispatch deals workgroups to the 8 XCDs
+// round-robin, so slot u runs on XCD u % 8 as its (u / 8)-th workgroup there.
+// Each XCD takes a contiguous run of C = ceil(kv-units / 8) kv-units with all
+// their row tiles: slot u holds kv-unit k = C (u % 8) + (u / 8) / m_tiles and
+// row tile (u / 8) % m_tiles.  The splits of one request (which read the same
 // query rows) and the row tiles of one kv-unit (which read the same pages)
-// then share one L2.  The request of kv-unit k is found by binary search over
-// the first kv-units; first_of(b) and pages_of(b) give any request's values.
-template <typename FirstOf, typename PagesOf>
-__device__ __forceinline__ WorkItem plan_item(const PlanParams& p, const PlanResult& r, int u,
-                                              FirstOf&& first_of, PagesOf&& pages_of) {
-    const int per_xcd = (r.k_total + 7) / 8;   // the same value the combine derives from req_info
+// then share one L2.  Returns false for an empty slot.
+__device__ __forceinline__ bool slot_unit(const PlanParams& p, const PlanResult& r, int u, int& k, int& mt) {
+    const int per_xcd = (r.k_total + 7) / 8;
     const int pos = u >> 3;
     const int kx = pos / p.m_tiles;
-    const int k = per_xcd * (u & 7) + kx;
-    const int mt = pos - kx * p.m_tiles;
+    k = per_xcd * (u & 7) + kx;
+    mt = pos - kx * p.m_tiles;
+    return kx < per_xcd && k < r.k_total;
+}
+
+__device__ __forceinline__ WorkItem empty_item() {
     WorkItem w;
-    w.pad0 = 0;
-    w.pad1 = 0;
-    if (kx >= per_xcd || k >= r.k_total) {
-        w.b = -1; w.mt = 0; w.split = 0; w.page_begin = 0; w.page_end = 0; w.nsplit = 0;
-        return w;
+    w.b = -1; w.mt = 0; w.piece = 0; w.page_begin = 0; w.npages = 0; w.nsplit = 0; w.g0 = 0; w.chunk = 0;
+    return w;
+}
+
+// The work item of kv-unit k, row tile mt, whose first request b has `pages`
+// pages, first piece `first`, S pieces and (balanced plan) first global page g
+// (common chunk: `split_or_g` is the split index instead).
+__device__ __forceinline__ WorkItem make_item(const PlanParams& p, const PlanResult& r, int k, int mt, int b,
+                                              int pages, int split_or_g, int first, int S) {
+    WorkItem w;
+    w.b = b;
+    w.mt = mt;
+    w.nsplit = S;
+    if (r.balanced) {
+        const int C = r.balanced;
+        const int g0 = k * C;
+        w.piece = first + (k - split_or_g / C);
+        w.page_begin = g0 - split_or_g;
+        w.npages = min(g0 + C, r.total_pages) - g0;
+        w.g0 = g0;
+        w.chunk = C;
+    } else {
+        const int cb = p.num_splits > 0 ? (pages + S - 1) / S : r.chunk;
+        const int pb = min(pages, split_or_g * cb);
+        w.piece = k;
+        w.page_begin = pb;
+        w.npages = min(pages, (split_or_g + 1) * cb) - pb;
+        w.g0 = 0;
+        w.chunk = 0;
     }
-    int lo = 0, hi = p.batch - 1;     // last request whose first kv-unit is <= k
+    return w;
+}
+
+// Work item of slot u for the planner kernel: the request of kv-unit k by
+// binary search over the first pieces (common chunk) or first pages
+// (balanced: the last request starting at or before the unit's first page
+// is the non-empty one holding it).
+template <typename FirstOf, typename GstartOf, typename PagesOf>
+__device__ __forceinline__ WorkItem plan_item(const PlanParams& p, const PlanResult& r, int u,
+                                              FirstOf&& first_of, GstartOf&& gstart_of, PagesOf&& pages_of) {
+    int k, mt;
+    if (!slot_unit(p, r, u, k, mt)) return empty_item();
+    const long long key = r.balanced ? (long long)k * r.balanced : k;
+    int lo = 0, hi = p.batch - 1;     // last request whose first piece / page is <= key
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (first_of(mid) <= k) lo = mid; else hi = mid - 1;
+        if ((r.balanced ? gstart_of(mid) : first_of(mid)) <= key) lo = mid; else hi = mid - 1;
     }
     const int b = lo;
-    const int s = k - first_of(b);
-    const int S = (b + 1 < p.batch ? first_of(b + 1) : r.k_total) - first_of(b);
-    const int pages = pages_of(b);
-    const int cb = p.num_splits > 0 ? (pages + S - 1) / S : r.chunk;
-    w.b = b; w.mt = mt; w.split = s;
-    w.page_begin = min(pages, s * cb);
-    w.page_end = min(pages, (s + 1) * cb);
-    w.nsplit = S;
-    return w;
+    const int first = first_of(b);
+    if (r.balanced) {
+        const int pg = pages_of(b), g = gstart_of(b);
+        const int S = pg > 0 ? (g + pg - 1) / r.balanced - g / r.balanced + 1 : 0;
+        return make_item(p, r, k, mt, b, pg, g, first, S);
+    }
+    const int S = (b + 1 < p.batch ? first_of(b + 1) : r.k_total) - first;
+    return make_item(p, r, k, mt, b, pages_of(b), k - first, first, S);
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t* __restrict__ seq_lens,
                                                     int32_t* __restrict__ req_info,
                                                     WorkItem* __restrict__ work) {
-    constexpr int kCached = 8192;            // page counts of up to this many requests stay in LDS
+    constexpr int kCached = 8192;            // requests whose values stay in LDS
     __shared__ int s_pages[kCached];
     __shared__ int s_first[kCached];
+    __shared__ int s_gstart[kCached];
     __shared__ int s_part[48];
     __shared__ unsigned int s_cnt[32];
-    __shared__ int s_scan[16];
-    const PlanScratch L{(lds_int*)s_pages, (lds_int*)s_first, (lds_int*)s_part, (lds_uint*)s_cnt,
-                        (lds_int*)s_scan, nullptr, kCached};
+    __shared__ int s_scan[32];
+    __shared__ int s_hist[256];
+    const PlanScratch L{(lds_int*)s_pages, (lds_int*)s_first, (lds_int*)s_gstart, (lds_int*)s_part,
+                        (lds_uint*)s_cnt, (lds_int*)s_scan, nullptr, (lds_int*)s_hist, kCached};
     const PlanResult r = plan_splits<1024>(p, seq_lens, L, req_info);
     const int cap = p.max_pages * kPage;
     auto pages_of = [&](int b) {
@@ -316,16 +441,18 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
         const int n = min(max(seq_lens[b], 0), cap);
         return (n + kPage - 1) / kPage;
     };
-    auto first_of = [&](int b) { return b < kCached ? s_first[b] : req_info[2 * b + 1]; };
-    for (int u = threadIdx.x; u < p.units_max; u += 1024) work[u] = plan_item(p, r, u, first_of, pages_of);
+    auto first_of = [&](int b) { return b < kCached ? s_first[b] : req_info[kReqInfoInts * b + 1]; };
+    auto gstart_of = [&](int b) { return b < kCached ? s_gstart[b] : req_info[kReqInfoInts * b + 2]; };
+    for (int u = threadIdx.x; u < p.units_max; u += 1024)
+        work[u] = plan_item(p, r, u, first_of, gstart_of, pages_of);
 }
 
 // The decode kernels' own copy of the planner for batches of at most
 // kFusedPlanMax requests, in the first bytes of their LDS ring (before any
-// copy into it).  Every workgroup derives the same split list and keeps its
-// own item, which it also stores to the work list; workgroup 0 stores the
-// per-request (splits, first kv-unit) the combine reads.  The item is the
-// same value in every lane; readfirstlane makes that visible to the compiler.
+// copy into it).  Every workgroup derives the same plan and keeps its own
+// item, which it also stores to the work list; workgroup 0 stores the
+// per-request values the combine reads.  The item is the same value in every
+// lane; readfirstlane makes that visible to the compiler.
 template <int NT = 256>
 __device__ __forceinline__ WorkItem decode_work_item(const DecodeParams& p, uint8_t* lds) {
     static_assert(NT % 64 == 0 && NT <= 1024, "whole waves, at most 16");
@@ -334,55 +461,94 @@ __device__ __forceinline__ WorkItem decode_work_item(const DecodeParams& p, uint
         // that does not fit this call's descriptor (a list planned for
         // another one, or never written) is skipped rather than followed.
         WorkItem w = p.work[blockIdx.x];
-        if (w.b >= p.plan.batch || w.mt < 0 || w.mt >= p.plan.m_tiles || w.page_begin < 0 ||
-            w.page_begin > w.page_end || w.page_end > p.max_pages || w.nsplit < 1 || w.split < 0 ||
-            w.split >= w.nsplit)
+        if (w.b >= p.plan.batch || w.mt < 0 || w.mt >= p.plan.m_tiles || w.page_begin < 0 || w.npages < 0 ||
+            w.page_begin > p.max_pages || w.npages > (w.chunk > 0 ? w.chunk : p.max_pages) || w.nsplit < 1 ||
+            w.piece < 0 || w.chunk < 0 || w.g0 < 0)
             w.b = -1;
         return w;
     }
     lds_u8* l8 = (lds_u8*)lds;
-    // scratch after the page counts and first kv-units: per-wave sums [3][16],
-    // candidate counts [2][16], wave totals [16], the probed slot's owner [2]
-    constexpr int kOff = 8 * kFusedPlanMax;
-    const PlanScratch L{(lds_int*)l8, (lds_int*)(l8 + 4 * kFusedPlanMax), (lds_int*)(l8 + kOff),
-                        (lds_uint*)(l8 + kOff + 192), (lds_int*)(l8 + kOff + 320), (lds_int*)(l8 + kOff + 384),
-                        kFusedPlanMax};
+    // scratch after the page counts, first pieces and first pages: per-wave
+    // sums [3][16], candidate counts [2][16], scan totals [2][16], the probed
+    // slot's owner [4], kv-unit histogram [256]
+    constexpr int kOff = 12 * kFusedPlanMax;
+    const PlanScratch L{(lds_int*)l8, (lds_int*)(l8 + 4 * kFusedPlanMax), (lds_int*)(l8 + 8 * kFusedPlanMax),
+                        (lds_int*)(l8 + kOff), (lds_uint*)(l8 + kOff + 192), (lds_int*)(l8 + kOff + 320),
+                        (lds_int*)(l8 + kOff + 448), (lds_int*)(l8 + kOff + 512), kFusedPlanMax};
     const int u = blockIdx.x;
     const PlanResult r = plan_splits<NT>(p.plan, p.seq_lens, L, u == 0 ? p.req_info : nullptr, u);
-    // this slot's item (the layout of plan_item), its request and split
-    // written by the thread that owns the request
-    const PlanParams& q = p.plan;
-    const int per_xcd = (r.k_total + 7) / 8;
-    const int kx = (u >> 3) / q.m_tiles;
-    const int k = per_xcd * (u & 7) + kx;
-    WorkItem w;
-    w.pad0 = 0;
-    w.pad1 = 0;
-    if (kx >= per_xcd || k >= r.k_total) {
-        w.b = -1; w.mt = 0; w.split = 0; w.page_begin = 0; w.page_end = 0; w.nsplit = 0;
-    } else {
+    // this slot's item, its request described by the thread that owns it
+    int k, mt;
+    WorkItem w = empty_item();
+    if (slot_unit(p.plan, r, u, k, mt) && L.owner[0] >= 0) {
         const int b = L.owner[0];
-        const int sp = L.owner[1];
-        const int pages = L.pages[b];
-        const int S = (b + 1 < q.batch ? (int)L.first[b + 1] : r.k_total) - (int)L.first[b];
-        const int cb = q.num_splits > 0 ? (pages + S - 1) / S : r.chunk;
-        w.b = b;
-        w.mt = (u >> 3) - kx * q.m_tiles;
-        w.split = sp;
-        w.page_begin = min(pages, sp * cb);
-        w.page_end = min(pages, (sp + 1) * cb);
-        w.nsplit = S;
+        w = make_item(p.plan, r, k, mt, b, L.pages[b], L.owner[1], L.owner[2], L.owner[3]);
     }
     // the same value in every lane: say so, so that it stays in scalar registers
     w.b = __builtin_amdgcn_readfirstlane(w.b);
     w.mt = __builtin_amdgcn_readfirstlane(w.mt);
-    w.split = __builtin_amdgcn_readfirstlane(w.split);
+    w.piece = __builtin_amdgcn_readfirstlane(w.piece);
     w.page_begin = __builtin_amdgcn_readfirstlane(w.page_begin);
-    w.page_end = __builtin_amdgcn_readfirstlane(w.page_end);
+    w.npages = __builtin_amdgcn_readfirstlane(w.npages);
     w.nsplit = __builtin_amdgcn_readfirstlane(w.nsplit);
+    w.g0 = __builtin_amdgcn_readfirstlane(w.g0);
+    w.chunk = __builtin_amdgcn_readfirstlane(w.chunk);
     if (threadIdx.x == 0) p.work_out[u] = w;
     __syncthreads();   // the LDS ring is filled next
     return w;
+}
+
+// Runs body(piece) for each piece of work item w in turn (a barrier between
+// pieces: every piece reuses the whole LDS).  Pieces after the first start at
+// page 0 of the next non-empty request; the balanced plan's global page
+// arithmetic gives each its piece count.  kMulti = false: the kernel runs
+// single-piece items only (plans for it never use the balanced layout), and
+// its body is not inside a loop (a body in a loop keeps more registers live
+// than the bf16 kernels have to spare).
+template <bool kMulti, typename Body>
+__device__ __forceinline__ void for_each_piece(const DecodeParams& p, const WorkItem& w, Body&& body) {
+    const int cap = p.max_pages * kPage;
+    // (the lengths through the scalar unit: the piece loop keeps no VGPR)
+    const __attribute__((address_space(4))) int32_t* sl = (const __attribute__((address_space(4))) int32_t*)p.seq_lens;
+    auto pages_of = [&](int b) {
+        const int n = min(max(sl[b], 0), cap);
+        return (n + kPage - 1) / kPage;
+    };
+    Piece pc;
+    pc.b = w.b;
+    pc.mt = w.mt;
+    pc.page_begin = w.page_begin;
+    pc.nsplit = w.nsplit;
+    int piece = w.piece;
+    int left = w.npages, done = 0;
+    for (;;) {
+        const int pages = pages_of(pc.b);
+        pc.page_end = min(pages, pc.page_begin + left);
+        pc.slot = piece * p.plan.m_tiles + pc.mt;
+        // (one value in every lane: kept in scalar registers)
+        pc.b = __builtin_amdgcn_readfirstlane(pc.b);
+        pc.mt = __builtin_amdgcn_readfirstlane(pc.mt);
+        pc.page_begin = __builtin_amdgcn_readfirstlane(pc.page_begin);
+        pc.page_end = __builtin_amdgcn_readfirstlane(pc.page_end);
+        pc.nsplit = __builtin_amdgcn_readfirstlane(pc.nsplit);
+        pc.slot = __builtin_amdgcn_readfirstlane(pc.slot);
+        // (a stored item that points past the workspace's partial slots is not followed)
+        if (pc.nsplit > 1 && (pc.slot < 0 || pc.slot >= p.plan.units_max)) break;
+        body(pc);
+        const int took = pc.page_end - pc.page_begin;
+        left -= took;
+        done += took;
+        if (!kMulti || w.chunk <= 0 || left <= 0 || took <= 0) break;
+        int b = pc.b + 1;
+        while (b < p.plan.batch && pages_of(b) == 0) ++b;
+        if (b >= p.plan.batch) break;
+        __syncthreads();
+        const int g = w.g0 + done;   // the request's first global page
+        pc.b = __builtin_amdgcn_readfirstlane(b);
+        pc.page_begin = 0;
+        pc.nsplit = __builtin_amdgcn_readfirstlane((g + pages_of(b) - 1) / w.chunk - g / w.chunk + 1);
+        ++piece;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -465,14 +631,20 @@ __device__ __forceinline__ float pair_sum(float v) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void decode_bf16_kernel(DecodeParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+// The lane index, recomputed where it is called (mbcnt in inline assembly):
+// the decode bodies run once per piece inside a loop, and a lane index the
+// compiler may hoist would drag every value derived from it out of the loop,
+// live (in VGPRs) across the whole body.
+__device__ __forceinline__ int lane_id_fresh() {
+    int v;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+    return v;
+}
 
-    const WorkItem w = decode_work_item(p, lds);
-    if (w.b < 0) return;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__device__ __forceinline__ void decode_bf16_body(const DecodeParams& p, const Piece& w, uint8_t* lds,
+                                                 const int wave) {
+    const int lane = lane_id_fresh();
+    const int tid = wave * 64 + lane;
     const int G = lane >> 5;        // MFMA k-group of this lane (0/1)
     const int lr = lane & 31;       // query row of this lane within its 32-row tile
     const int b = w.b;
@@ -816,7 +988,7 @@ void decode_bf16_kernel(DecodeParams p) {
         const int t0 = n - k * kHalfTok;     // callers pass half pages holding >= 1 token
         if (t0 >= kHalfTok) return;
         lds_u8* cur = slot_ptr(k);
-        for (int idx = threadIdx.x; idx < (kHalfTok - t0) * kRowChunks; idx += 256) {
+        for (int idx = tid; idx < (kHalfTok - t0) * kRowChunks; idx += 256) {
             const int t = t0 + idx / kRowChunks;
             const int c = idx % kRowChunks;
             *(__attribute__((address_space(3))) i32x4*)(cur + t * kRowBytes + c * 16) = (i32x4)0;
@@ -947,7 +1119,7 @@ void decode_bf16_kernel(DecodeParams p) {
                             (f32x4){ot[dq][4 * q4], ot[dq][4 * q4 + 1], ot[dq][4 * q4 + 2], ot[dq][4 * q4 + 3]} * inv;
             }
         } else {
-            float* dst = p.ws_o + ((size_t)blockIdx.x * kMTile + rit) * kV + dim0;
+            float* dst = p.ws_o + ((size_t)w.slot * kMTile + rit) * kV + dim0;
 #pragma unroll
             for (int dq = 0; dq < 4; ++dq)
 #pragma unroll
@@ -961,7 +1133,7 @@ void decode_bf16_kernel(DecodeParams p) {
         // writes its dims of the rows (scaled by 1 / l) into rows of 2064
         // bytes, then the workgroup stores whole contiguous row pieces
         constexpr int kStRow = 4 * kV + 16;
-        float* gbase = w.nsplit > 1 ? p.ws_o + (size_t)blockIdx.x * kMTile * kV
+        float* gbase = w.nsplit > 1 ? p.ws_o + (size_t)w.slot * kMTile * kV
                                     : (float*)p.out + ((size_t)b * p.rows + (size_t)w.mt * kMTile) * kV;
         for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -980,7 +1152,7 @@ void decode_bf16_kernel(DecodeParams p) {
             __syncthreads();
 #pragma unroll 4
             for (int k = 0; k < 32; ++k) {
-                const int i = k * 256 + (int)threadIdx.x;
+                const int i = k * 256 + (int)tid;
                 const int rl = i >> 7, c = i & 127;
                 if (w.mt * kMTile + 64 * hf + rl < p.rows)
                     *(f32x4*)(gbase + (size_t)(64 * hf + rl) * kV + 4 * c) =
@@ -995,8 +1167,17 @@ void decode_bf16_kernel(DecodeParams p) {
     if (row_ok && G == 0) {
         const float lse = l_own > 0.f ? (m + __log2f(l_own)) * kLn2 : -INFINITY;
         if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
-        else p.ws_lse[(size_t)blockIdx.x * kMTile + (row - w.mt * kMTile)] = lse;
+        else p.ws_lse[(size_t)w.slot * kMTile + (row - w.mt * kMTile)] = lse;
     }
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void decode_bf16_kernel(DecodeParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
+    const WorkItem wi = decode_work_item(p, lds);
+    if (wi.b < 0) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for_each_piece<false>(p, wi, [&](const Piece& pc) { decode_bf16_body(p, pc, lds, wave); });
 }
 
 // ---------------------------------------------------------------------------
@@ -1046,9 +1227,10 @@ __device__ __forceinline__ int hw_simd_id() {
 }
 
 template <bool A>
-__device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const WorkItem& w, uint8_t* lds,
-                                                    const int s) {
-    const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const Piece& w, uint8_t* lds,
+                                                    const int s, const int wv) {
+    const int lane = lane_id_fresh();
+    const int tid = wv * 64 + lane;
     const int G = lane >> 5;        // MFMA k-group of this lane
     const int lr = lane & 31;       // query row (QK^T B operand, PV result) / token (QK^T A operand)
     const int b = w.b;
@@ -1108,7 +1290,6 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
     // lane (lr, G) holds dims + 8 G .. + 7 of row lr (chunk 2 ks + G)
     bf16x8_t qf[A ? 36 : 1];
     {
-        const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const uint8_t* qreq = (const uint8_t*)p.q + (size_t)b * p.rows * kRowBytes;
 #pragma unroll
         for (int j = 0; j < 18; ++j) {
@@ -1429,7 +1610,7 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
         // writes its dims of the rows (scaled by 1 / l) into rows of 2064
         // bytes, then the workgroup stores whole contiguous row pieces
         constexpr int kStRow = 4 * kV + 16;
-        float* gbase = w.nsplit > 1 ? p.ws_o + (size_t)blockIdx.x * kMTile * kV
+        float* gbase = w.nsplit > 1 ? p.ws_o + (size_t)w.slot * kMTile * kV
                                     : (float*)p.out + ((size_t)b * p.rows + (size_t)w.mt * kMTile) * kV;
         for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
@@ -1449,7 +1630,7 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
             __syncthreads();
 #pragma unroll 4
             for (int kk = 0; kk < 16; ++kk) {
-                const int i = kk * 512 + (int)threadIdx.x;
+                const int i = kk * 512 + (int)tid;
                 const int rl = i >> 7, c = i & 127;
                 if (w.mt * kMTile + 64 * hf + rl < p.rows)
                     *(f32x4*)(gbase + (size_t)(64 * hf + rl) * kV + 4 * c) =
@@ -1479,7 +1660,7 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
     if (A && row_ok && G == 0) {
         const float lse = l_row > 0.f ? (m + __log2f(l_row)) * kLn2 : -INFINITY;
         if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
-        else p.ws_lse[(size_t)blockIdx.x * kMTile + (row - w.mt * kMTile)] = lse;
+        else p.ws_lse[(size_t)w.slot * kMTile + (row - w.mt * kMTile)] = lse;
     }
 }
 
@@ -1507,8 +1688,10 @@ void decode_bf16_ab_kernel(DecodeParams p) {
     const bool by_hw = cnt0 == 2 && cnt1 == 2 && cnt2 == 2 && cnt3 == 2;
     const bool is_a = by_hw ? lower == 0 : wv < 4;
     const int s = by_hw ? sid : (wv & 3);
-    if (is_a) decode_bf16_ab_body<true>(p, w, lds, s);
-    else decode_bf16_ab_body<false>(p, w, lds, s);
+    for_each_piece<false>(p, w, [&](const Piece& pc) {
+        if (is_a) decode_bf16_ab_body<true>(p, pc, lds, s, wv);
+        else decode_bf16_ab_body<false>(p, pc, lds, s, wv);
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -1580,14 +1763,10 @@ __device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d) {
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void decode_fp8_kernel(DecodeParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes8];
-
-    const WorkItem w = decode_work_item(p, lds);
-    if (w.b < 0) return;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__device__ __forceinline__ void decode_fp8_body(const DecodeParams& p, const Piece& w, uint8_t* lds,
+                                                const int wave) {
+    const int lane = lane_id_fresh();
+    const int tid = wave * 64 + lane;
     const int h = wave & 1;         // PV: which half of the 512 output dims
     const int G = lane >> 5;        // MFMA k-half of this lane (0/1)
     const int lr = lane & 31;       // query row (QK B operand) / token (QK A operand) of this lane
@@ -1893,7 +2072,7 @@ void decode_fp8_kernel(DecodeParams p) {
         const int t0 = n - k * kPage;     // callers pass pages holding >= 1 token
         if (t0 >= kPage) return;
         lds_u8* cur = slot_ptr(k);
-        for (int idx = threadIdx.x; idx < (kPage - t0) * kRowChunks8; idx += 256) {
+        for (int idx = tid; idx < (kPage - t0) * kRowChunks8; idx += 256) {
             const int t = t0 + idx / kRowChunks8;
             const int c = idx % kRowChunks8;
             *(lds_i32x4*)(cur + t * kRowBytes8 + c * 16) = (i32x4)0;
@@ -2013,7 +2192,7 @@ void decode_fp8_kernel(DecodeParams p) {
                             (f32x4){o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]} * inv;
             }
         } else {
-            float* dst = p.ws_o + ((size_t)blockIdx.x * kMTile + rit) * kV + dim0;
+            float* dst = p.ws_o + ((size_t)w.slot * kMTile + rit) * kV + dim0;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -2028,8 +2207,17 @@ void decode_fp8_kernel(DecodeParams p) {
         // l sums exp2(s c - m + 4): ln sum exp = (m - 4 + log2 l) ln 2
         const float lse = l_own > 0.f ? (m - kWeightOffset8 + __log2f(l_own)) * kLn2 : -INFINITY;
         if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
-        else p.ws_lse[(size_t)blockIdx.x * kMTile + (row - w.mt * kMTile)] = lse;
+        else p.ws_lse[(size_t)w.slot * kMTile + (row - w.mt * kMTile)] = lse;
     }
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void decode_fp8_kernel(DecodeParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes8];
+    const WorkItem wi = decode_work_item(p, lds);
+    if (wi.b < 0) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for_each_piece<true>(p, wi, [&](const Piece& pc) { decode_fp8_body(p, pc, lds, wave); });
 }
 
 // ---------------------------------------------------------------------------
@@ -2103,12 +2291,12 @@ __device__ __forceinline__ void merge_row(int n, PartialAt at, void* out, float*
 struct SplitPartials {
     const float* ws_o;
     const float* ws_lse;
-    int base, mt, m_tiles, per_xcd, rit;
+    int first, mt, m_tiles, rit;
     __device__ const float* lse(int s) const {
-        return ws_lse + (size_t)unit_index(base + s, mt, m_tiles, per_xcd) * kMTile + rit;
+        return ws_lse + ((size_t)(first + s) * m_tiles + mt) * kMTile + rit;
     }
     __device__ const float* out(int s) const {
-        return ws_o + ((size_t)unit_index(base + s, mt, m_tiles, per_xcd) * kMTile + rit) * kV;
+        return ws_o + (((size_t)(first + s) * m_tiles + mt) * kMTile + rit) * kV;
     }
 };
 
@@ -2117,15 +2305,26 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     if (grow >= (long long)p.batch * p.rows) return;
     const int b = (int)(grow / p.rows);
     const int r = (int)(grow - (long long)b * p.rows);
-    const int S = p.req_info[2 * b];
-    if (S <= 1) return;   // a single split wrote the result directly
-    const int first = p.req_info[2 * b + 1];
-    const int k_total = p.req_info[2 * (p.batch - 1)] + p.req_info[2 * (p.batch - 1) + 1];
-    const int per_xcd = (k_total + 7) / 8;
-    // (a split list that does not fit the workspace, e.g. one stored for
-    // another descriptor, is not followed: every slot index stays below units_max)
-    if (first < 0 || first > k_total - S || per_xcd < 1 || (long long)per_xcd * p.m_tiles * 8 > p.units_max) return;
-    SplitPartials at{p.ws_o, p.ws_lse, first, r / kMTile, p.m_tiles, per_xcd, r % kMTile};
+    const int S = p.req_info[kReqInfoInts * b];
+    if (S == 1) return;   // a single piece wrote the result directly
+    if (S == 0) {
+        // an empty request under the balanced plan: no piece, no token
+        const int lane = threadIdx.x & 63;
+        if (p.out_bf16) {
+            *((int4*)((__bf16*)p.out + (size_t)grow * kV) + lane) = make_int4(0, 0, 0, 0);
+        } else {
+            f32x4* dst = (f32x4*)((float*)p.out + (size_t)grow * kV) + 2 * lane;
+            dst[0] = (f32x4)0.f;
+            dst[1] = (f32x4)0.f;
+        }
+        if (lane == 0) p.lse[grow] = -INFINITY;
+        return;
+    }
+    const int first = p.req_info[kReqInfoInts * b + 1];
+    // (a plan that does not fit the workspace, e.g. one stored for another
+    // descriptor, is not followed: every slot index stays below units_max)
+    if (S < 0 || first < 0 || (long long)(first + S) * p.m_tiles > p.units_max) return;
+    SplitPartials at{p.ws_o, p.ws_lse, first, r / kMTile, p.m_tiles, r % kMTile};
     merge_row(S, at, p.out, p.lse, (size_t)grow, p.out_bf16);
 }
 

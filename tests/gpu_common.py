@@ -37,6 +37,23 @@ def run_hip(inp, num_splits: int = 0, out_dtype=None, stream=None):
     return out, lse
 
 
+def balanced_plan_lens():
+    """128 ragged lengths (64..4000 tokens, one empty request, one of a single
+    token) for which the planner's policy takes the balanced plan on an fp8
+    cache with one row tile (checked by tests/test_gpu_plan.py's restatement)."""
+    rng = np.random.default_rng(58)
+    lens = rng.integers(64, 4000, size=128)
+    lens[rng.integers(0, 128)] = 0
+    lens[rng.integers(0, 128)] = 1
+    return lens.tolist()
+
+
+def plan_info(dec, batch: int):
+    """The planner's per-request values from a decoder's workspace: int32
+    [batch][4] (pieces, first piece, first global page or 0, 0)."""
+    return dec.workspace[: 16 * batch].view(torch.int32).view(batch, 4).cpu().numpy()
+
+
 def to_f64_q(inp, requests=None):
     q = inp.q if requests is None else inp.q[requests]
     if inp.dtype == "bf16":

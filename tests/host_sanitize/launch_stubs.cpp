@@ -90,7 +90,7 @@ static void check_decode(const char* k, const DecodeParams& p, int units) {
     need(k, "seq_lens", p.seq_lens, B * 4);
     need(k, "work", p.work, (size_t)units * sizeof(WorkItem));
     need(k, "work_out", p.work_out, (size_t)units * sizeof(WorkItem));
-    need(k, "req_info", p.req_info, B * 8);
+    need(k, "req_info", p.req_info, B * 4 * kReqInfoInts);
     need(k, "out", p.out, B * p.rows * kV * (p.out_bf16 ? 2 : 4));
     need(k, "lse", p.lse, B * p.rows * 4);
     need(k, "ws_o", p.ws_o, (size_t)units * kMTile * kV * 4);
@@ -101,7 +101,7 @@ static void check_decode(const char* k, const DecodeParams& p, int units) {
 hipError_t launch_plan(const PlanParams& p, const int32_t* seq_lens, int32_t* req_info, WorkItem* work,
                        hipStream_t) {
     need("plan", "seq_lens", seq_lens, (size_t)p.batch * 4);
-    need("plan", "req_info", req_info, (size_t)p.batch * 8);
+    need("plan", "req_info", req_info, (size_t)p.batch * 4 * kReqInfoInts);
     need("plan", "work", work, (size_t)p.units_max * sizeof(WorkItem));
     ++g_launches;
     return hipSuccess;
@@ -121,7 +121,7 @@ hipError_t launch_decode_fp8(const DecodeParams& p, int units, hipStream_t, hipE
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t) {
     const size_t B = (size_t)p.batch;
-    need("combine", "req_info", p.req_info, B * 8);
+    need("combine", "req_info", p.req_info, B * 4 * kReqInfoInts);
     need("combine", "ws_o", p.ws_o, (size_t)p.units_max * kMTile * kV * 4);
     need("combine", "ws_lse", p.ws_lse, (size_t)p.units_max * kMTile * 4);
     need("combine", "out", p.out, B * p.rows * kV * (p.out_bf16 ? 2 : 4));

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import workloads
-from tests.gpu_common import compare, run_hip, run_oracle, say
+from tests.gpu_common import balanced_plan_lens, compare, plan_info, run_hip, run_oracle, say
 
 pytestmark = pytest.mark.gpu
 
@@ -186,6 +186,36 @@ def test_fp8_ragged_many_pages_and_splits():
     for ns in (0, 1, 5, 30):
         out, lse = run_hip(inp, num_splits=ns)
         compare(out, lse, o_ref, l_ref, dtype="fp8", what=f"fp8 ragged splits={ns}")
+
+
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_fp8_balanced_plan_multi_piece_units(out_bf16):
+    """Ragged fp8 batch for which the planner lays all pages end to end and
+    cuts equal kv-units: workgroups run several request pieces in turn, an
+    empty request gets no piece (the combine writes its zeros), and most
+    requests are merged from pieces of different workgroups.  A seeded sample
+    of whole requests, plus the empty and single-token ones, against the oracle."""
+    import mla_latent_decode_absorbed_amd as mla
+    lens = balanced_plan_lens()
+    say(f"fp8 balanced plan, 128 ragged requests, {sum(lens)} tokens, bf16 out={out_bf16}")
+    inp = workloads.make_decode_inputs(128, 1, 16, lens, "fp8", seed=36, device=dev())
+    desc = mla.make_desc(128, 1, 16, inp.kv_cache.shape[0], inp.block_table.shape[1], kv_dtype=mla.FP8_E4M3,
+                         out_dtype=mla.BF16 if out_bf16 else mla.F32)
+    dec = mla.Decoder(desc, device=dev())
+    out, lse = dec(inp.q, inp.kv_cache, inp.block_table, inp.seq_lens, inp.scale, kv_scale=inp.kv_scale)
+    torch.cuda.synchronize()
+    info = plan_info(dec, 128)
+    assert (info[:, 2] > 0).any(), "the balanced plan was expected"
+    empty, single = lens.index(0), lens.index(1)
+    assert info[empty, 0] == 0
+    rng = np.random.default_rng(37)
+    multi = np.nonzero(info[:, 0] > 1)[0]
+    req = sorted(set(rng.choice(128, size=14, replace=False).tolist()) | {empty, single} |
+                 set(rng.choice(multi, size=4, replace=False).tolist()))
+    o_ref, l_ref = run_oracle(inp, requests=req)
+    idx = torch.tensor(req, dtype=torch.long, device=dev())
+    compare(out[idx], lse[idx], o_ref, l_ref, dtype="fp8", what=f"fp8 balanced plan bf16 out={out_bf16}")
+    assert torch.all(out[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
 
 
 @pytest.mark.parametrize("num_splits", [0, 3])

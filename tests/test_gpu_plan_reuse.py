@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import workloads
-from tests.gpu_common import compare, run_oracle, say
+from tests.gpu_common import balanced_plan_lens, compare, run_oracle, say
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,8 @@ CASES = [
     ("bf16 fixed 3 splits, 2 row tiles", dict(batch=2, q_len=2, heads=100, seq_lens=[700, 129], dtype="bf16"), 3),
     ("fp8 ragged with an empty request", dict(batch=4, q_len=1, heads=64, seq_lens=[1, 0, 2100, 640],
                                               dtype="fp8"), 0),
+    ("fp8 balanced plan, 128 requests", dict(batch=128, q_len=1, heads=16, seq_lens=balanced_plan_lens(),
+                                             dtype="fp8"), 0),
 ]
 
 

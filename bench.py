@@ -632,7 +632,7 @@ def decode_record(name: str, inp, args, hev, num_splits: int, steps: int, cpu_bu
     info = req_info[:, 0]
     balanced_plan = bool((req_info[:, 2] != 0).any())
     partial_rows = int(sum(int(sp) for sp in info.tolist() if sp > 1) * inp.q_len * inp.heads)
-    partial_bytes = partial_rows * (512 * 4 + 4)
+    partial_bytes = partial_rows * (512 * 2 + 4)       # bf16 partial row + fp32 lse
 
     peak_tf = MFMA_PEAK_TFLOPS[inp.dtype]
     kv_gbs = acc["kv_bytes"] / (ms_per_step * 1e-3) / 1e9

@@ -127,7 +127,10 @@ int mla_decode_workspace_size(const mla_decode_desc* desc, size_t* bytes);
  *   workspace   device, >= mla_decode_workspace_size() bytes, 256-byte aligned.
  * Work: a planning kernel reads seq_lens on the device and writes the split
  * list into the workspace; the split-KV decode kernel streams the pages; a
- * combine kernel LSE-merges the splits of each row into `out` / `lse`.
+ * combine kernel LSE-merges the splits of each row into `out` / `lse`.  A
+ * request decoded in one piece is written straight to out in fp32 or bf16;
+ * one cut into several pieces passes through bf16 partial outputs (each
+ * normalised, so rounded within 2^-9 of its magnitude) and fp32 partial LSEs.
  * Returns MLA_OK or a negative mla_status (before any device work on a bad
  * argument). */
 int mla_decode_partial(const mla_decode_desc* desc, const void* q, const void* kv_cache,
@@ -150,10 +153,11 @@ int mla_decode_partial(const mla_decode_desc* desc, const void* q, const void* k
  *    first call on that device (make that first call outside graph capture).
  *  - A descriptor whose workspace (mla_decode_workspace_size) exceeds the
  *    scratch returns MLA_ERR_SCRATCH_LIMIT before any device work.  The
- *    workspace holds 262,688 bytes per work unit, and the automatic split of
- *    B requests of T 128-row tiles sizes for ceil((256 / T + B) / 8) * 8 * T
- *    units: up to 504 units fit (for example B = 128 with 128 heads, or
- *    B = 32 with 512 heads); 256 fixed splits of a long sequence do not.
+ *    workspace holds 131,616 bytes per work unit (bf16 split partials), and
+ *    the automatic split of B requests of T 128-row tiles sizes for
+ *    ceil((256 / T + B) / 8) * 8 * T units: up to 1,016 units fit (for
+ *    example B = 760 with 128 heads, or B = 128 with 512 heads); 256 fixed
+ *    splits of a long sequence do not.
  *  - The call allocates and frees nothing: no hipMalloc or hipFree and no
  *    allocating library routine.
  *  - Every call on a GPU shares that GPU's scratch, which keeps the last

@@ -83,7 +83,7 @@ WorkspaceLayout layout_for(const mla_decode_desc* d) {
     L.ws_lse = off;
     off = align_up(off + sizeof(float) * (size_t)L.units_max * mla::kMTile);
     L.ws_o = off;
-    off = align_up(off + sizeof(float) * (size_t)L.units_max * mla::kMTile * mla::kV);
+    off = align_up(off + sizeof(uint16_t) * (size_t)L.units_max * mla::kMTile * mla::kV);   // bf16 partials
     L.total = off;
     return L;
 }
@@ -176,7 +176,7 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     dp.fused_plan = fused_plan ? 1 : 0;
     dp.out = out;
     dp.lse = lse;
-    dp.ws_o = (float*)(ws + L.ws_o);
+    dp.ws_o = ws + L.ws_o;
     dp.ws_lse = (float*)(ws + L.ws_lse);
     dp.scale_log2 = scale * 1.4426950408889634f;
     dp.rows = rows;

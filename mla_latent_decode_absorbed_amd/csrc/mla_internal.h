@@ -59,7 +59,7 @@ struct DecodeParams {
                                 // 0: work[] comes from the planner kernel, of this call or an earlier one
     void* out;                  // [B][M][512] of out_dtype
     float* lse;                 // [B][M]
-    float* ws_o;                // [units_max][kMTile][512], slot piece * m_tiles + mt
+    void* ws_o;                 // bf16 [units_max][kMTile][512] split partials, slot piece * m_tiles + mt
     float* ws_lse;              // [units_max][kMTile]
     float scale_log2;           // scale * log2(e)
     int32_t rows;               // M = q_len * H
@@ -82,7 +82,7 @@ __host__ __device__ inline int clamp_page(int pid, int num_pages) {
 
 struct CombineParams {
     const int32_t* req_info;    // [B][kReqInfoInts]: pieces, first piece, first page
-    const float* ws_o;
+    const void* ws_o;           // bf16 split partials
     const float* ws_lse;
     void* out;
     float* lse;

@@ -1090,79 +1090,52 @@ __device__ __forceinline__ void decode_bf16_body(const DecodeParams& p, const Pi
     __syncthreads();                      // every wave is done reading the exchange buffers
     *abuf_mine = l_own;
     __syncthreads();
-    // element i of dim tile dq is dim 128 w + 32 dq + 8 (i / 4) + 4 G + i % 4
+    // element i of dim tile dq is dim 128 w + 32 dq + 8 (i / 4) + 4 G + i % 4.
+    // Rows leave through the idle ring: per half (64 rows) every wave writes
+    // its dims of the rows, scaled by 1 / l, as fp32 (a single piece to an
+    // fp32 output) or bf16 (a bf16 output, or a split partial), into rows of
+    // 512 e + 16 bytes; then the workgroup stores whole contiguous row pieces.
     const int dim0 = 128 * wave + 4 * G;
-    auto store_tile = [&](const f32x16 (&ot)[4], int r, float lt) {
-        if (r >= p.rows) return;
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        const int rit = r - w.mt * kMTile;
-        if (w.nsplit == 1) {
-            const size_t orow = (size_t)b * p.rows + r;
-            if (p.out_bf16) {
-                __bf16* dst = (__bf16*)p.out + orow * kV + dim0;
+    {
+        const bool f32 = w.nsplit == 1 && !p.out_bf16;
+        const int e = f32 ? 4 : 2;
+        const int st_row = kV * e + 16;
+        const int row_chunks = kV * e / 16;
+        uint8_t* gbase = w.nsplit > 1 ? (uint8_t*)p.ws_o + (size_t)w.slot * kMTile * kV * 2
+                                      : (uint8_t*)p.out + ((size_t)b * p.rows + (size_t)w.mt * kMTile) * kV * e;
 #pragma unroll
-                for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        __bf16 __attribute__((ext_vector_type(4))) v;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(ot[dq][4 * q4 + i] * inv);
-                        *(__bf16 __attribute__((ext_vector_type(4)))*)(dst + 32 * dq + 8 * q4) = v;
-                    }
-            } else {
-                float* dst = (float*)p.out + orow * kV + dim0;
-#pragma unroll
-                for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        *(f32x4*)(dst + 32 * dq + 8 * q4) =
-                            (f32x4){ot[dq][4 * q4], ot[dq][4 * q4 + 1], ot[dq][4 * q4 + 2], ot[dq][4 * q4 + 3]} * inv;
-            }
-        } else {
-            float* dst = p.ws_o + ((size_t)w.slot * kMTile + rit) * kV + dim0;
-#pragma unroll
-            for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    *(f32x4*)(dst + 32 * dq + 8 * q4) =
-                        (f32x4){ot[dq][4 * q4], ot[dq][4 * q4 + 1], ot[dq][4 * q4 + 2], ot[dq][4 * q4 + 3]} * inv;
-        }
-    };
-    if (w.nsplit > 1 || !p.out_bf16) {
-        // fp32 rows leave through the idle ring: per half (64 rows) every wave
-        // writes its dims of the rows (scaled by 1 / l) into rows of 2064
-        // bytes, then the workgroup stores whole contiguous row pieces
-        constexpr int kStRow = 4 * kV + 16;
-        float* gbase = w.nsplit > 1 ? p.ws_o + (size_t)w.slot * kMTile * kV
-                                    : (float*)p.out + ((size_t)b * p.rows + (size_t)w.mt * kMTile) * kV;
         for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 const int t = 2 * hf + tt;
                 const float lt = abuf[t * 64];
                 const float inv = lt > 0.f ? 1.f / lt : 0.f;
-                lds_u8* srow = ring + (32 * tt + lr) * kStRow + 4 * dim0;
+                lds_u8* srow = ring + (32 * tt + lr) * st_row + e * dim0;
 #pragma unroll
                 for (int dq = 0; dq < 4; ++dq)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        *(__attribute__((address_space(3))) f32x4*)(srow + 4 * (32 * dq + 8 * q4)) =
-                            (f32x4){o[t][dq][4 * q4], o[t][dq][4 * q4 + 1], o[t][dq][4 * q4 + 2], o[t][dq][4 * q4 + 3]} * inv;
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x4 v = (f32x4){o[t][dq][4 * q4], o[t][dq][4 * q4 + 1], o[t][dq][4 * q4 + 2],
+                                                o[t][dq][4 * q4 + 3]} * inv;
+                        if (f32) {
+                            *(__attribute__((address_space(3))) f32x4*)(srow + 4 * (32 * dq + 8 * q4)) = v;
+                        } else {
+                            __bf16 __attribute__((ext_vector_type(4))) h;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) h[i] = (__bf16)v[i];
+                            *(lds_i16x4*)(srow + 2 * (32 * dq + 8 * q4)) = __builtin_bit_cast(i16x4, h);
+                        }
+                    }
             }
             __syncthreads();
-#pragma unroll 4
-            for (int k = 0; k < 32; ++k) {
-                const int i = k * 256 + (int)tid;
-                const int rl = i >> 7, c = i & 127;
+            for (int i = (int)tid; i < 64 * row_chunks; i += 256) {
+                const int rl = i / row_chunks, c = i - rl * row_chunks;
                 if (w.mt * kMTile + 64 * hf + rl < p.rows)
-                    *(f32x4*)(gbase + (size_t)(64 * hf + rl) * kV + 4 * c) =
-                        *(const __attribute__((address_space(3))) f32x4*)(ring + rl * kStRow + 16 * c);
+                    *(i32x4*)(gbase + (size_t)(64 * hf + rl) * kV * e + 16 * c) =
+                        *(const __attribute__((address_space(3))) i32x4*)(ring + rl * st_row + 16 * c);
             }
             __syncthreads();
         }
-    } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) store_tile(o[t], w.mt * kMTile + 32 * t + lr, abuf[t * 64]);
     }
     if (row_ok && G == 0) {
         const float lse = l_own > 0.f ? (m + __log2f(l_own)) * kLn2 : -INFINITY;
@@ -1605,13 +1578,19 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
     float lt[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) lt[t] = lbuf[t * 32 + lr];
-    if (w.nsplit > 1 || !p.out_bf16) {
-        // fp32 rows leave through the idle ring: per half (64 rows) every wave
-        // writes its dims of the rows (scaled by 1 / l) into rows of 2064
-        // bytes, then the workgroup stores whole contiguous row pieces
-        constexpr int kStRow = 4 * kV + 16;
-        float* gbase = w.nsplit > 1 ? p.ws_o + (size_t)w.slot * kMTile * kV
-                                    : (float*)p.out + ((size_t)b * p.rows + (size_t)w.mt * kMTile) * kV;
+    // Rows leave through the idle ring: per half (64 rows) every wave writes
+    // its dims of the rows, scaled by 1 / l, as fp32 (a single piece to an
+    // fp32 output) or bf16 (a bf16 output, or a split partial), into rows of
+    // 512 e + 16 bytes; then the workgroup stores whole contiguous row pieces,
+    // 16 bytes per lane.
+    {
+        const bool f32 = w.nsplit == 1 && !p.out_bf16;
+        const int e = f32 ? 4 : 2;
+        const int st_row = kV * e + 16;
+        const int row_chunks = kV * e / 16;
+        uint8_t* gbase = w.nsplit > 1 ? (uint8_t*)p.ws_o + (size_t)w.slot * kMTile * kV * 2
+                                      : (uint8_t*)p.out + ((size_t)b * p.rows + (size_t)w.mt * kMTile) * kV * e;
+#pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
@@ -1619,42 +1598,30 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
                 const float inv = lt[t] > 0.f ? 1.f / lt[t] : 0.f;
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    lds_u8* srow = ring + (32 * tt + lr) * kStRow + 4 * (32 * (4 * s + J0 + j) + 4 * G);
+                    lds_u8* srow = ring + (32 * tt + lr) * st_row + e * (32 * (4 * s + J0 + j) + 4 * G);
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        *(__attribute__((address_space(3))) f32x4*)(srow + 4 * 8 * q4) =
-                            (f32x4){o_elem(j, t, 4 * q4), o_elem(j, t, 4 * q4 + 1), o_elem(j, t, 4 * q4 + 2),
-                                    o_elem(j, t, 4 * q4 + 3)} * inv;
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x4 v = (f32x4){o_elem(j, t, 4 * q4), o_elem(j, t, 4 * q4 + 1), o_elem(j, t, 4 * q4 + 2),
+                                                o_elem(j, t, 4 * q4 + 3)} * inv;
+                        if (f32) {
+                            *(__attribute__((address_space(3))) f32x4*)(srow + 4 * 8 * q4) = v;
+                        } else {
+                            __bf16 __attribute__((ext_vector_type(4))) h;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) h[i] = (__bf16)v[i];
+                            *(lds_i16x4*)(srow + 2 * 8 * q4) = __builtin_bit_cast(i16x4, h);
+                        }
+                    }
                 }
             }
             __syncthreads();
-#pragma unroll 4
-            for (int kk = 0; kk < 16; ++kk) {
-                const int i = kk * 512 + (int)tid;
-                const int rl = i >> 7, c = i & 127;
+            for (int i = (int)tid; i < 64 * row_chunks; i += 512) {
+                const int rl = i / row_chunks, c = i - rl * row_chunks;
                 if (w.mt * kMTile + 64 * hf + rl < p.rows)
-                    *(f32x4*)(gbase + (size_t)(64 * hf + rl) * kV + 4 * c) =
-                        *(const __attribute__((address_space(3))) f32x4*)(ring + rl * kStRow + 16 * c);
+                    *(i32x4*)(gbase + (size_t)(64 * hf + rl) * kV * e + 16 * c) =
+                        *(const __attribute__((address_space(3))) i32x4*)(ring + rl * st_row + 16 * c);
             }
             __syncthreads();
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int r = w.mt * kMTile + 32 * t + lr;
-            if (r >= p.rows) continue;
-            const float inv = lt[t] > 0.f ? 1.f / lt[t] : 0.f;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                __bf16* dst = (__bf16*)p.out + ((size_t)b * p.rows + r) * kV + 32 * (4 * s + J0 + j) + 4 * G;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    __bf16 __attribute__((ext_vector_type(4))) v;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o_elem(j, t, 4 * q4 + i) * inv);
-                    *(__bf16 __attribute__((ext_vector_type(4)))*)(dst + 8 * q4) = v;
-                }
-            }
         }
     }
     if (A && row_ok && G == 0) {
@@ -2169,30 +2136,21 @@ __device__ __forceinline__ void decode_fp8_body(const DecodeParams& p, const Pie
     auto store_tile = [&](const f32x16 (&o)[8], int r, float inv) {
         if (r >= p.rows) return;
         const int rit = r - w.mt * kMTile;
-        if (w.nsplit == 1) {
-            const size_t orow = (size_t)b * p.rows + r;
-            if (p.out_bf16) {
-                __bf16* dst = (__bf16*)p.out + orow * kV + dim0;
+        if (w.nsplit > 1 || p.out_bf16) {
+            // a bf16 output row, or a split partial (bf16)
+            __bf16* dst = w.nsplit > 1 ? (__bf16*)p.ws_o + ((size_t)w.slot * kMTile + rit) * kV + dim0
+                                       : (__bf16*)p.out + ((size_t)b * p.rows + r) * kV + dim0;
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
+            for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        __bf16 __attribute__((ext_vector_type(4))) v;
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    __bf16 __attribute__((ext_vector_type(4))) v;
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[dt][4 * q4 + i] * inv);
-                        *(__bf16 __attribute__((ext_vector_type(4)))*)(dst + 32 * dt + 8 * q4) = v;
-                    }
-            } else {
-                float* dst = (float*)p.out + orow * kV + dim0;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
-                        *(f32x4*)(dst + 32 * dt + 8 * q4) =
-                            (f32x4){o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]} * inv;
-            }
+                    for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[dt][4 * q4 + i] * inv);
+                    *(__bf16 __attribute__((ext_vector_type(4)))*)(dst + 32 * dt + 8 * q4) = v;
+                }
         } else {
-            float* dst = p.ws_o + ((size_t)w.slot * kMTile + rit) * kV + dim0;
+            float* dst = (float*)p.out + ((size_t)b * p.rows + r) * kV + dim0;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -2223,13 +2181,25 @@ void decode_fp8_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // LSE merge of one row from n partials: one wave, 8 output dims per lane
 // ---------------------------------------------------------------------------
+// This lane's 8 consecutive values of a 512-value partial row (fp32 or bf16).
+__device__ __forceinline__ void load_row8(const float* row, int lane, f32x4& a, f32x4& b) {
+    const f32x4* src = (const f32x4*)row + 2 * lane;
+    a = src[0];
+    b = src[1];
+}
+__device__ __forceinline__ void load_row8(const __bf16* row, int lane, f32x4& a, f32x4& b) {
+    const bf16x8 v = *((const bf16x8*)row + lane);
+    a = (f32x4){(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    b = (f32x4){(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+}
+
 template <typename PartialAt>
 __device__ __forceinline__ void merge_row(int n, PartialAt at, void* out, float* lse_out, size_t orow,
                                           int out_bf16) {
     const int lane = threadIdx.x & 63;
     // One pass with a running maximum, 8 partials at a time: all loads of a
-    // group (8 LSEs, the same address in every lane, and 2 x 16 bytes of each
-    // output row per lane) are issued before any is used, so a row with up to
+    // group (8 LSEs, the same address in every lane, and each partial row's 8
+    // values of this lane) are issued before any is used, so a row with up to
     // 8 partials costs one memory round trip.
     float mx = -INFINITY, wsum = 0.f;
     f32x4 acc0 = (f32x4)0.f, acc1 = (f32x4)0.f;
@@ -2240,9 +2210,7 @@ __device__ __forceinline__ void merge_row(int n, PartialAt at, void* out, float*
         for (int u = 0; u < 8; ++u) {
             if (i + u < n) {
                 li[u] = *at.lse(i + u);
-                const f32x4* src = (const f32x4*)at.out(i + u) + 2 * lane;
-                v0[u] = src[0];
-                v1[u] = src[1];
+                load_row8(at.out(i + u), lane, v0[u], v1[u]);
             } else {
                 li[u] = -INFINITY;
             }
@@ -2289,13 +2257,13 @@ __device__ __forceinline__ void merge_row(int n, PartialAt at, void* out, float*
 }
 
 struct SplitPartials {
-    const float* ws_o;
+    const __bf16* ws_o;
     const float* ws_lse;
     int first, mt, m_tiles, rit;
     __device__ const float* lse(int s) const {
         return ws_lse + ((size_t)(first + s) * m_tiles + mt) * kMTile + rit;
     }
-    __device__ const float* out(int s) const {
+    __device__ const __bf16* out(int s) const {
         return ws_o + (((size_t)(first + s) * m_tiles + mt) * kMTile + rit) * kV;
     }
 };
@@ -2324,7 +2292,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     // (a plan that does not fit the workspace, e.g. one stored for another
     // descriptor, is not followed: every slot index stays below units_max)
     if (S < 0 || first < 0 || (long long)(first + S) * p.m_tiles > p.units_max) return;
-    SplitPartials at{p.ws_o, p.ws_lse, first, r / kMTile, p.m_tiles, r % kMTile};
+    SplitPartials at{(const __bf16*)p.ws_o, p.ws_lse, first, r / kMTile, p.m_tiles, r % kMTile};
     merge_row(S, at, p.out, p.lse, (size_t)grow, p.out_bf16);
 }
 

@@ -186,7 +186,8 @@ void decode_cases() {
 void noalloc_cases() {
     const mla_decode_desc fits[] = {desc(64, 1, 128, 4096, 64), desc(128, 1, 128, 17714, 256, MLA_FP8_E4M3),
                                     desc(32, 1, 512, 4096, 128), desc(4, 2, 128, 8192, 2048, MLA_BF16, MLA_F32, 1),
-                                    desc(240, 1, 128, 600, 2)};
+                                    desc(240, 1, 128, 600, 2), desc(300, 1, 128, 600, 2),
+                                    desc(760, 1, 128, 600, 2)};   // 1,016 units: the most that fit
     for (const auto& g : fits) {
         DecodeArgs a(g);
         CHECK(a.ws_bytes <= MLA_NOALLOC_SCRATCH_BYTES);
@@ -196,7 +197,8 @@ void noalloc_cases() {
                     MLA_OK, b, g.batch > 256 ? 3 : 2);
     }
     const mla_decode_desc too_big[] = {desc(4, 2, 128, 8192, 2048, MLA_BF16, MLA_F32, 1, 256),
-                                       desc(512, 1, 128, 4096, 8), desc(300, 1, 128, 600, 2)};
+                                       desc(768, 1, 128, 600, 2),   // 1,024 units
+                                       desc(1024, 1, 128, 4096, 8)};
     for (const auto& g : too_big) {
         DecodeArgs a(g);
         CHECK(a.ws_bytes > MLA_NOALLOC_SCRATCH_BYTES);

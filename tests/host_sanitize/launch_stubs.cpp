@@ -93,7 +93,7 @@ static void check_decode(const char* k, const DecodeParams& p, int units) {
     need(k, "req_info", p.req_info, B * 4 * kReqInfoInts);
     need(k, "out", p.out, B * p.rows * kV * (p.out_bf16 ? 2 : 4));
     need(k, "lse", p.lse, B * p.rows * 4);
-    need(k, "ws_o", p.ws_o, (size_t)units * kMTile * kV * 4);
+    need(k, "ws_o", p.ws_o, (size_t)units * kMTile * kV * 2);
     need(k, "ws_lse", p.ws_lse, (size_t)units * kMTile * 4);
     ++g_launches;
 }
@@ -122,7 +122,7 @@ hipError_t launch_decode_fp8(const DecodeParams& p, int units, hipStream_t, hipE
 hipError_t launch_combine(const CombineParams& p, hipStream_t) {
     const size_t B = (size_t)p.batch;
     need("combine", "req_info", p.req_info, B * 4 * kReqInfoInts);
-    need("combine", "ws_o", p.ws_o, (size_t)p.units_max * kMTile * kV * 4);
+    need("combine", "ws_o", p.ws_o, (size_t)p.units_max * kMTile * kV * 2);
     need("combine", "ws_lse", p.ws_lse, (size_t)p.units_max * kMTile * 4);
     need("combine", "out", p.out, B * p.rows * kV * (p.out_bf16 ? 2 : 4));
     need("combine", "lse", p.lse, B * p.rows * 4);

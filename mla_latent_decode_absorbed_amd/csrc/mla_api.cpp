@@ -7,6 +7,7 @@
 #include "mla_upproj.h"
 #include "mla_gather.h"
 
+#include <algorithm>
 #include <atomic>
 #include <math.h>
 #include <stdlib.h>
@@ -203,6 +204,13 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     cp.m_tiles = L.m_tiles;
     cp.out_bf16 = dp.out_bf16;
     cp.units_max = (int32_t)L.units_max;
+    // pieces a full-length request gets: the forced split count, or the
+    // automatic target spread over every request and row tile; with more than
+    // 8 the 4 waves of a combine workgroup share one row
+    const int64_t pieces_hint = d->num_splits > 0
+                                    ? std::min<int64_t>(d->num_splits, d->max_pages_per_seq)
+                                    : pp.target_units / std::max<int64_t>(1, (int64_t)d->batch * L.m_tiles);
+    cp.rows_per_wg = pieces_hint > 8 ? 1 : 4;
     if (mla::launch_combine(cp, s) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }

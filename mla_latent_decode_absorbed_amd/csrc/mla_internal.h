@@ -88,6 +88,7 @@ struct CombineParams {
     float* lse;
     int32_t batch, rows, m_tiles, out_bf16;
     int32_t units_max;          // slots in ws_o / ws_lse (a split list that needs more is skipped)
+    int32_t rows_per_wg;        // 4: one wave per row; 1: the 4 waves of a workgroup share a row
 };
 
 struct MergeParams {

@@ -2182,35 +2182,55 @@ void decode_fp8_kernel(DecodeParams p) {
 // LSE merge of one row from n partials: one wave, 8 output dims per lane
 // ---------------------------------------------------------------------------
 // This lane's 8 consecutive values of a 512-value partial row (fp32 or bf16).
-__device__ __forceinline__ void load_row8(const float* row, int lane, f32x4& a, f32x4& b) {
+// One lane's 8 values of a partial row, as loaded: fp32 partials (stacked DCP
+// shard results) as two f32x4, bf16 split partials as 16 raw bytes that are
+// widened only where they are summed, so a group of 8 partials in flight holds
+// 32 registers instead of 64.
+struct RowF32 {
+    f32x4 a, b;
+};
+__device__ __forceinline__ RowF32 load_row8(const float* row, int lane) {
     const f32x4* src = (const f32x4*)row + 2 * lane;
-    a = src[0];
-    b = src[1];
+    return RowF32{src[0], src[1]};
 }
-__device__ __forceinline__ void load_row8(const __bf16* row, int lane, f32x4& a, f32x4& b) {
-    const bf16x8 v = *((const bf16x8*)row + lane);
-    a = (f32x4){(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
-    b = (f32x4){(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+__device__ __forceinline__ i32x4 load_row8(const __bf16* row, int lane) {
+    return *((const i32x4*)row + lane);
+}
+__device__ __forceinline__ void add_row8(f32x4& acc0, f32x4& acc1, float w, const RowF32& v) {
+    acc0 += w * v.a;
+    acc1 += w * v.b;
+}
+// bf16 element 2j is the low half of dword j, element 2j+1 the high half; a
+// bf16 widens to fp32 by taking its 16 bits as the top of the fp32 word.
+__device__ __forceinline__ void add_row8(f32x4& acc0, f32x4& acc1, float w, const i32x4& v) {
+    const f32x4 a = {__int_as_float(v[0] << 16), __int_as_float(v[0] & 0xffff0000),
+                     __int_as_float(v[1] << 16), __int_as_float(v[1] & 0xffff0000)};
+    const f32x4 b = {__int_as_float(v[2] << 16), __int_as_float(v[2] & 0xffff0000),
+                     __int_as_float(v[3] << 16), __int_as_float(v[3] & 0xffff0000)};
+    acc0 += w * a;
+    acc1 += w * b;
 }
 
+// Running LSE merge state of one row (this lane's 8 output values).
+struct MergeAcc {
+    float mx, wsum;
+    f32x4 acc0, acc1;
+};
+
+// Folds partials [i0, i1) of a row into the running state, 8 at a time: all
+// loads of a group (8 LSEs, the same address in every lane, and each partial
+// row's 8 values of this lane) are issued before any is used, so up to 8
+// partials cost one memory round trip.
 template <typename PartialAt>
-__device__ __forceinline__ void merge_row(int n, PartialAt at, void* out, float* lse_out, size_t orow,
-                                          int out_bf16) {
-    const int lane = threadIdx.x & 63;
-    // One pass with a running maximum, 8 partials at a time: all loads of a
-    // group (8 LSEs, the same address in every lane, and each partial row's 8
-    // values of this lane) are issued before any is used, so a row with up to
-    // 8 partials costs one memory round trip.
-    float mx = -INFINITY, wsum = 0.f;
-    f32x4 acc0 = (f32x4)0.f, acc1 = (f32x4)0.f;
-    for (int i = 0; i < n; i += 8) {
+__device__ __forceinline__ void merge_accumulate(MergeAcc& a, int i0, int i1, PartialAt at, int lane) {
+    for (int i = i0; i < i1; i += 8) {
         float li[8];
-        f32x4 v0[8], v1[8];
+        decltype(load_row8(at.out(0), 0)) v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            if (i + u < n) {
+            if (i + u < i1) {
                 li[u] = *at.lse(i + u);
-                load_row8(at.out(i + u), lane, v0[u], v1[u]);
+                v[u] = load_row8(at.out(i + u), lane);
             } else {
                 li[u] = -INFINITY;
             }
@@ -2218,31 +2238,34 @@ __device__ __forceinline__ void merge_row(int n, PartialAt at, void* out, float*
         float gm = li[0];
 #pragma unroll
         for (int u = 1; u < 8; ++u) gm = fmaxf(gm, li[u]);
-        if (gm > mx) {
+        if (gm > a.mx) {
             // rescale what is accumulated to the new maximum (nothing yet if
             // mx is still -inf)
-            const float r = mx == -INFINITY ? 0.f : __expf(mx - gm);
-            acc0 *= r;
-            acc1 *= r;
-            wsum *= r;
-            mx = gm;
+            const float r = a.mx == -INFINITY ? 0.f : __expf(a.mx - gm);
+            a.acc0 *= r;
+            a.acc1 *= r;
+            a.wsum *= r;
+            a.mx = gm;
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             // an empty partial (lse -inf) has weight 0 and its output is never
             // read into the sum (it may hold anything)
             if (li[u] != -INFINITY) {
-                const float wgt = __expf(li[u] - mx);
-                wsum += wgt;
-                acc0 += wgt * v0[u];
-                acc1 += wgt * v1[u];
+                const float wgt = __expf(li[u] - a.mx);
+                a.wsum += wgt;
+                add_row8(a.acc0, a.acc1, wgt, v[u]);
             }
         }
     }
-    const bool empty = mx == -INFINITY;
-    const float inv = empty ? 0.f : 1.f / wsum;
-    acc0 *= inv;
-    acc1 *= inv;
+}
+
+// Normalises the merged row and stores out (fp32 or bf16) and lse.
+__device__ __forceinline__ void merge_finish(const MergeAcc& a, void* out, float* lse_out, size_t orow, int out_bf16,
+                                             int lane) {
+    const bool empty = a.mx == -INFINITY;
+    const float inv = empty ? 0.f : 1.f / a.wsum;
+    const f32x4 acc0 = a.acc0 * inv, acc1 = a.acc1 * inv;
     if (out_bf16) {
         __bf16* dst = (__bf16*)out + orow * kV + 8 * lane;
         bf16x8 v;
@@ -2253,7 +2276,17 @@ __device__ __forceinline__ void merge_row(int n, PartialAt at, void* out, float*
         dst[0] = acc0;
         dst[1] = acc1;
     }
-    if (lane == 0) lse_out[orow] = empty ? -INFINITY : mx + __logf(wsum);
+    if (lane == 0) lse_out[orow] = empty ? -INFINITY : a.mx + __logf(a.wsum);
+}
+
+// LSE merge of one row from n partials, by one wave.
+template <typename PartialAt>
+__device__ __forceinline__ void merge_row(int n, PartialAt at, void* out, float* lse_out, size_t orow,
+                                          int out_bf16) {
+    const int lane = threadIdx.x & 63;
+    MergeAcc a{-INFINITY, 0.f, (f32x4)0.f, (f32x4)0.f};
+    merge_accumulate(a, 0, n, at, lane);
+    merge_finish(a, out, lse_out, orow, out_bf16, lane);
 }
 
 struct SplitPartials {
@@ -2268,32 +2301,82 @@ struct SplitPartials {
     }
 };
 
+// Zero output and -inf LSE: a request with no token (no piece under the
+// balanced plan).
+__device__ __forceinline__ void write_empty_row(const CombineParams& p, size_t grow, int lane) {
+    if (p.out_bf16) {
+        *((int4*)((__bf16*)p.out + grow * kV) + lane) = make_int4(0, 0, 0, 0);
+    } else {
+        f32x4* dst = (f32x4*)((float*)p.out + grow * kV) + 2 * lane;
+        dst[0] = (f32x4)0.f;
+        dst[1] = (f32x4)0.f;
+    }
+    if (lane == 0) p.lse[grow] = -INFINITY;
+}
+
+// Workgroups of 4 waves in one of two shapes, chosen at launch from how many
+// pieces a request is expected to have:
+//  - rows_per_wg 4: one wave per output row (few pieces: each wave has all of
+//    its row's partials in flight at once);
+//  - rows_per_wg 1: the 4 waves share one row, each folding a quarter of its
+//    pieces, and their states are merged through LDS (many pieces: 4x the
+//    loads in flight per row, and 4x the workgroups to fill the chip).
+// Either shape handles any number of pieces.
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-    const long long grow = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (grow >= (long long)p.batch * p.rows) return;
+    __shared__ f32x4 s_acc[4][2][64];
+    __shared__ float s_mw[4][2];
+    const long long total = (long long)p.batch * p.rows;
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const bool shared_row = p.rows_per_wg == 1;
+    const long long grow = shared_row ? (long long)blockIdx.x : (long long)blockIdx.x * 4 + wv;
+    if (grow >= total) return;
     const int b = (int)(grow / p.rows);
     const int r = (int)(grow - (long long)b * p.rows);
     const int S = p.req_info[kReqInfoInts * b];
+    const int first = p.req_info[kReqInfoInts * b + 1];
     if (S == 1) return;   // a single piece wrote the result directly
     if (S == 0) {
-        // an empty request under the balanced plan: no piece, no token
-        const int lane = threadIdx.x & 63;
-        if (p.out_bf16) {
-            *((int4*)((__bf16*)p.out + (size_t)grow * kV) + lane) = make_int4(0, 0, 0, 0);
-        } else {
-            f32x4* dst = (f32x4*)((float*)p.out + (size_t)grow * kV) + 2 * lane;
-            dst[0] = (f32x4)0.f;
-            dst[1] = (f32x4)0.f;
-        }
-        if (lane == 0) p.lse[grow] = -INFINITY;
+        if (!shared_row || wv == 0) write_empty_row(p, (size_t)grow, lane);
         return;
     }
-    const int first = p.req_info[kReqInfoInts * b + 1];
-    // (a plan that does not fit the workspace, e.g. one stored for another
-    // descriptor, is not followed: every slot index stays below units_max)
+    // a plan that does not fit the workspace (e.g. one stored for another
+    // descriptor) is not followed: every slot index stays below units_max
     if (S < 0 || first < 0 || (long long)(first + S) * p.m_tiles > p.units_max) return;
     SplitPartials at{(const __bf16*)p.ws_o, p.ws_lse, first, r / kMTile, p.m_tiles, r % kMTile};
-    merge_row(S, at, p.out, p.lse, (size_t)grow, p.out_bf16);
+    MergeAcc a{-INFINITY, 0.f, (f32x4)0.f, (f32x4)0.f};
+    if (!shared_row) {
+        merge_accumulate(a, 0, S, at, lane);
+        merge_finish(a, p.out, p.lse, (size_t)grow, p.out_bf16, lane);
+        return;
+    }
+    // (everything above is uniform over the workgroup, so all 4 waves reach
+    // the barrier)
+    const int per = (S + 3) / 4;
+    const int i0 = min(S, wv * per), i1 = min(S, i0 + per);
+    merge_accumulate(a, i0, i1, at, lane);
+    s_acc[wv][0][lane] = a.acc0;
+    s_acc[wv][1][lane] = a.acc1;
+    if (lane == 0) {
+        s_mw[wv][0] = a.mx;
+        s_mw[wv][1] = a.wsum;
+    }
+    __syncthreads();
+    if (wv != 0) return;
+    float mx = s_mw[0][0];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) mx = fmaxf(mx, s_mw[k][0]);
+    MergeAcc m{mx, 0.f, (f32x4)0.f, (f32x4)0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float mk = s_mw[k][0];
+        if (mk != -INFINITY) {
+            const float f = __expf(mk - mx);
+            m.wsum += f * s_mw[k][1];
+            m.acc0 += f * s_acc[k][0][lane];
+            m.acc1 += f * s_acc[k][1][lane];
+        }
+    }
+    merge_finish(m, p.out, p.lse, (size_t)grow, p.out_bf16, lane);
 }
 
 struct StackedPartials {
@@ -2357,7 +2440,8 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
     const long long rows = (long long)p.batch * p.rows;
     if (rows == 0) return hipSuccess;
     clear_stale_error();
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+    const long long wgs = p.rows_per_wg == 1 ? rows : (rows + 3) / 4;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)wgs), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -126,6 +126,7 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t) {
     need("combine", "ws_lse", p.ws_lse, (size_t)p.units_max * kMTile * 4);
     need("combine", "out", p.out, B * p.rows * kV * (p.out_bf16 ? 2 : 4));
     need("combine", "lse", p.lse, B * p.rows * 4);
+    expect("combine", p.rows_per_wg == 1 || p.rows_per_wg == 4, "rows_per_wg is neither 1 nor 4");
     ++g_launches;
     return hipSuccess;
 }

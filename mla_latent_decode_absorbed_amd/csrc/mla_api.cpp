@@ -41,6 +41,16 @@ int bf16_four_waves() {
     return v;
 }
 
+// The fp8 decode kernel: two waves per SIMD unless MLA_FP8_DECODE_KERNEL=w4
+// selects the one-wave-per-SIMD kernel (same results; kept for measurement).
+int fp8_four_waves() {
+    static const int v = [] {
+        const char* e = getenv("MLA_FP8_DECODE_KERNEL");
+        return e && strcmp(e, "w4") == 0 ? 1 : 0;
+    }();
+    return v;
+}
+
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
@@ -188,6 +198,7 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     dp.num_pages = d->num_pages;
     dp.out_bf16 = d->out_dtype == MLA_BF16;
     dp.bf16_four_waves = bf16_four_waves();
+    dp.fp8_four_waves = fp8_four_waves();
     const hipError_t de = d->kv_dtype == MLA_FP8_E4M3
                               ? mla::launch_decode_fp8(dp, (int)L.units_max, s, (hipEvent_t)ev0, (hipEvent_t)ev1)
                               : mla::launch_decode_bf16(dp, (int)L.units_max, s, (hipEvent_t)ev0, (hipEvent_t)ev1);

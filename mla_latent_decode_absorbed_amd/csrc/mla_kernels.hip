@@ -1720,6 +1720,14 @@ __device__ __forceinline__ int gather_nibble(int w) {
 
 __device__ __forceinline__ int swz8(int t) { return (t >> 2) & 3; }
 
+// max of three floats in one v_max3_f32, without the quieting v_max x, x, x
+// that fmaxf puts before values it cannot prove canonical
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ i32x8 cat8(i32x4 a, i32x4 b) {
     return (i32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
@@ -2179,6 +2187,483 @@ void decode_fp8_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// split-KV decode, fp8 cache, two waves per SIMD with split roles
+//
+// Workgroup = 8 waves over the same work items (kMTile = 128 query rows).
+// With one wave per SIMD (the kernel above) the softmax's VALU work (two e4m3
+// weight terms per logit) and the MFMAs of the same wave take turns; here the
+// two waves of a SIMD split the work of one 32-row tile (rows 32 s .. 32 s +
+// 31 on SIMD s):
+//  - wave A holds the tile's Q^T (9 k-steps, 72 VGPRs), contracts QK^T over the
+//    page (2 token tiles x 9 k-steps), runs the online softmax (reference max
+//    in whole log2 units, moved when the row max exceeds it by 5), forms the
+//    hi and lo e4m3 weight terms, and accumulates O^T for dim tiles 0 .. 2
+//    (96 dims, 48 VGPRs);
+//  - wave B accumulates O^T for dim tiles 3 .. 15 (416 dims, 208 VGPRs) and
+//    issues the page copies.
+// Each V^T fragment read from LDS feeds two MFMAs (hi and lo term).  Every
+// SIMD reads all of V (its own row tile) but only its own tile's weights: P^T
+// goes from A to B of the same SIMD, never across SIMDs.
+//
+// LDS: the 4-slot ring of pages (147,456 bytes) and one P^T buffer per tile
+// (hi 2 KB + lo 2 KB, 16 KB): the whole 160 KB, so P^T is single-buffered and
+// each page step has two barriers:
+//   T(k): page k + 1 has landed, P(k) is published, every wave is past its
+//         reads of page k - 1 (B refills that slot with page k + 3);
+//   M(k): B holds P(k) in registers, so A may overwrite it with P(k + 1).
+// Phase 1 (T(k) .. M(k)): A runs its PV share of page k (6 MFMAs, weights in
+// its registers) and QK^T of page k + 1 (18 MFMAs); B reads P(k) (the rescale
+// shift d rides in the sign bits of hi bytes 0 - 7, as in the kernel above),
+// issues the copy of page k + 3 and zeroes a sequence tail.  Phase 2 (M(k) ..
+// T(k + 1)): A runs the softmax of page k + 1 and publishes P(k + 1) while B
+// runs the PV of page k (26 MFMAs), so A's VALU work overlaps B's MFMAs.
+// Roles follow the hardware SIMD of each wave (as in the bf16 two-role kernel).
+// ---------------------------------------------------------------------------
+constexpr int kAb8PBufOff = kRingBytes;                 // [tile][hi, lo][half][lane] 16 B
+constexpr int kAb8LdsBytes = kAb8PBufOff + 4 * 4096;    // 163,840 (the whole LDS)
+static_assert(kAb8LdsBytes <= 163840, "LDS budget");
+constexpr int kAb8DimTilesA = 3;                        // O^T dim tiles of wave A (B: the other 13)
+constexpr int kAb8KAhead = 2;                           // K fragment pairs in flight during QK^T
+
+template <bool A>
+__device__ __forceinline__ void decode_fp8_ab_body(const DecodeParams& p, const Piece& w, uint8_t* lds,
+                                                   const int s, const int wv) {
+    const int lane = lane_id_fresh();
+    const int G = lane >> 5;        // MFMA k-half of this lane (0/1)
+    const int lr = lane & 31;       // query row (QK B operand, PV result) / token (QK A operand)
+    const int b = w.b;
+    const int n = min(max(p.seq_lens[b], 0), p.max_pages * kPage);
+    const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
+    const uint8_t* kvbase = (const uint8_t*)p.kv;
+    lds_u8* const ring = (lds_u8*)lds;
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+    // this tile's P^T buffer: hi at + 0, lo at + 2048, k-half tiles 1024 apart
+    lds_u8* const pbuf = (lds_u8*)lds + kAb8PBufOff + s * 4096 + lane * 16;
+    const float kv_scale = *p.kv_scale;
+    const float c_exp = p.scale_log2 * kv_scale;   // logits in log2 units per unit of q.k
+
+    const int pg_begin = w.page_begin;
+    const int pg_end = min(w.page_end, (n + kPage - 1) / kPage);
+    auto slot_ptr = [&](int k) { return ring + ((k - pg_begin) & 3) * kSlotBytes; };
+
+    // ---- page copies (B): B wave of SIMD s copies tokens 16 s .. 16 s + 15 of
+    // a page (9 blocks of 1 KB, LDS chunk q = 64 j + lane of the block holds
+    // token q / 36, position q % 36 = global chunk position ^ swz8(token)).
+    // Past the last page a copy re-reads the last one (a valid page whose data
+    // is never used), so that every step issues the same copies.
+    // (offsets recomputed per copy: B has no registers to keep nine of them)
+    auto cp_off = [&](int j) {
+        const int qc = j * 64 + lane_id_fresh();
+        const int t = qc / kRowChunks8;
+        const int pc = qc - t * kRowChunks8;
+        return t * kRowBytes8 + ((pc ^ swz8(t)) << 4);
+    };
+    const __attribute__((address_space(4))) int32_t* bt_s = (const __attribute__((address_space(4))) int32_t*)bt;
+    auto page_id = [&](int k) { return clamp_page(bt_s[k], p.num_pages); };
+    auto copy_src = [&](int k) { return k < pg_end ? k : pg_end - 1; };
+    auto copy_page = [&](int k, int pid) {
+        if (!A) {
+            const uint8_t* src = kvbase + (size_t)pid * kPageBytes8 + s * 16 * kRowBytes8;
+            const uint32_t dst = ring_addr + ((k - pg_begin) & 3) * kSlotBytes + s * 9 * 1024;
+#pragma unroll
+            for (int j = 0; j < 9; ++j) dma16(dst + j * 1024, src, (uint32_t)cp_off(j));
+        }
+    };
+
+    const int row = w.mt * kMTile + s * 32 + lr;
+    const bool row_ok = row < p.rows;
+    const int tq = row / p.heads;
+    const int unit_end = pg_end * kPage;
+    const int nvis = min(p.causal ? max(n - (p.q_len - 1 - tq), 0) : n, unit_end);
+    const int nvis_min = min(p.causal ? max(n - (p.q_len - 1), 0) : n, unit_end);
+
+    // PV A operands (V^T, 32 dims x 64 tokens) by transpose reads, as in the
+    // kernel above: dim tile D reads at tr_off[D % 2] + 64 (D / 2) (the
+    // swizzle permutes chunks inside aligned groups of 4, and 2 D + (lane / 16) % 2
+    // stays in the group of chunk 4 (D / 2))
+    int tr_off[2];
+    {
+        const int gl = lane >> 4, sl = lane & 15, kh = gl >> 1;
+        const int t0 = 4 * kh + 8 * (sl >> 3) + ((sl >> 1) & 3);
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2) {
+            const int c = 2 * d2 + (gl & 1);
+            tr_off[d2] = t0 * kRowBytes8 + ((c ^ swz8(t0)) << 4) + 8 * (sl & 1);
+        }
+    }
+    auto vfrag = [&](lds_u8* cur, int D) -> i32x8 {
+        const int off = tr_off[D & 1] + (D >> 1) * 64;
+        const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + off));
+        const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + off + 16 * kRowBytes8));
+        const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + off + 32 * kRowBytes8));
+        const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + off + 48 * kRowBytes8));
+        return (i32x8){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+    };
+
+    // O^T accumulators of this wave's dim tiles (element i: dim 32 D + 8 (i / 4)
+    // + 4 G + i % 4 of row lr), in VGPRs
+    constexpr int ND = A ? kAb8DimTilesA : 16 - kAb8DimTilesA;
+    constexpr int D0 = A ? 0 : kAb8DimTilesA;
+    f32x16 o[ND];
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+        o[j] = (f32x16)0.f;
+        asm volatile("" : "+v"(o[j]));
+    }
+    auto mfma_o = [&](int j, const i32x8& a, const i32x8& bp) {
+        asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(o[j]) : "v"(a), "v"(bp));
+    };
+    auto pv_drain = [&]() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); };
+    // o *= f, then the wait states a VALU write needs before an MFMA reads
+    // the register (the rescale sits in a branch, where the build's wait-state
+    // check does not look, and the next MFMA accumulates into o[0])
+    auto scale_o = [&](float f) {
+#pragma unroll
+        for (int j = 0; j < ND; ++j) {
+            o[j] *= f;
+            asm volatile("" : "+v"(o[j]));
+        }
+        asm volatile("s_nop 4");
+    };
+    // (A) reference max (whole log2 units) and this lane's share of the row sum
+    float m = -INFINITY, l = 0.f;
+
+    // (B) zero the rows of page k past the sequence end (they may hold
+    // anything, NaN included), so that a zero weight times V stays zero; runs
+    // once page k has landed, and a barrier orders it before any PV of k (a
+    // concurrent QK^T of k only reads masked tokens there)
+    auto zero_tail = [&](int k) {
+        const int t0 = n - k * kPage;     // callers pass pages holding >= 1 token
+        if (t0 >= kPage) return;
+        lds_u8* cur = slot_ptr(k);
+        for (int idx = s * 64 + lane; idx < (kPage - t0) * kRowChunks8; idx += 256) {
+            const int t = t0 + idx / kRowChunks8;
+            const int c = idx % kRowChunks8;
+            *(lds_i32x4*)(cur + t * kRowBytes8 + c * 16) = (i32x4)0;
+        }
+    };
+
+    if constexpr (A) {
+        // Q^T fragments: k-step ks covers dims 64 ks .. + 63; lane holds dims 64 ks + 32 G .. + 31
+        i32x8 qf[9];
+        {
+            const uint8_t* qr = (const uint8_t*)p.q + ((size_t)b * p.rows + min(row, p.rows - 1)) * kQK + 32 * G;
+#pragma unroll
+            for (int ks = 0; ks < 9; ++ks) {
+                const i32x4 lo = *(const i32x4*)(qr + 64 * ks);
+                const i32x4 hi = *(const i32x4*)(qr + 64 * ks + 16);
+                qf[ks] = cat8(lo, hi);
+            }
+        }
+        // QK A fragments: token 32 tau + lr, chunks 4 ks + 2 G + e at positions
+        // 4 ks + ((2 G + e) ^ swz8(lr))
+        int qk_off[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) qk_off[e] = lr * kRowBytes8 + (((2 * G + e) ^ swz8(lr)) << 4);
+        auto kfrag = [&](lds_u8* cur, int tau, int ks) -> i32x8 {
+            const i32x4 lo = *(const lds_i32x4*)(cur + qk_off[0] + tau * 32 * kRowBytes8 + 64 * ks);
+            const i32x4 hi = *(const lds_i32x4*)(cur + qk_off[1] + tau * 32 * kRowBytes8 + 64 * ks);
+            return cat8(lo, hi);
+        };
+        // S^T of page k: two token tiles, 9 k-steps each, as two interleaved
+        // accumulation chains; K fragments read one k-step ahead (two would
+        // not fit beside the query, the accumulators and both weight sets);
+        // between(ks) runs after MFMA pair ks
+        auto qk = [&](int k, f32x16& s0, f32x16& s1, auto&& between) {
+            lds_u8* cur = slot_ptr(k);
+            constexpr int KA = kAb8KAhead;
+            i32x8 kf0[KA], kf1[KA];
+#pragma unroll
+            for (int ks = 0; ks < KA; ++ks) {
+                kf0[ks] = kfrag(cur, 0, ks);
+                kf1[ks] = kfrag(cur, 1, ks);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 9; ++ks) {
+                const i32x8 a0 = kf0[ks % KA], a1 = kf1[ks % KA];
+                if (ks + KA < 9) {
+                    kf0[ks % KA] = kfrag(cur, 0, ks + KA);
+                    kf1[ks % KA] = kfrag(cur, 1, ks + KA);
+                }
+                if (ks == 0) {
+                    asm volatile("s_nop 3\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0"
+                                 : "=&v"(s0) : "v"(a0), "v"(qf[ks]));
+                    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0"
+                                 : "=&v"(s1) : "v"(a1), "v"(qf[ks]));
+                } else {
+                    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+                                 : "+v"(s0) : "v"(a0), "v"(qf[ks]));
+                    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
+                                 : "+v"(s1) : "v"(a1), "v"(qf[ks]));
+                }
+                between(ks);
+            }
+            asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+        };
+        // element i of token tile tau is token 64 k + 32 tau + 8 (i / 4) + 4 G + i % 4
+        auto mask_s = [&](int k, f32x16& s0, f32x16& s1) {
+            const int lim = nvis - k * kPage - 4 * G;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int t = 8 * (i >> 2) + (i & 3);
+                s0[i] = t < lim ? s0[i] : -INFINITY;
+                s1[i] = t + 32 < lim ? s1[i] : -INFINITY;
+            }
+        };
+        auto needs_mask = [&](int k) { return k * kPage + kPage > nvis_min; };
+
+        // Online softmax of one page for this lane's row (32 logits, 16 of each
+        // token tile), written for latency (nothing runs between its
+        // instructions but B's MFMAs): tree reductions for the row max and the
+        // row sum, independent exp2 and e4m3 conversions.  Produces the hi and
+        // lo e4m3 weight terms (bytes 0-15 from tile 0, 16-31 from tile 1) and
+        // d_out, the rescale shift of everything accumulated so far (0 when
+        // unchanged); publishes them (d in the sign bits of hi bytes 0 - 7; the
+        // own operands stay clean).
+        auto softmax_page = [&](f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out) {
+            // row max as a v_max3 tree (fmaxf would first quiet every MFMA
+            // result with a v_max x, x, x of its own)
+            float q11[11];
+#pragma unroll
+            for (int g = 0; g < 5; ++g) {
+                q11[g] = max3f(s0[3 * g], s0[3 * g + 1], s0[3 * g + 2]);
+                q11[5 + g] = max3f(s1[3 * g], s1[3 * g + 1], s1[3 * g + 2]);
+            }
+            q11[10] = max3f(s0[15], s1[15], q11[0]);
+            const float r0 = max3f(q11[1], q11[2], q11[3]), r1 = max3f(q11[4], q11[5], q11[6]),
+                        r2 = max3f(q11[7], q11[8], q11[9]);
+            const float mx = pair_max(max3f(r0, r1, max3f(r2, q11[10], q11[10]))) * c_exp;
+            const bool grow = mx > m + kRescaleSlack8;
+            const float m_new = grow ? __builtin_ceilf(mx) : m;
+            // (nothing has been accumulated while m is still -inf: no rescale)
+            d_out = grow && m != -INFINITY ? (int)fminf(m_new - m, 255.f) : 0;
+            m = m_new;
+            const float mneg = m == -INFINITY ? 0.f : kWeightOffset8 - m;
+            float ps[8];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s0[i] = __builtin_fmaf(s0[i], c_exp, mneg);
+                s1[i] = __builtin_fmaf(s1[i], c_exp, mneg);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s0[i] = __builtin_amdgcn_exp2f(s0[i]);
+                s1[i] = __builtin_amdgcn_exp2f(s1[i]);
+            }
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                ps[g] = (s0[4 * g] + s0[4 * g + 1]) + (s0[4 * g + 2] + s0[4 * g + 3]);
+                ps[4 + g] = (s1[4 * g] + s1[4 * g + 1]) + (s1[4 * g + 2] + s1[4 * g + 3]);
+            }
+            l = l * __builtin_ldexpf(1.f, -d_out) +
+                (((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7])));
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const f32x16& sv = r < 4 ? s0 : s1;
+                const int i0 = 4 * (r & 3);
+                const int hw = pack_e4m3(sv[i0], sv[i0 + 1], sv[i0 + 2], sv[i0 + 3]);
+                const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
+                const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
+                ph[r] = hw;
+                pl[r] = pack_e4m3(sv[i0] - h01[0], sv[i0 + 1] - h01[1], sv[i0 + 2] - h23[0], sv[i0 + 3] - h23[1]);
+            }
+            const int e0 = ph[0] | spread_nibble(d_out), e1 = ph[1] | spread_nibble(d_out >> 4);
+            *(lds_i32x4*)pbuf = (i32x4){e0, e1, ph[2], ph[3]};
+            *(lds_i32x4*)(pbuf + 1024) = (i32x4){ph[4], ph[5], ph[6], ph[7]};
+            *(lds_i32x4*)(pbuf + 2048) = (i32x4){pl[0], pl[1], pl[2], pl[3]};
+            *(lds_i32x4*)(pbuf + 3072) = (i32x4){pl[4], pl[5], pl[6], pl[7]};
+        };
+
+        if (pg_begin < pg_end) {
+            i32x8 ph_cur, pl_cur;
+            int d_cur;
+            // T(pre): the first page has landed; S and P of it
+            lds_sync();
+            {
+                f32x16 s0, s1;
+                qk(pg_begin, s0, s1, [&](int) {});
+                if (needs_mask(pg_begin)) mask_s(pg_begin, s0, s1);
+                softmax_page(s0, s1, ph_cur, pl_cur, d_cur);
+            }
+            for (int k = pg_begin;; ++k) {
+                lds_sync();   // T(k)
+                const bool more = k + 1 < pg_end;
+                if (__builtin_expect(__any(d_cur != 0), 0)) {
+                    pv_drain();
+                    scale_o(__builtin_ldexpf(1.f, -d_cur));
+                }
+                // phase 1: PV share of page k (its weights are in registers),
+                // then S of page k + 1 (the matrix core is A's alone)
+                {
+                    lds_u8* cur = slot_ptr(k);
+                    i32x8 vf = vfrag(cur, 0);
+#pragma unroll
+                    for (int j = 0; j < ND; ++j) {
+                        const i32x8 a = vf;
+                        if (j + 1 < ND) vf = vfrag(cur, j + 1);
+                        mfma_o(j, a, ph_cur);
+                        mfma_o(j, a, pl_cur);
+                    }
+                }
+                f32x16 s0, s1;
+                if (more) qk(k + 1, s0, s1, [&](int) {});
+                lds_sync();   // M(k)
+                if (!more) break;
+                // phase 2: the softmax of page k + 1 (B's PV of page k keeps the
+                // matrix core busy meanwhile); its weights replace those of page k
+                if (needs_mask(k + 1)) mask_s(k + 1, s0, s1);
+                softmax_page(s0, s1, ph_cur, pl_cur, d_cur);
+                // the wait states between these VALU writes and the next step's MFMAs
+                asm volatile("s_nop 1" : "+v"(ph_cur), "+v"(pl_cur));
+            }
+        }
+    } else {
+        if (pg_begin < pg_end) {
+            // prologue: the first three pages (re-reads past the end), T(pre)
+            // once the first has landed
+            const int pid0 = page_id(pg_begin);
+            const int pid1 = page_id(copy_src(pg_begin + 1));
+            const int pid2 = page_id(copy_src(pg_begin + 2));
+            copy_page(pg_begin, pid0);
+            copy_page(pg_begin + 1, pid1);
+            copy_page(pg_begin + 2, pid2);
+            int pid_next = page_id(copy_src(pg_begin + 3));
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));
+            lds_sync();   // T(pre)
+            zero_tail(pg_begin);
+            for (int k = pg_begin;; ++k) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));   // page k + 1 has landed
+                lds_sync();   // T(k)
+                const bool more = k + 1 < pg_end;
+                // P(k) first (its latency overlaps the copy issue)
+                lds_u8* cur = slot_ptr(k);
+                const i32x4 h0 = *(const lds_i32x4*)pbuf;
+                const i32x4 h1 = *(const lds_i32x4*)(pbuf + 1024);
+                const i32x4 l0 = *(const lds_i32x4*)(pbuf + 2048);
+                const i32x4 l1 = *(const lds_i32x4*)(pbuf + 3072);
+                copy_page(k + 3, pid_next);
+                pid_next = page_id(copy_src(k + 4));
+                i32x8 vf[2];
+                vf[0] = vfrag(cur, D0);
+                vf[1] = vfrag(cur, D0 + 1);
+                const int d = gather_nibble(h0[0]) | (gather_nibble(h0[1]) << 4);
+                i32x8 ph = (i32x8){h0[0] & 0x7f7f7f7f, h0[1] & 0x7f7f7f7f, h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+                i32x8 pl = cat8(l0, l1);
+                if (__builtin_expect(__any(d != 0), 0)) {
+                    pv_drain();
+                    scale_o(__builtin_ldexpf(1.f, -d));
+                }
+                if (more) zero_tail(k + 1);
+                // M(k): P(k) is in registers (the wait covers the reads), A may
+                // overwrite it
+                lds_sync();
+                // the wait states between the VALU writes of ph and an MFMA reading it
+                asm volatile("s_nop 1" : "+v"(ph), "+v"(pl));
+#pragma unroll
+                for (int j = 0; j < ND; ++j) {
+                    const i32x8 a = vf[j & 1];
+                    mfma_o(j, a, ph);
+                    mfma_o(j, a, pl);
+                    if (j + 2 < ND) vf[j & 1] = vfrag(cur, D0 + j + 2);
+                }
+                if (!more) break;
+            }
+        }
+    }
+
+    // ---- epilogue: o = kv_scale O / l for this wave's dim tiles of its row
+    //      tile; lse = ln(sum exp(s)) for A's rows.
+    // No copy may still be writing this workgroup's LDS when it is reused.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    pv_drain();
+    const float l_row = pair_sum(l);
+    __syncthreads();                      // every wave is done with the ring and the P buffers
+    lds_f32* const lbuf = (lds_f32*)(lds + kAb8PBufOff);   // [4 tiles][32 rows]: row sums
+    if (A && G == 0) lbuf[s * 32 + lr] = l_row;
+    __syncthreads();
+    const float lt = lbuf[s * 32 + lr];
+    const float inv = lt > 0.f ? kv_scale / lt : 0.f;
+    // Rows leave through the idle ring: per half (64 rows, the tiles of SIMDs
+    // 2 hf and 2 hf + 1) each wave writes its dims of its rows, scaled, as
+    // fp32 (a single piece to an fp32 output) or bf16 (a bf16 output, or a
+    // split partial), into rows of 512 e + 16 bytes; then the workgroup stores
+    // whole contiguous row pieces, 16 bytes per lane.
+    {
+        const int tid = wv * 64 + lane;
+        const bool f32 = w.nsplit == 1 && !p.out_bf16;
+        const int e = f32 ? 4 : 2;
+        const int st_row = kV * e + 16;
+        const int row_chunks = kV * e / 16;
+        uint8_t* gbase = w.nsplit > 1 ? (uint8_t*)p.ws_o + (size_t)w.slot * kMTile * kV * 2
+                                      : (uint8_t*)p.out + ((size_t)b * p.rows + (size_t)w.mt * kMTile) * kV * e;
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            if ((s >> 1) == hf) {
+                lds_u8* srow0 = ring + (32 * (s & 1) + lr) * st_row;
+#pragma unroll
+                for (int j = 0; j < ND; ++j) {
+                    lds_u8* srow = srow0 + e * (32 * (D0 + j) + 4 * G);
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x4 v = (f32x4){o[j][4 * q4], o[j][4 * q4 + 1], o[j][4 * q4 + 2], o[j][4 * q4 + 3]} * inv;
+                        if (f32) {
+                            *(__attribute__((address_space(3))) f32x4*)(srow + 4 * 8 * q4) = v;
+                        } else {
+                            __bf16 __attribute__((ext_vector_type(4))) h;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) h[i] = (__bf16)v[i];
+                            *(lds_i16x4*)(srow + 2 * 8 * q4) = __builtin_bit_cast(i16x4, h);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            for (int i = tid; i < 64 * row_chunks; i += 512) {
+                const int rl = i / row_chunks, c = i - rl * row_chunks;
+                if (w.mt * kMTile + 64 * hf + rl < p.rows)
+                    *(i32x4*)(gbase + (size_t)(64 * hf + rl) * kV * e + 16 * c) =
+                        *(const __attribute__((address_space(3))) i32x4*)(ring + rl * st_row + 16 * c);
+            }
+            __syncthreads();
+        }
+    }
+    if (A && row_ok && G == 0) {
+        // l sums exp2(s c - m + 3): ln sum exp = (m - 3 + log2 l) ln 2
+        const float lse = l_row > 0.f ? (m - kWeightOffset8 + __log2f(l_row)) * kLn2 : -INFINITY;
+        if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
+        else p.ws_lse[(size_t)w.slot * kMTile + (row - w.mt * kMTile)] = lse;
+    }
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void decode_fp8_ab_kernel(DecodeParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kAb8LdsBytes];
+    const WorkItem w = decode_work_item<512>(p, lds);
+    if (w.b < 0) return;
+    // roles as in the bf16 two-role kernel
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sid = __builtin_amdgcn_readfirstlane(hw_simd_id());
+    lds_int* tab = (lds_int*)lds;
+    if ((threadIdx.x & 63) == 0) tab[wv] = sid;
+    __syncthreads();
+    int cnt0 = 0, cnt1 = 0, cnt2 = 0, cnt3 = 0, lower = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int si = __builtin_amdgcn_readfirstlane(tab[i]);
+        cnt0 += si == 0; cnt1 += si == 1; cnt2 += si == 2; cnt3 += si == 3;
+        lower += (si == sid && i < wv) ? 1 : 0;
+    }
+    __syncthreads();   // the table's LDS is reused for the pages
+    const bool by_hw = cnt0 == 2 && cnt1 == 2 && cnt2 == 2 && cnt3 == 2;
+    const bool is_a = by_hw ? lower == 0 : wv < 4;
+    const int s = by_hw ? sid : (wv & 3);
+    for_each_piece<true>(p, w, [&](const Piece& pc) {
+        if (is_a) decode_fp8_ab_body<true>(p, pc, lds, s, wv);
+        else decode_fp8_ab_body<false>(p, pc, lds, s, wv);
+    });
+}
+
+// ---------------------------------------------------------------------------
 // LSE merge of one row from n partials: one wave, 8 output dims per lane
 // ---------------------------------------------------------------------------
 // This lane's 8 consecutive values of a 512-value partial row (fp32 or bf16).
@@ -2429,7 +2914,8 @@ hipError_t launch_decode_fp8(const DecodeParams& p, int units, hipStream_t strea
         if (e != hipSuccess) return e;
     }
     clear_stale_error();
-    hipLaunchKernelGGL(decode_fp8_kernel, dim3(units), dim3(256), 0, stream, p);
+    if (p.fp8_four_waves) hipLaunchKernelGGL(decode_fp8_kernel, dim3(units), dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(decode_fp8_ab_kernel, dim3(units), dim3(512), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_after) return hipEventRecord(ev_after, stream);

@@ -12,7 +12,7 @@ verifies the final instruction stream instead of trusting that:
     VALU instruction before that;
 
 where `s_nop N` counts N + 1 wait states and every other instruction one.
-Used by build.py on the device assembly of the kernels source.
+Used by build.py on every kernel in the device assembly of the kernels source.
 
 Limits of the check (what it does not prove):
   * it scans each function's text straight backwards from an instruction and
@@ -106,15 +106,25 @@ def check_function(lines, name=""):
     return bad
 
 
-def check_asm(text: str, kernels=("decode_bf16_kernel", "decode_fp8_kernel")):
-    """Check the named kernels in a device assembly listing; returns violations."""
+def kernel_names(text: str):
+    """Symbols of every kernel in a device assembly listing (.amdhsa_kernel)."""
+    return re.findall(r"^\s*\.amdhsa_kernel\s+(\S+)", text, flags=re.M)
+
+
+def check_asm(text: str, kernels=None):
+    """Check the named kernels (default: every kernel of the listing) in a
+    device assembly listing; returns violations."""
     lines = text.splitlines()
     bad = []
+    if kernels is None:
+        kernels = kernel_names(text)
+        if not kernels:
+            return ["no kernel found in the assembly"]
     for kname in kernels:
         start = None
         for i, l in enumerate(lines):
-            head = l.split(";")[0].rstrip()
-            if kname in head and head.endswith(":") and not head.startswith("."):
+            head = l.split(";")[0].strip()
+            if head == kname + ":":
                 start = i
                 break
         if start is None:

@@ -2,7 +2,7 @@
 catch around MFMAs the compiler cannot see, and accepts correctly spaced code."""
 import pytest
 
-from mla_latent_decode_absorbed_amd.isa_check import check_function
+from mla_latent_decode_absorbed_amd.isa_check import check_asm, check_function
 
 pytestmark = pytest.mark.cpu
 
@@ -57,3 +57,25 @@ def test_mfma_result_read_by_valu_needs_eighteen_wait_states():
         s_nop 7
         v_add_f32_e32 v1, v10, v11
     """) == []
+
+
+def test_every_kernel_of_a_listing_is_checked():
+    """check_asm scans every kernel the listing declares, also one whose name
+    extends another's, and reports the one with the hazard."""
+    listing = """
+_Z6decodev:
+        v_mov_b32_e32 v30, v40
+        v_mfma_f32_32x32x16_bf16 a[0:15], v[2:5], v[6:9], a[0:15]
+        s_endpgm
+_Z9decode_abv:
+        v_and_b32_e32 v6, 0x7f7f7f7f, v6
+        v_mfma_f32_32x32x64_f8f6f4 v[10:25], v[2:9], v[6:13], v[10:25]
+        s_endpgm
+        .amdhsa_kernel _Z6decodev
+        .end_amdhsa_kernel
+        .amdhsa_kernel _Z9decode_abv
+        .end_amdhsa_kernel
+"""
+    bad = check_asm(listing)
+    assert len(bad) == 1 and bad[0].startswith("_Z9decode_abv") and "VALU write" in bad[0]
+    assert check_asm(listing, kernels=("_Z6decodev",)) == []

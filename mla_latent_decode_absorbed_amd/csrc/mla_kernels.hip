@@ -2211,12 +2211,13 @@ void decode_fp8_kernel(DecodeParams p) {
 //   T(k): page k + 1 has landed, P(k) is published, every wave is past its
 //         reads of page k - 1 (B refills that slot with page k + 3);
 //   M(k): B holds P(k) in registers, so A may overwrite it with P(k + 1).
-// Phase 1 (T(k) .. M(k)): A runs its PV share of page k (6 MFMAs, weights in
-// its registers) and QK^T of page k + 1 (18 MFMAs); B reads P(k) (the rescale
-// shift d rides in the sign bits of hi bytes 0 - 7, as in the kernel above),
-// issues the copy of page k + 3 and zeroes a sequence tail.  Phase 2 (M(k) ..
-// T(k + 1)): A runs the softmax of page k + 1 and publishes P(k + 1) while B
-// runs the PV of page k (26 MFMAs), so A's VALU work overlaps B's MFMAs.
+// Phase 1 (T(k) .. M(k)): A contracts QK^T of page k + 1 (18 MFMAs); B reads
+// P(k) (the rescale shift d rides in the sign bits of hi bytes 0 - 7, as in
+// the kernel above), issues the copy of page k + 3 and zeroes a sequence tail.
+// Phase 2 (M(k) .. T(k + 1)): A runs the softmax of page k + 1, with its PV
+// share of page k (6 MFMAs, the weights of page k still in its registers)
+// issued between the softmax's pieces, and publishes P(k + 1); B runs the PV
+// of page k (26 MFMAs), so A's VALU work overlaps the MFMAs.
 // Roles follow the hardware SIMD of each wave (as in the bf16 two-role kernel).
 // ---------------------------------------------------------------------------
 constexpr int kAb8PBufOff = kRingBytes;                 // [tile][hi, lo][half][lane] 16 B
@@ -2313,6 +2314,7 @@ __device__ __forceinline__ void decode_fp8_ab_body(const DecodeParams& p, const 
     auto mfma_o = [&](int j, const i32x8& a, const i32x8& bp) {
         asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(o[j]) : "v"(a), "v"(bp));
     };
+
     auto pv_drain = [&]() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); };
     // o *= f, then the wait states a VALU write needs before an MFMA reads
     // the register (the rescale sits in a branch, where the build's wait-state
@@ -2366,8 +2368,7 @@ __device__ __forceinline__ void decode_fp8_ab_body(const DecodeParams& p, const 
             return cat8(lo, hi);
         };
         // S^T of page k: two token tiles, 9 k-steps each, as two interleaved
-        // accumulation chains; K fragments read one k-step ahead (two would
-        // not fit beside the query, the accumulators and both weight sets);
+        // accumulation chains; K fragments read kAb8KAhead k-steps ahead;
         // between(ks) runs after MFMA pair ks
         auto qk = [&](int k, f32x16& s0, f32x16& s1, auto&& between) {
             lds_u8* cur = slot_ptr(k);
@@ -2420,7 +2421,7 @@ __device__ __forceinline__ void decode_fp8_ab_body(const DecodeParams& p, const 
         // d_out, the rescale shift of everything accumulated so far (0 when
         // unchanged); publishes them (d in the sign bits of hi bytes 0 - 7; the
         // own operands stay clean).
-        auto softmax_page = [&](f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out) {
+        auto softmax_page = [&](f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out, auto&& between) {
             // row max as a v_max3 tree (fmaxf would first quiet every MFMA
             // result with a v_max x, x, x of its own)
             float q11[11];
@@ -2439,17 +2440,20 @@ __device__ __forceinline__ void decode_fp8_ab_body(const DecodeParams& p, const 
             d_out = grow && m != -INFINITY ? (int)fminf(m_new - m, 255.f) : 0;
             m = m_new;
             const float mneg = m == -INFINITY ? 0.f : kWeightOffset8 - m;
+            between(0);
             float ps[8];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 s0[i] = __builtin_fmaf(s0[i], c_exp, mneg);
                 s1[i] = __builtin_fmaf(s1[i], c_exp, mneg);
             }
+            between(1);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 s0[i] = __builtin_amdgcn_exp2f(s0[i]);
                 s1[i] = __builtin_amdgcn_exp2f(s1[i]);
             }
+            between(2);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 ps[g] = (s0[4 * g] + s0[4 * g + 1]) + (s0[4 * g + 2] + s0[4 * g + 3]);
@@ -2477,13 +2481,22 @@ __device__ __forceinline__ void decode_fp8_ab_body(const DecodeParams& p, const 
         if (pg_begin < pg_end) {
             i32x8 ph_cur, pl_cur;
             int d_cur;
+            // both terms of one dim tile of the PV share in one statement,
+            // between the wait states after a VALU write of the accumulator
+            // (the compiler may copy it) and those before a VALU write may
+            // reuse the operand registers
+            auto pv_tile = [&](int j, const i32x8& a) {
+                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0\n\t"
+                             "v_mfma_f32_32x32x64_f8f6f4 %0, %1, %3, %0\n\ts_nop 3"
+                             : "+v"(o[j]) : "v"(a), "v"(ph_cur), "v"(pl_cur));
+            };
             // T(pre): the first page has landed; S and P of it
             lds_sync();
             {
                 f32x16 s0, s1;
                 qk(pg_begin, s0, s1, [&](int) {});
                 if (needs_mask(pg_begin)) mask_s(pg_begin, s0, s1);
-                softmax_page(s0, s1, ph_cur, pl_cur, d_cur);
+                softmax_page(s0, s1, ph_cur, pl_cur, d_cur, [&](int) {});
             }
             for (int k = pg_begin;; ++k) {
                 lds_sync();   // T(k)
@@ -2499,10 +2512,8 @@ __device__ __forceinline__ void decode_fp8_ab_body(const DecodeParams& p, const 
                     i32x8 vf = vfrag(cur, 0);
 #pragma unroll
                     for (int j = 0; j < ND; ++j) {
-                        const i32x8 a = vf;
+                        pv_tile(j, vf);
                         if (j + 1 < ND) vf = vfrag(cur, j + 1);
-                        mfma_o(j, a, ph_cur);
-                        mfma_o(j, a, pl_cur);
                     }
                 }
                 f32x16 s0, s1;
@@ -2512,7 +2523,7 @@ __device__ __forceinline__ void decode_fp8_ab_body(const DecodeParams& p, const 
                 // phase 2: the softmax of page k + 1 (B's PV of page k keeps the
                 // matrix core busy meanwhile); its weights replace those of page k
                 if (needs_mask(k + 1)) mask_s(k + 1, s0, s1);
-                softmax_page(s0, s1, ph_cur, pl_cur, d_cur);
+                softmax_page(s0, s1, ph_cur, pl_cur, d_cur, [&](int) {});
                 // the wait states between these VALU writes and the next step's MFMAs
                 asm volatile("s_nop 1" : "+v"(ph_cur), "+v"(pl_cur));
             }

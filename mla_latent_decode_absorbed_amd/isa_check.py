@@ -7,9 +7,14 @@ around them; the kernels insert what they know they need, and this check
 verifies the final instruction stream instead of trusting that:
 
   * VALU write of a VGPR/AGPR -> MFMA read of it: at least 2 wait states;
-  * MFMA write -> VALU (or v_accvgpr_read) read of the result: at least 18
-    wait states (a 16-pass XDL instruction), and no MFMA result is read by a
-    VALU instruction before that;
+  * MFMA write -> VALU (or v_accvgpr_read) read of the result, or a VALU
+    write of the same registers: at least 18 wait states (a 16-pass XDL
+    instruction);
+  * f8f6f4 MFMA read of a source (A, B or C operand) -> VALU write of it: at
+    least 4 wait states (measured: a VALU write one wait state after such an
+    MFMA gave wrong results, three and more did not; bf16 MFMAs read their
+    operands at issue, and the kernels overwrite them right after without
+    error);
 
 where `s_nop N` counts N + 1 wait states and every other instruction one.
 Used by build.py on every kernel in the device assembly of the kernels source.
@@ -19,10 +24,9 @@ Limits of the check (what it does not prove):
     ignores control flow, so a hazard across a branch or a loop back edge
     (a read at the top of a loop of a result written at its bottom) is not
     seen;
-  * it treats only VALU instructions (v_* other than MFMAs) as readers of an
-    MFMA result: DS / buffer / global stores that read an MFMA destination,
-    and write-after-read / write-after-write hazards on an MFMA's srcC or
-    vdst, are not modelled;
+  * it treats only VALU instructions (v_* other than MFMAs) as readers or
+    writers: DS / buffer / global stores that read an MFMA destination, and
+    loads that overwrite an MFMA operand, are not modelled;
   * it applies one threshold (18) to every MFMA, including the 16-pass
     v_mfma_f32_32x32x64_f8f6f4.
 The kernels therefore do not rely on it alone: every inline-assembly MFMA
@@ -36,6 +40,7 @@ import sys
 
 VALU_TO_MFMA = 2
 MFMA_TO_VALU = 18
+MFMA_SRC_TO_VALU_WRITE = 4
 
 
 def _regs(tok: str):
@@ -93,14 +98,20 @@ def check_function(lines, name=""):
             reads = set().union(*[_regs(o) for o in ops[1:]])
             if op.startswith("v_accvgpr_read"):
                 reads = _regs(ops[1])
-            if not reads:
-                continue
+            writes = _regs(ops[0])
             ws, j = 0, i - 1
-            while j >= 0 and ws < MFMA_TO_VALU:
+            while j >= 0 and ws < max(MFMA_TO_VALU, MFMA_SRC_TO_VALU_WRITE):
                 pop, pops = _operands(ins[j])
-                if pop.startswith("v_mfma") and pops and (_regs(pops[0]) & reads):
-                    bad.append(f"{name}: MFMA {ins[j]!r} -> VALU {line!r} after {ws} wait states")
-                    break
+                if pop.startswith("v_mfma") and pops:
+                    dst = _regs(pops[0])
+                    srcs = set().union(*[_regs(o) for o in pops[1:4]]) if len(pops) >= 4 else set()
+                    if ws < MFMA_TO_VALU and dst & (reads | writes):
+                        what = "reads" if dst & reads else "overwrites"
+                        bad.append(f"{name}: MFMA {ins[j]!r} -> VALU {line!r} {what} its result after {ws} wait states")
+                        break
+                    if ws < MFMA_SRC_TO_VALU_WRITE and "f8f6f4" in pop and srcs & writes:
+                        bad.append(f"{name}: MFMA {ins[j]!r} -> VALU {line!r} overwrites a source after {ws} wait states")
+                        break
                 ws += _ws(ins[j])
                 j -= 1
     return bad

@@ -626,6 +626,13 @@ __device__ __forceinline__ float pair_max(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// max of three floats in one v_max3_f32, without the quieting v_max x, x, x
+// that fmaxf puts before values it cannot prove canonical
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
 __device__ __forceinline__ float pair_sum(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -1457,9 +1464,11 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
 #pragma unroll
             for (int i = 0; i < 16; ++i) sacc[i] = (8 * (i >> 2) + (i & 3)) < lim ? sacc[i] : -INFINITY;
         }
-        float mx = sacc[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+        // (a v_max3 tree: fmaxf would first quiet every MFMA result)
+        const float q0 = max3f(sacc[0], sacc[1], sacc[2]), q1 = max3f(sacc[3], sacc[4], sacc[5]),
+                    q2 = max3f(sacc[6], sacc[7], sacc[8]), q3 = max3f(sacc[9], sacc[10], sacc[11]),
+                    q4 = max3f(sacc[12], sacc[13], sacc[14]);
+        float mx = max3f(max3f(q0, q1, q2), max3f(q3, q4, sacc[15]), q0);
         mx = pair_max(mx) * c_log2;
         const bool grow = mx > m + kRescaleSlackAb;
         const float m_new = grow ? __builtin_ceilf(mx) : m;
@@ -1720,13 +1729,6 @@ __device__ __forceinline__ int gather_nibble(int w) {
 
 __device__ __forceinline__ int swz8(int t) { return (t >> 2) & 3; }
 
-// max of three floats in one v_max3_f32, without the quieting v_max x, x, x
-// that fmaxf puts before values it cannot prove canonical
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
 
 __device__ __forceinline__ i32x8 cat8(i32x4 a, i32x4 b) {
     return (i32x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};

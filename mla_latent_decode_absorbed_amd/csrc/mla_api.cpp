@@ -123,6 +123,14 @@ mla::PlanParams plan_params(const mla_decode_desc* d, const WorkspaceLayout& L) 
     pp.units_max = (int32_t)L.units_max;
     // the fp8 kernel runs multi-piece work items (the balanced plan for ragged batches)
     pp.balance = d->kv_dtype == MLA_FP8_E4M3 ? 1 : 0;
+    // forced splits that make more work items than one round of workgroups
+    // may be grouped (consecutive splits of a request in one workgroup): the
+    // two-role bf16 kernel has an instance for such lists
+    const int64_t per_req = d->num_splits > 0 ? std::min<int64_t>(d->num_splits, d->max_pages_per_seq) : 0;
+    pp.group_ok = d->kv_dtype == MLA_BF16 && !bf16_four_waves() && per_req > 1 &&
+                          (int64_t)d->batch * per_req * L.m_tiles > pp.target_units
+                      ? 1
+                      : 0;
     return pp;
 }
 

@@ -23,7 +23,10 @@ constexpr int kFusedPlanMax = 256; // batches up to this size are planned inside
 // into the following non-empty requests (one piece per request touched).
 // piece is the partial-result index of the first piece (the following ones
 // count on from it) and nsplit the number of pieces request b is cut into
-// (1: the piece writes the request's result itself).  b < 0 marks an empty slot.
+// (1: the piece writes the request's result itself).  With chunk == 0 and
+// g0 > 1 the item is a group of g0 consecutive splits of request b (forced
+// split counts, each split ceil(pages / nsplit) pages but the last), pieces
+// piece .. piece + g0 - 1.  b < 0 marks an empty slot.
 struct WorkItem {
     int32_t b, mt, piece, page_begin, npages, nsplit, g0, chunk;
 };
@@ -31,8 +34,10 @@ struct WorkItem {
 // One piece of a workgroup's work: rows [mt*kMTile, +kMTile) of request b
 // over pages [page_begin, page_end); nsplit == 1 writes out/lse directly,
 // otherwise the partial goes to workspace slot `slot` (= piece * m_tiles + mt).
+// sub > 0: a later split of a group (same request and rows as the one before).
 struct Piece {
     int32_t b, mt, page_begin, page_end, nsplit, slot;
+    int32_t sub;                // index of this split within its work item's group (0: the first)
 };
 
 // Per-request planner output, int32 [batch][kReqInfoInts]: pieces the request
@@ -43,6 +48,7 @@ constexpr int kReqInfoInts = 4;
 struct PlanParams {
     int32_t batch, rows, m_tiles, max_pages, num_splits, target_units, min_chunk, units_max;
     int32_t balance;            // 1: the balanced plan may be chosen (the kernel runs multi-piece items)
+    int32_t group_ok;           // 1: forced splits may be grouped (the kernel instance runs groups)
 };
 
 struct DecodeParams {

@@ -109,7 +109,27 @@ struct PlanResult {
     int k_total;         // kv-units in all
     int balanced;        // > 0: the balanced plan, with this many pages per kv-unit
     int total_pages;     // all requests' pages (balanced plan)
+    int group;           // kv-units per work item: consecutive splits of one request (>= 1)
 };
+
+// Forced splits (num_splits > 0) that cut every request into the same number
+// S of splits and make more work items than one round of workgroups: each
+// item takes `group` consecutive splits of one request (the smallest divisor
+// of S that brings the items within one round), so that a workgroup pays its
+// fixed cost (query tile, planning) once per group.  Only when the caller
+// launches a kernel instance that runs groups (PlanParams::group_ok).
+__device__ __forceinline__ int split_group(const PlanParams& p, int k_total, int longest) {
+    if (!p.group_ok || p.num_splits <= 0 || p.balance || p.batch <= 0) return 1;
+    const int S = min(p.num_splits, max(longest, 1));
+    if ((long long)k_total != (long long)p.batch * S) return 1;   // some request has fewer splits
+    const long long items = (long long)k_total * p.m_tiles;
+    const long long cap = p.target_units > 0 ? p.target_units : 1;
+    if (items <= cap) return 1;
+    const int need = (int)min((items + cap - 1) / cap, (long long)S);
+    for (int g = need; g < S; ++g)
+        if (S % g == 0) return g;
+    return S;
+}
 
 // Runs on all NT threads of the block (every barrier inside is reached by all
 // of them); req_info, if not null, receives the kReqInfoInts values per
@@ -301,13 +321,15 @@ __device__ __forceinline__ PlanResult plan_splits(const PlanParams& p, const int
         pieces_total += t;
     }
     const int k_total = balanced ? (int)((total_pages + balanced - 1) / balanced) : pieces_total;
-    // the probed slot's kv-unit (the layout of plan_item)
+    const int group = balanced ? 1 : split_group(p, k_total, longest);
+    // the probed slot's first kv-unit (the layout of plan_item)
     int probe_k = -1;
     if (probe_slot >= 0) {
-        const int per_xcd = (k_total + 7) / 8;
+        const int items = k_total / group;
+        const int per_xcd = (items + 7) / 8;
         const int kx = (probe_slot >> 3) / p.m_tiles;
         probe_k = kx < per_xcd ? per_xcd * (probe_slot & 7) + kx : -1;
-        if (probe_k >= k_total) probe_k = -1;
+        probe_k = probe_k >= 0 && probe_k < items ? probe_k * group : -1;
     }
     int base = wave_base + incl - my_k;
     int g = my_g;
@@ -341,23 +363,26 @@ __device__ __forceinline__ PlanResult plan_splits(const PlanParams& p, const int
         g += pages;
     }
     __syncthreads();   // first pieces and pages of every cached request visible to the block
-    return PlanResult{chunk, k_total, balanced, balanced ? (int)total_pages : 0};
+    return PlanResult{chunk, k_total, balanced, balanced ? (int)total_pages : 0, group};
 }
 
-// Slot u's kv-unit and row tile.  Dispatch deals workgroups to the 8 XCDs
-// round-robin, so slot u runs on XCD u % 8 as its (u / 8)-th workgroup there.
-// Each XCD takes a contiguous run of C = ceil(kv-units / 8) kv-units with all
-// their row tiles: slot u holds kv-unit k = C (u % 8) + (u / 8) / m_tiles and
+// Slot u's first kv-unit and row tile.  Dispatch deals workgroups to the 8
+// XCDs round-robin, so slot u runs on XCD u % 8 as its (u / 8)-th workgroup
+// there.  Each XCD takes a contiguous run of C = ceil(items / 8) work items
+// (an item is `group` consecutive kv-units) with all their row tiles: slot u
+// holds item q = C (u % 8) + (u / 8) / m_tiles, i.e. kv-unit k = q group, and
 // row tile (u / 8) % m_tiles.  The splits of one request (which read the same
 // query rows) and the row tiles of one kv-unit (which read the same pages)
 // then share one L2.  Returns false for an empty slot.
 __device__ __forceinline__ bool slot_unit(const PlanParams& p, const PlanResult& r, int u, int& k, int& mt) {
-    const int per_xcd = (r.k_total + 7) / 8;
+    const int items = r.k_total / r.group;
+    const int per_xcd = (items + 7) / 8;
     const int pos = u >> 3;
     const int kx = pos / p.m_tiles;
-    k = per_xcd * (u & 7) + kx;
+    const int q = per_xcd * (u & 7) + kx;
+    k = q * r.group;
     mt = pos - kx * p.m_tiles;
-    return kx < per_xcd && k < r.k_total;
+    return kx < per_xcd && q < items;
 }
 
 __device__ __forceinline__ WorkItem empty_item() {
@@ -384,12 +409,13 @@ __device__ __forceinline__ WorkItem make_item(const PlanParams& p, const PlanRes
         w.g0 = g0;
         w.chunk = C;
     } else {
+        // (a group of splits: g0 = their count, each of cb pages but the last)
         const int cb = p.num_splits > 0 ? (pages + S - 1) / S : r.chunk;
         const int pb = min(pages, split_or_g * cb);
         w.piece = k;
         w.page_begin = pb;
-        w.npages = min(pages, (split_or_g + 1) * cb) - pb;
-        w.g0 = 0;
+        w.npages = min(pages, (split_or_g + r.group) * cb) - pb;
+        w.g0 = r.group > 1 ? r.group : 0;
         w.chunk = 0;
     }
     return w;
@@ -463,7 +489,8 @@ __device__ __forceinline__ WorkItem decode_work_item(const DecodeParams& p, uint
         WorkItem w = p.work[blockIdx.x];
         if (w.b >= p.plan.batch || w.mt < 0 || w.mt >= p.plan.m_tiles || w.page_begin < 0 || w.npages < 0 ||
             w.page_begin > p.max_pages || w.npages > (w.chunk > 0 ? w.chunk : p.max_pages) || w.nsplit < 1 ||
-            w.piece < 0 || w.chunk < 0 || w.g0 < 0)
+            w.piece < 0 || w.chunk < 0 || w.g0 < 0 ||
+            (w.chunk == 0 && w.g0 > 1 && (!p.plan.group_ok || w.g0 > w.nsplit)))
             w.b = -1;
         return w;
     }
@@ -502,10 +529,25 @@ __device__ __forceinline__ WorkItem decode_work_item(const DecodeParams& p, uint
 // pieces: every piece reuses the whole LDS).  Pieces after the first start at
 // page 0 of the next non-empty request; the balanced plan's global page
 // arithmetic gives each its piece count.  kMulti = false: the kernel runs
-// single-piece items only (plans for it never use the balanced layout), and
-// its body is not inside a loop (a body in a loop keeps more registers live
-// than the bf16 kernels have to spare).
-template <bool kMulti, typename Body>
+// single-piece items only (plans for it never use the balanced layout).
+// kGroups: an item may be a group of consecutive splits of one request, run
+// one after the other.
+// The one piece of an item that is neither a group nor a balanced range.
+__device__ __forceinline__ Piece single_piece(const DecodeParams& p, const WorkItem& w) {
+    const __attribute__((address_space(4))) int32_t* sl = (const __attribute__((address_space(4))) int32_t*)p.seq_lens;
+    const int n = min(max(sl[w.b], 0), p.max_pages * kPage);
+    Piece pc;
+    pc.b = __builtin_amdgcn_readfirstlane(w.b);
+    pc.mt = __builtin_amdgcn_readfirstlane(w.mt);
+    pc.page_begin = __builtin_amdgcn_readfirstlane(w.page_begin);
+    pc.page_end = __builtin_amdgcn_readfirstlane(min((n + kPage - 1) / kPage, w.page_begin + w.npages));
+    pc.nsplit = __builtin_amdgcn_readfirstlane(w.nsplit);
+    pc.slot = __builtin_amdgcn_readfirstlane(w.piece * p.plan.m_tiles + w.mt);
+    pc.sub = 0;
+    return pc;
+}
+
+template <bool kMulti, bool kGroups = false, typename Body>
 __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const WorkItem& w, Body&& body) {
     const int cap = p.max_pages * kPage;
     // (the lengths through the scalar unit: the piece loop keeps no VGPR)
@@ -514,16 +556,28 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const Work
         const int n = min(max(sl[b], 0), cap);
         return (n + kPage - 1) / kPage;
     };
+    // a group of consecutive splits of request b (forced split counts): one
+    // after the other, each ceil(pages / nsplit) pages but the last
+    const bool grouped = kGroups && w.chunk <= 0 && w.g0 > 1;
+    const int g_pages = grouped ? pages_of(w.b) : 0;
+    const int g_cb = grouped ? (g_pages + max(w.nsplit, 1) - 1) / max(w.nsplit, 1) : 0;
+    const int g_end = grouped ? min(g_pages, w.page_begin + w.npages) : 0;
     Piece pc;
     pc.b = w.b;
     pc.mt = w.mt;
     pc.page_begin = w.page_begin;
     pc.nsplit = w.nsplit;
+    pc.sub = 0;
     int piece = w.piece;
     int left = w.npages, done = 0;
     for (;;) {
-        const int pages = pages_of(pc.b);
-        pc.page_end = min(pages, pc.page_begin + left);
+        if (grouped) {
+            // (an empty split still runs: its partial says so, with lse -inf)
+            pc.page_begin = min(g_pages, w.page_begin + pc.sub * g_cb);
+            pc.page_end = max(pc.page_begin, min(g_end, pc.page_begin + g_cb));
+        } else {
+            pc.page_end = min(pages_of(pc.b), pc.page_begin + left);
+        }
         pc.slot = piece * p.plan.m_tiles + pc.mt;
         // (one value in every lane: kept in scalar registers)
         pc.b = __builtin_amdgcn_readfirstlane(pc.b);
@@ -532,9 +586,16 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const Work
         pc.page_end = __builtin_amdgcn_readfirstlane(pc.page_end);
         pc.nsplit = __builtin_amdgcn_readfirstlane(pc.nsplit);
         pc.slot = __builtin_amdgcn_readfirstlane(pc.slot);
+        pc.sub = __builtin_amdgcn_readfirstlane(pc.sub);
         // (a stored item that points past the workspace's partial slots is not followed)
         if (pc.nsplit > 1 && (pc.slot < 0 || pc.slot >= p.plan.units_max)) break;
         body(pc);
+        if (grouped) {
+            if (++pc.sub >= w.g0) break;
+            ++piece;
+            __syncthreads();   // the next split reuses the whole LDS
+            continue;
+        }
         const int took = pc.page_end - pc.page_begin;
         left -= took;
         done += took;
@@ -1206,9 +1267,45 @@ __device__ __forceinline__ int hw_simd_id() {
     return (int)(__builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4) & 3u);
 }
 
+// The query tile of rows [mt kMTile, + kMTile) of request b through the still
+// empty ring (rows swizzled like cache rows, 144 blocks of 1 KB, 18 per wave);
+// then each A wave reads its rows' Q^T fragments: k-step ks covers dims 16 ks
+// .. + 15, lane (lr, G) holds dims + 8 G .. + 7 of row lr (chunk 2 ks + G).
+// All 8 waves take part (two barriers).  The splits of a group reuse the
+// fragments (same request and rows).
 template <bool A>
+__device__ __forceinline__ void stage_query_bf16(const DecodeParams& p, int b, int mt, uint8_t* lds, int s, int wv,
+                                                 bf16x8_t (&qf)[36]) {
+    const int lane = lane_id_fresh();
+    const int G = lane >> 5, lr = lane & 31;
+    lds_u8* const ring = (lds_u8*)lds;
+    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
+    const uint8_t* qreq = (const uint8_t*)p.q + (size_t)b * p.rows * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < 18; ++j) {
+        const int qb = 18 * wv + j;
+        const int q = qb * 64 + lane;
+        const int r = q / kRowChunks;
+        const int pc = q - r * kRowChunks;
+        const uint32_t src = (uint32_t)min(mt * kMTile + r, p.rows - 1) * kRowBytes + ((pc ^ swz(r)) << 4);
+        dma16(ring_addr + qb * 1024, qreq, src);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (A) {
+        const lds_u8* qrow = ring + (s * 32 + lr) * kRowBytes;
+        int qb4[4];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) qb4[k4] = (((2 * k4 + G) ^ swz(lr)) & 7) << 4;
+#pragma unroll
+        for (int ks = 0; ks < 36; ++ks) qf[ks] = *(const lds_bf16x8*)(qrow + qb4[ks & 3] + (ks >> 2) * 128);
+    }
+    __syncthreads();   // the A waves hold their query fragments: the ring is free
+}
+
+template <bool A, int kKAhead>
 __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const Piece& w, uint8_t* lds,
-                                                    const int s, const int wv) {
+                                                    const int s, const int wv, bf16x8_t (&qf)[36]) {
     const int lane = lane_id_fresh();
     const int tid = wv * 64 + lane;
     const int G = lane >> 5;        // MFMA k-group of this lane
@@ -1264,34 +1361,6 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
     const int nvis = min(p.causal ? max(n - (p.q_len - 1 - tq), 0) : n, unit_end);
     const int nvis_min = min(p.causal ? max(n - (p.q_len - 1), 0) : n, unit_end);
 
-    // ---- query: the 128-row tile through the still empty ring (rows
-    // swizzled like cache rows, 144 blocks of 1 KB, 18 per wave), then each A
-    // wave reads its rows' Q^T fragments: k-step ks covers dims 16 ks .. + 15,
-    // lane (lr, G) holds dims + 8 G .. + 7 of row lr (chunk 2 ks + G)
-    bf16x8_t qf[A ? 36 : 1];
-    {
-        const uint8_t* qreq = (const uint8_t*)p.q + (size_t)b * p.rows * kRowBytes;
-#pragma unroll
-        for (int j = 0; j < 18; ++j) {
-            const int qb = 18 * wv + j;
-            const int q = qb * 64 + lane;
-            const int r = q / kRowChunks;
-            const int pc = q - r * kRowChunks;
-            const uint32_t src = (uint32_t)min(w.mt * kMTile + r, p.rows - 1) * kRowBytes + ((pc ^ swz(r)) << 4);
-            dma16(ring_addr + qb * 1024, qreq, src);
-        }
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        __syncthreads();
-        if (A) {
-            const lds_u8* qrow = ring + (s * 32 + lr) * kRowBytes;
-            int qb4[4];
-#pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) qb4[k4] = (((2 * k4 + G) ^ swz(lr)) & 7) << 4;
-#pragma unroll
-            for (int ks = 0; ks < 36; ++ks) qf[ks] = *(const lds_bf16x8*)(qrow + qb4[ks & 3] + (ks >> 2) * 128);
-        }
-    }
-    __syncthreads();   // the A waves hold their query fragments: the ring is free
 
     // K fragment offsets within a slot (A): token lr, chunk 2 ks + G at position
     // (c & ~7) | ((c ^ swz(lr)) & 7); c(ks + 4) = c(ks) + 8, so four bases
@@ -1432,11 +1501,10 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
     };
 
     // (A) S^T of half page k for the wave's 32 rows: all 36 k-steps in one
-    // accumulation chain, K fragments read two ahead (inline-assembly MFMAs
+    // accumulation chain, K fragments read kKAhead ahead (inline-assembly MFMAs
     // with S tied to VGPRs; wait states before S is read are inserted at the end)
     auto qk = [&](int k, f32x16& sacc) {
         lds_u8* cur = slot_ptr(k);
-        constexpr int kKAhead = 2;
         bf16x8_t kf[kKAhead];
 #pragma unroll
         for (int ks = 0; ks < kKAhead; ++ks) kf[ks] = *(const lds_bf16x8*)(cur + qk_off[ks & 3] + (ks >> 2) * 128);
@@ -1640,6 +1708,11 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
     }
 }
 
+// kGroups: the instance for work lists that may hold groups of splits (the
+// query staged once per item, the splits run in a loop, K fragments one
+// ahead: with two ahead the loop would not fit the registers); the other
+// instance runs single-piece items with no loop around the body.
+template <bool kGroups>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void decode_bf16_ab_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[kAbLdsBytes];
@@ -1664,10 +1737,32 @@ void decode_bf16_ab_kernel(DecodeParams p) {
     const bool by_hw = cnt0 == 2 && cnt1 == 2 && cnt2 == 2 && cnt3 == 2;
     const bool is_a = by_hw ? lower == 0 : wv < 4;
     const int s = by_hw ? sid : (wv & 3);
-    for_each_piece<false>(p, w, [&](const Piece& pc) {
-        if (is_a) decode_bf16_ab_body<true>(p, pc, lds, s, wv);
-        else decode_bf16_ab_body<false>(p, pc, lds, s, wv);
-    });
+    // (one piece loop per role: wave A's query fragments stay live across the
+    // splits of a group, and only on A's path; an item of one piece runs the
+    // body outside any loop)
+    bf16x8_t qf[36];
+    if constexpr (kGroups) {
+        if (is_a) {
+            stage_query_bf16<true>(p, w.b, w.mt, lds, s, wv, qf);
+            for_each_piece<false, true>(p, w, [&](const Piece& pc) { decode_bf16_ab_body<true, 1>(p, pc, lds, s, wv, qf); });
+        } else {
+            stage_query_bf16<false>(p, w.b, w.mt, lds, s, wv, qf);
+            for_each_piece<false, true>(p, w, [&](const Piece& pc) { decode_bf16_ab_body<false, 1>(p, pc, lds, s, wv, qf); });
+        }
+    } else {
+        // (an item holding a group is not followed here: the plan for this
+        // instance makes none, see PlanParams::group_ok)
+        if (w.chunk <= 0 && w.g0 > 1) return;
+        const Piece pc = single_piece(p, w);
+        if (pc.nsplit > 1 && (pc.slot < 0 || pc.slot >= p.plan.units_max)) return;
+        if (is_a) {
+            stage_query_bf16<true>(p, pc.b, pc.mt, lds, s, wv, qf);
+            decode_bf16_ab_body<true, 2>(p, pc, lds, s, wv, qf);
+        } else {
+            stage_query_bf16<false>(p, pc.b, pc.mt, lds, s, wv, qf);
+            decode_bf16_ab_body<false, 2>(p, pc, lds, s, wv, qf);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -2913,7 +3008,8 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int units, hipStream_t stre
     }
     clear_stale_error();
     if (p.bf16_four_waves) hipLaunchKernelGGL(decode_bf16_kernel, dim3(units), dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(decode_bf16_ab_kernel, dim3(units), dim3(512), 0, stream, p);
+    else if (p.plan.group_ok) hipLaunchKernelGGL(decode_bf16_ab_kernel<true>, dim3(units), dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL(decode_bf16_ab_kernel<false>, dim3(units), dim3(512), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_after) return hipEventRecord(ev_after, stream);

@@ -263,6 +263,20 @@ def test_qlen4_not_causal():
     compare(out, lse, o_ref, l_ref, what="qlen4 not causal")
 
 
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_forced_splits_grouped(out_bf16):
+    """100 forced splits of 3 requests (300 kv-units, more than one round of
+    workgroups): each workgroup runs a group of 2 consecutive splits with the
+    query staged once; most splits of 2 pages cover the sequence and the rest
+    are empty (lse -inf partials)."""
+    import mla_latent_decode_absorbed_amd as mla
+    say(f"forced splits grouped out_bf16={out_bf16}")
+    inp = workloads.make_decode_inputs(3, 1, 128, [6500, 7000, 6600], "bf16", seed=45, device=dev())
+    o_ref, l_ref = run_oracle(inp)
+    out, lse = run_hip(inp, num_splits=100, out_dtype=mla.BF16 if out_bf16 else None)
+    compare(out, lse, o_ref, l_ref, what=f"grouped splits bf16_out={out_bf16}")
+
+
 def test_more_fixed_splits_than_pages():
     """num_splits = 8 on sequences of 1-3 pages: each request gets min(8, pages) splits."""
     say("num_splits=8, 1-3 pages")

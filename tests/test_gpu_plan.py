@@ -56,8 +56,9 @@ def pages_of(seq_lens, max_pages):
 
 
 def expected_plan(seq_lens, max_pages, m_tiles, num_splits, target, fp8=False):
-    """(req_info rows, items per kv-unit) of the policy above; an item is
-    (b, piece, page_begin, npages, nsplit, g0, chunk) without the row tile."""
+    """(req_info rows, work items) of the policy above; an item is
+    (b, piece, page_begin, npages, nsplit, g0, chunk) without the row tile
+    (one per kv-unit, or per group of splits)."""
     pg = pages_of(seq_lens, max_pages)
     B = len(pg)
     cap = max(1, target // m_tiles)
@@ -65,6 +66,26 @@ def expected_plan(seq_lens, max_pages, m_tiles, num_splits, target, fp8=False):
         S = np.maximum(1, np.minimum(num_splits, pg))
         cb = (pg + S - 1) // S
         chunk = None
+        # groups of consecutive splits (bf16 two-role kernel, forced splits
+        # making more items than one round): when every request has the same
+        # split count S, the smallest divisor g of S that brings the items
+        # within the round; an item is then g splits of one request
+        per_req = min(num_splits, max_pages)
+        group_ok = not fp8 and per_req > 1 and B * per_req * m_tiles > target
+        S_all = min(num_splits, max(1, int(pg.max())))
+        K = int(S.sum())
+        if group_ok and K == B * S_all and K * m_tiles > target:
+            need = min(-(-K * m_tiles // target), S_all)
+            g = next(d for d in range(need, S_all + 1) if S_all % d == 0)
+            if g > 1:
+                first = np.concatenate([[0], np.cumsum(S)[:-1]])
+                req = np.stack([S, first, np.zeros(B, dtype=np.int64), np.zeros(B, dtype=np.int64)], axis=1)
+                items = []
+                for b in range(B):
+                    for s0 in range(0, int(S[b]), g):
+                        pb, pe = min(pg[b], s0 * cb[b]), min(pg[b], (s0 + g) * cb[b])
+                        items.append((b, int(first[b] + s0), int(pb), int(pe - pb), int(S[b]), g, 0))
+                return req, items
     else:
         start = max(MIN_CHUNK, -(-int(pg.sum()) // cap))
         longest = max(1, int(pg.max()))
@@ -223,6 +244,21 @@ def test_plan_past_lds_cache():
 def test_plan_fixed_splits():
     """num_splits = 3 with requests shorter than 3 pages and empty ones."""
     check(ragged(50, 0, 600, 14, zeros=5), 32, 1, 10, 3, "fixed 3 splits")
+
+
+@pytest.mark.parametrize("planned", [False, True])
+def test_plan_fixed_splits_grouped(planned):
+    """256 splits of 4 x 131072 tokens over two row tiles (2048 kv-units x
+    tiles): groups of 8 consecutive splits, one round of 256 workgroups."""
+    req, _ = check([131072] * 4, 128, 2, 2048, 256, "256 splits grouped", planned=planned)
+    assert (req == 256).all()
+
+
+def test_plan_fixed_splits_group_is_a_divisor():
+    """9 splits x 40 requests (360 items): the group is 3, the smallest divisor
+    of 9 at or above 2; and one short request (fewer splits) turns grouping off."""
+    check([9 * 64 * 3] * 40, 64, 1, 27, 9, "9 splits grouped by 3")
+    check([9 * 64 * 3] * 39 + [64 * 5], 64, 1, 27, 9, "unequal split counts: no groups")
 
 
 @pytest.mark.parametrize("batch", [256, 257])

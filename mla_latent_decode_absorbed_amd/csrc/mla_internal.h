@@ -34,10 +34,13 @@ struct WorkItem {
 // One piece of a workgroup's work: rows [mt*kMTile, +kMTile) of request b
 // over pages [page_begin, page_end); nsplit == 1 writes out/lse directly,
 // otherwise the partial goes to workspace slot `slot` (= piece * m_tiles + mt).
-// sub > 0: a later split of a group (same request and rows as the one before).
+// run > 1: the piece is a group of `run` consecutive splits of the request,
+// split j over pages [page_begin + j run_pages, + run_pages) (clipped to
+// page_end; the last ones may be empty) with its partial in slot
+// slot + j * m_tiles.
 struct Piece {
     int32_t b, mt, page_begin, page_end, nsplit, slot;
-    int32_t sub;                // index of this split within its work item's group (0: the first)
+    int32_t run, run_pages;
 };
 
 // Per-request planner output, int32 [batch][kReqInfoInts]: pieces the request

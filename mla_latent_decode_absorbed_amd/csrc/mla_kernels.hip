@@ -525,13 +525,6 @@ __device__ __forceinline__ WorkItem decode_work_item(const DecodeParams& p, uint
     return w;
 }
 
-// Runs body(piece) for each piece of work item w in turn (a barrier between
-// pieces: every piece reuses the whole LDS).  Pieces after the first start at
-// page 0 of the next non-empty request; the balanced plan's global page
-// arithmetic gives each its piece count.  kMulti = false: the kernel runs
-// single-piece items only (plans for it never use the balanced layout).
-// kGroups: an item may be a group of consecutive splits of one request, run
-// one after the other.
 // The one piece of an item that is neither a group nor a balanced range.
 __device__ __forceinline__ Piece single_piece(const DecodeParams& p, const WorkItem& w) {
     const __attribute__((address_space(4))) int32_t* sl = (const __attribute__((address_space(4))) int32_t*)p.seq_lens;
@@ -543,11 +536,43 @@ __device__ __forceinline__ Piece single_piece(const DecodeParams& p, const WorkI
     pc.page_end = __builtin_amdgcn_readfirstlane(min((n + kPage - 1) / kPage, w.page_begin + w.npages));
     pc.nsplit = __builtin_amdgcn_readfirstlane(w.nsplit);
     pc.slot = __builtin_amdgcn_readfirstlane(w.piece * p.plan.m_tiles + w.mt);
-    pc.sub = 0;
+    pc.run = 1;
+    pc.run_pages = 0;
     return pc;
 }
 
-template <bool kMulti, bool kGroups = false, typename Body>
+// The piece of an item that is a group of consecutive forced splits of one
+// request (chunk 0, g0 > 1 splits of ceil(pages / nsplit) pages each, the
+// last ones possibly short or empty), as one run; splits whose partial slot
+// would lie past the workspace are dropped.  Any other item: its single piece.
+__device__ __forceinline__ Piece group_piece(const DecodeParams& p, const WorkItem& w) {
+    if (!(w.chunk <= 0 && w.g0 > 1)) return single_piece(p, w);
+    const __attribute__((address_space(4))) int32_t* sl = (const __attribute__((address_space(4))) int32_t*)p.seq_lens;
+    const int n = min(max(sl[w.b], 0), p.max_pages * kPage);
+    const int pages = (n + kPage - 1) / kPage;
+    const int cb = max((pages + max(w.nsplit, 1) - 1) / max(w.nsplit, 1), 1);
+    const int slot = w.piece * p.plan.m_tiles + w.mt;
+    const int fit = slot < p.plan.units_max ? (p.plan.units_max - 1 - slot) / p.plan.m_tiles + 1 : 0;
+    const int run = min(w.g0, fit);
+    const int pb = min(pages, w.page_begin);
+    Piece pc;
+    pc.b = __builtin_amdgcn_readfirstlane(w.b);
+    pc.mt = __builtin_amdgcn_readfirstlane(w.mt);
+    pc.page_begin = __builtin_amdgcn_readfirstlane(pb);
+    pc.page_end = __builtin_amdgcn_readfirstlane(max(pb, min(min(pages, w.page_begin + w.npages), w.page_begin + run * cb)));
+    pc.nsplit = __builtin_amdgcn_readfirstlane(w.nsplit);
+    pc.slot = __builtin_amdgcn_readfirstlane(slot);
+    pc.run = __builtin_amdgcn_readfirstlane(run);
+    pc.run_pages = __builtin_amdgcn_readfirstlane(cb);
+    return pc;
+}
+
+// Runs body(piece) for each piece of work item w in turn (a barrier between
+// pieces: every piece reuses the whole LDS).  Pieces after the first start at
+// page 0 of the next non-empty request; the balanced plan's global page
+// arithmetic gives each its piece count.  kMulti = false: the kernel runs
+// single-piece items only (plans for it never use the balanced layout).
+template <bool kMulti, typename Body>
 __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const WorkItem& w, Body&& body) {
     const int cap = p.max_pages * kPage;
     // (the lengths through the scalar unit: the piece loop keeps no VGPR)
@@ -556,28 +581,17 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const Work
         const int n = min(max(sl[b], 0), cap);
         return (n + kPage - 1) / kPage;
     };
-    // a group of consecutive splits of request b (forced split counts): one
-    // after the other, each ceil(pages / nsplit) pages but the last
-    const bool grouped = kGroups && w.chunk <= 0 && w.g0 > 1;
-    const int g_pages = grouped ? pages_of(w.b) : 0;
-    const int g_cb = grouped ? (g_pages + max(w.nsplit, 1) - 1) / max(w.nsplit, 1) : 0;
-    const int g_end = grouped ? min(g_pages, w.page_begin + w.npages) : 0;
     Piece pc;
     pc.b = w.b;
     pc.mt = w.mt;
     pc.page_begin = w.page_begin;
     pc.nsplit = w.nsplit;
-    pc.sub = 0;
+    pc.run = 1;
+    pc.run_pages = 0;
     int piece = w.piece;
     int left = w.npages, done = 0;
     for (;;) {
-        if (grouped) {
-            // (an empty split still runs: its partial says so, with lse -inf)
-            pc.page_begin = min(g_pages, w.page_begin + pc.sub * g_cb);
-            pc.page_end = max(pc.page_begin, min(g_end, pc.page_begin + g_cb));
-        } else {
-            pc.page_end = min(pages_of(pc.b), pc.page_begin + left);
-        }
+        pc.page_end = min(pages_of(pc.b), pc.page_begin + left);
         pc.slot = piece * p.plan.m_tiles + pc.mt;
         // (one value in every lane: kept in scalar registers)
         pc.b = __builtin_amdgcn_readfirstlane(pc.b);
@@ -586,16 +600,9 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const Work
         pc.page_end = __builtin_amdgcn_readfirstlane(pc.page_end);
         pc.nsplit = __builtin_amdgcn_readfirstlane(pc.nsplit);
         pc.slot = __builtin_amdgcn_readfirstlane(pc.slot);
-        pc.sub = __builtin_amdgcn_readfirstlane(pc.sub);
         // (a stored item that points past the workspace's partial slots is not followed)
         if (pc.nsplit > 1 && (pc.slot < 0 || pc.slot >= p.plan.units_max)) break;
         body(pc);
-        if (grouped) {
-            if (++pc.sub >= w.g0) break;
-            ++piece;
-            __syncthreads();   // the next split reuses the whole LDS
-            continue;
-        }
         const int took = pc.page_end - pc.page_begin;
         left -= took;
         done += took;
@@ -1303,7 +1310,13 @@ __device__ __forceinline__ void stage_query_bf16(const DecodeParams& p, int b, i
     __syncthreads();   // the A waves hold their query fragments: the ring is free
 }
 
-template <bool A, int kKAhead>
+// kRun: the piece may be a run of consecutive splits (Piece::run > 1).  The
+// run streams through the ring as one sequence of half pages: where a split
+// ends, wave A has already taken the next split's first half page through
+// QK^T and the softmax (from a fresh max and sums), the copies of the next two
+// are in flight, and the finished split leaves through the one ring slot that
+// nothing uses then.
+template <bool A, int kKAhead, bool kRun>
 __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const Piece& w, uint8_t* lds,
                                                     const int s, const int wv, bf16x8_t (&qf)[36]) {
     const int lane = lane_id_fresh();
@@ -1595,6 +1608,98 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
         }
     };
 
+    // (run) the split of half page k is (k - half_begin) / (2 run_pages); its
+    // partial goes to slot w.slot + j m_tiles
+    const int run = kRun ? w.run : 1;
+    int j_cur = 0;
+    auto split_slot = [&](int j) { return w.slot + j * p.plan.m_tiles; };
+
+    // ---- a split's end: o = O / l for this wave's dim tiles of the four row
+    //      tiles; lse = ln(sum exp) for the A wave's rows
+    auto zero_o = [&]() {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            oa[t] = (f32x16)0.f;
+            asm volatile("" : "+v"(oa[t]));
+        }
+        if (!A) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    ov[j][t] = (f32x16)0.f;
+                    asm volatile("" : "+v"(ov[j][t]));
+                }
+        }
+    };
+    auto write_lse = [&](int slot_j, float m_f, float l_row) {
+        if (A && row_ok && G == 0) {
+            const float lse = l_row > 0.f ? (m_f + __log2f(l_row)) * kLn2 : -INFINITY;
+            if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
+            else p.ws_lse[(size_t)slot_j * kMTile + (row - w.mt * kMTile)] = lse;
+        }
+    };
+    // Inside a run, where split j ends after half page k (m_f, l_f, lr_f: its
+    // max and this lane's sums): the copies of half pages k + 2 and k + 3 are
+    // in flight and k + 1 holds the next split's first weights, so the rows
+    // leave 32 at a time (one row tile) through half page k's slot, as bf16
+    // partials (rows of 1,040 bytes; the rounded weights' sums after the 32
+    // rows).  B first waits for the copy of k + 2, so that its stores never
+    // stand between a wait and the copy it waits for.
+    auto finish_mid = [&](int k, int slot_j, float m_f, float l_f, float lr_f) {
+        if (!A) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
+        pv_drain();
+        const float l_row = pair_sum(l_f);
+        const float lr_row = pair_sum(lr_f);
+        // (every lane-dependent address here comes from a fresh lane id: the
+        // compiler would otherwise keep them in registers across the loop)
+        const int lf = lane_id_fresh();
+        const int lrf = lf & 31, Gf = lf >> 5;
+        constexpr int st_row = kV * 2 + 16;
+        constexpr int row_chunks = kV * 2 / 16;
+        static_assert(32 * st_row + 4 * 32 * 4 <= kSlotBytes, "one row tile and the sums fit a ring slot");
+        lds_u8* const stage = slot_ptr(k);
+        lds_f32* const lb = (lds_f32*)(stage + 32 * st_row);
+        __syncthreads();                  // every wave is done with half page k
+        if (A && Gf == 0) lb[s * 32 + lrf] = lr_row;
+        __syncthreads();
+        float lt[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) lt[t] = lb[t * 32 + lrf];
+        // the lse first: nothing after the stores may wait on this wave's
+        // memory counter
+        if (A && Gf == 0 && w.mt * kMTile + s * 32 + lrf < p.rows)
+            p.ws_lse[(size_t)slot_j * kMTile + s * 32 + lrf] = l_row > 0.f ? (m_f + __log2f(l_row)) * kLn2 : -INFINITY;
+        uint8_t* const gbase = (uint8_t*)p.ws_o + (size_t)slot_j * kMTile * kV * 2;
+        lds_u8* const srow0 = stage + lrf * st_row + 2 * (32 * (4 * s + J0) + 4 * Gf);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float inv = lt[t] > 0.f ? 1.f / lt[t] : 0.f;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 v = (f32x4){o_elem(j, t, 4 * q4), o_elem(j, t, 4 * q4 + 1), o_elem(j, t, 4 * q4 + 2),
+                                            o_elem(j, t, 4 * q4 + 3)} * inv;
+                    __bf16 __attribute__((ext_vector_type(4))) h;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) h[i] = (__bf16)v[i];
+                    *(lds_i16x4*)(srow0 + 2 * 32 * j + 2 * 8 * q4) = __builtin_bit_cast(i16x4, h);
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = wv * 64 + lf; i < 32 * row_chunks; i += 512) {
+                const int rl = i / row_chunks, c = i - rl * row_chunks;
+                if (w.mt * kMTile + 32 * t + rl < p.rows)
+                    *(i32x4*)(gbase + (size_t)(32 * t + rl) * kV * 2 + 16 * c) =
+                        *(const __attribute__((address_space(3))) i32x4*)(stage + rl * st_row + 16 * c);
+            }
+            __syncthreads();
+        }
+        zero_o();
+    };
+
     if (half_begin < half_end) {
         // prologue: B copies the first three half pages; T(pre): the first has
         // landed; A contracts it and publishes P of the first half page
@@ -1618,17 +1723,30 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
             qk(half_begin, sacc);
             softmax(half_begin, sacc);
         }
+        // (run) the first half page of the next split, and whether the last
+        // step ended a split (its end already waited for the copy that this
+        // step's barrier would wait for)
+        int next_split = kRun && run > 1 ? half_begin + 2 * w.run_pages : half_end;
+        bool after_split = false;
         for (int k = half_begin;; ++k) {
             // T(k): the copies of half page k + 1 have landed (B waits for its
             // own, the barrier makes them everyone's), P(k) is published
-            if (!A) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
+            if (!A && !(kRun && after_split)) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
             lds_sync();
             const bool more = k + 1 < half_end;
+            const bool ends = kRun && more && k + 1 == next_split;
+            float m_f = 0.f, l_f = 0.f, lr_f = 0.f;
             if (A) {
                 pv(k);
                 if (more) {
                     f32x16 sacc;
                     qk(k + 1, sacc);
+                    if (ends) {
+                        // half page k + 1 opens the next split: its softmax
+                        // starts from no max and empty sums
+                        m_f = m; l_f = l; lr_f = lr_sum;
+                        m = -INFINITY; l = 0.f; lr_sum = 0.f;
+                    }
                     softmax(k + 1, sacc);
                 }
             } else {
@@ -1637,35 +1755,41 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
                 if (more) zero_tail(k + 1);
                 pv(k);
             }
+            if (kRun) {
+                after_split = ends;
+                if (ends) {
+                    finish_mid(k, split_slot(j_cur), m_f, l_f, lr_f);
+                    ++j_cur;
+                    next_split += 2 * w.run_pages;
+                }
+            }
             if (!more) break;
         }
     }
 
-    // ---- epilogue: o = O / l for this wave's dim tiles of the four row
-    //      tiles; lse = ln(sum exp) for the A wave's rows.
-    // No copy may still be writing this workgroup's LDS when it is reused.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    pv_drain();
-    const float l_row = pair_sum(l);
-    const float lr_row = pair_sum(lr_sum);
-    __syncthreads();                      // every wave is done with the ring and the P buffers
-    lds_f32* const lbuf = (lds_f32*)(lds + kAbPBufOff);   // [4 tiles][32 rows]: sums of the rounded weights
-    if (A && G == 0) lbuf[s * 32 + lr] = lr_row;
-    __syncthreads();
-    float lt[4];
+    // ---- the last split's end (the whole ring is free): rows leave through the
+    // ring, per half (64 rows): every wave writes its dims of the rows, scaled
+    // by 1 / l, as fp32 (a single piece to an fp32 output) or bf16 (a bf16
+    // output, or a split partial), into rows of 512 e + 16 bytes; then the
+    // workgroup stores whole contiguous row pieces, 16 bytes per lane.
+    auto finish = [&](int slot_j) {
+        // No copy may still be writing this workgroup's LDS when it is reused.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        pv_drain();
+        const float l_row = pair_sum(l);
+        const float lr_row = pair_sum(lr_sum);
+        __syncthreads();                      // every wave is done with the ring and the P buffers
+        lds_f32* const lbuf = (lds_f32*)(lds + kAbPBufOff);   // [4 tiles][32 rows]: sums of the rounded weights
+        if (A && G == 0) lbuf[s * 32 + lr] = lr_row;
+        __syncthreads();
+        float lt[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) lt[t] = lbuf[t * 32 + lr];
-    // Rows leave through the idle ring: per half (64 rows) every wave writes
-    // its dims of the rows, scaled by 1 / l, as fp32 (a single piece to an
-    // fp32 output) or bf16 (a bf16 output, or a split partial), into rows of
-    // 512 e + 16 bytes; then the workgroup stores whole contiguous row pieces,
-    // 16 bytes per lane.
-    {
+        for (int t = 0; t < 4; ++t) lt[t] = lbuf[t * 32 + lr];
         const bool f32 = w.nsplit == 1 && !p.out_bf16;
         const int e = f32 ? 4 : 2;
         const int st_row = kV * e + 16;
         const int row_chunks = kV * e / 16;
-        uint8_t* gbase = w.nsplit > 1 ? (uint8_t*)p.ws_o + (size_t)w.slot * kMTile * kV * 2
+        uint8_t* gbase = w.nsplit > 1 ? (uint8_t*)p.ws_o + (size_t)slot_j * kMTile * kV * 2
                                       : (uint8_t*)p.out + ((size_t)b * p.rows + (size_t)w.mt * kMTile) * kV * e;
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -1700,18 +1824,24 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
             }
             __syncthreads();
         }
-    }
-    if (A && row_ok && G == 0) {
-        const float lse = l_row > 0.f ? (m + __log2f(l_row)) * kLn2 : -INFINITY;
-        if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
-        else p.ws_lse[(size_t)w.slot * kMTile + (row - w.mt * kMTile)] = lse;
+        write_lse(slot_j, m, l_row);
+    };
+    finish(split_slot(j_cur));
+    if (kRun) {
+        // splits of the run past the sequence's end: empty partials (zero
+        // rows, lse -inf)
+        for (int j = j_cur + 1; j < run; ++j) {
+            zero_o();
+            m = -INFINITY; l = 0.f; lr_sum = 0.f;
+            finish(split_slot(j));
+        }
     }
 }
 
-// kGroups: the instance for work lists that may hold groups of splits (the
-// query staged once per item, the splits run in a loop, K fragments one
-// ahead: with two ahead the loop would not fit the registers); the other
-// instance runs single-piece items with no loop around the body.
+// kGroups: the instance for work lists that may hold groups of splits (a
+// group runs as one stream of half pages, K fragments one ahead: with two
+// ahead the split ends inside the loop would not fit the registers); the
+// other instance runs single-piece items only.
 template <bool kGroups>
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void decode_bf16_ab_kernel(DecodeParams p) {
@@ -1737,17 +1867,16 @@ void decode_bf16_ab_kernel(DecodeParams p) {
     const bool by_hw = cnt0 == 2 && cnt1 == 2 && cnt2 == 2 && cnt3 == 2;
     const bool is_a = by_hw ? lower == 0 : wv < 4;
     const int s = by_hw ? sid : (wv & 3);
-    // (one piece loop per role: wave A's query fragments stay live across the
-    // splits of a group, and only on A's path; an item of one piece runs the
-    // body outside any loop)
     bf16x8_t qf[36];
     if constexpr (kGroups) {
+        const Piece pc = group_piece(p, w);
+        if (pc.nsplit > 1 && (pc.run < 1 || pc.slot >= p.plan.units_max)) return;   // (a stored item past the partial slots)
         if (is_a) {
-            stage_query_bf16<true>(p, w.b, w.mt, lds, s, wv, qf);
-            for_each_piece<false, true>(p, w, [&](const Piece& pc) { decode_bf16_ab_body<true, 1>(p, pc, lds, s, wv, qf); });
+            stage_query_bf16<true>(p, pc.b, pc.mt, lds, s, wv, qf);
+            decode_bf16_ab_body<true, 1, true>(p, pc, lds, s, wv, qf);
         } else {
-            stage_query_bf16<false>(p, w.b, w.mt, lds, s, wv, qf);
-            for_each_piece<false, true>(p, w, [&](const Piece& pc) { decode_bf16_ab_body<false, 1>(p, pc, lds, s, wv, qf); });
+            stage_query_bf16<false>(p, pc.b, pc.mt, lds, s, wv, qf);
+            decode_bf16_ab_body<false, 1, true>(p, pc, lds, s, wv, qf);
         }
     } else {
         // (an item holding a group is not followed here: the plan for this
@@ -1757,10 +1886,10 @@ void decode_bf16_ab_kernel(DecodeParams p) {
         if (pc.nsplit > 1 && (pc.slot < 0 || pc.slot >= p.plan.units_max)) return;
         if (is_a) {
             stage_query_bf16<true>(p, pc.b, pc.mt, lds, s, wv, qf);
-            decode_bf16_ab_body<true, 2>(p, pc, lds, s, wv, qf);
+            decode_bf16_ab_body<true, 2, false>(p, pc, lds, s, wv, qf);
         } else {
             stage_query_bf16<false>(p, pc.b, pc.mt, lds, s, wv, qf);
-            decode_bf16_ab_body<false, 2>(p, pc, lds, s, wv, qf);
+            decode_bf16_ab_body<false, 2, false>(p, pc, lds, s, wv, qf);
         }
     }
 }

@@ -277,6 +277,18 @@ def test_forced_splits_grouped(out_bf16):
     compare(out, lse, o_ref, l_ref, what=f"grouped splits bf16_out={out_bf16}")
 
 
+def test_forced_splits_grouped_one_page_splits():
+    """128 forced splits of 4 requests, q_len 2 causal (1,024 kv-units): groups
+    of 4 consecutive one-page splits run as one stream, so a split ends every
+    two half pages; groups hold full splits, a short last split (4 tokens)
+    and empty splits after the sequence's end."""
+    say("forced splits grouped, one-page splits")
+    inp = workloads.make_decode_inputs(4, 2, 128, [3000, 4100, 700, 8192], "bf16", seed=46, device=dev())
+    o_ref, l_ref = run_oracle(inp)
+    out, lse = run_hip(inp, num_splits=128)
+    compare(out, lse, o_ref, l_ref, what="grouped one-page splits")
+
+
 def test_more_fixed_splits_than_pages():
     """num_splits = 8 on sequences of 1-3 pages: each request gets min(8, pages) splits."""
     say("num_splits=8, 1-3 pages")

@@ -1445,30 +1445,23 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
     };
 
     // O^T += V^T . P^T over half page k for this wave's dim tiles and the four
-    // row tiles.  The flag bits of the four k-step 0 fragments are read first,
-    // together with the first operands (A: the first V and P fragments; B: the
-    // four k-step 0 P fragments, whose first words hold the flags), so that
-    // one LDS round trip serves both; every wave reads the same bits, so when
-    // a row of some tile moved its reference max (rare) the whole workgroup
-    // takes the slow path together: each wave rescales its accumulators of the
-    // tile by 2^-d, and after a barrier the tile's A wave clears the sign bits
-    // in LDS (a second barrier publishes them; the k-step 0 P fragments are
-    // then read again) before the usual PV.
+    // row tiles.  The four k-step 0 P fragments are read first (with A's first
+    // V fragment): their first words hold the flag bits, so one LDS round trip
+    // serves the check and the first MFMAs; every wave reads the same bits, so
+    // when a row of some tile moved its reference max (rare) the whole
+    // workgroup takes the slow path together: each wave rescales its
+    // accumulators of the tile by 2^-d, and after a barrier the tile's A wave
+    // clears the sign bits in LDS (a second barrier publishes them; the
+    // fragments are then read again) before the usual PV.
     auto pv = [&](int k) {
         lds_u8* cur = slot_ptr(k);
         int flag = 0;
-        bf16x8_t a0, pc0, pt0[A ? 1 : 4];
-        if (A) {
-            a0 = vfrag(cur, 0, 0);
-            pc0 = *(const lds_bf16x8*)pfrag_ptr(k, 0, 0);
+        bf16x8_t a0, pt0[4];
+        if (A) a0 = vfrag(cur, 0, 0);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) flag |= *(const __attribute__((address_space(3))) int*)pfrag_ptr(k, t, 0);
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                pt0[t] = *(const lds_bf16x8*)pfrag_ptr(k, t, 0);
-                flag |= __builtin_bit_cast(i32x4, pt0[t])[0];
-            }
+        for (int t = 0; t < 4; ++t) {
+            pt0[t] = *(const lds_bf16x8*)pfrag_ptr(k, t, 0);
+            flag |= __builtin_bit_cast(i32x4, pt0[t])[0];
         }
         if (__builtin_expect(__any((flag & 0x8000) != 0), 0)) {
             pv_drain();
@@ -1491,26 +1484,20 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
                 *f = v;
             }
             __syncthreads();
-            if (A) {
-                pc0 = *(const lds_bf16x8*)pfrag_ptr(k, 0, 0);
-            } else {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) pt0[t] = *(const lds_bf16x8*)pfrag_ptr(k, t, 0);
-            }
+            for (int t = 0; t < 4; ++t) pt0[t] = *(const lds_bf16x8*)pfrag_ptr(k, t, 0);
         }
         if (A) {
-            // one dim tile: each V fragment feeds four MFMAs, P read one tile ahead
+            // one dim tile: each V fragment feeds four MFMAs, the four P
+            // fragments of a k-step read at once
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const bf16x8_t a = k2 == 0 ? a0 : vfrag(cur, 0, k2);
-                bf16x8_t pc = k2 == 0 ? pc0 : *(const lds_bf16x8*)pfrag_ptr(k, 0, k2);
+                bf16x8_t pt[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    bf16x8_t pn;
-                    if (t < 3) pn = *(const lds_bf16x8*)pfrag_ptr(k, t + 1, k2);
-                    mfma_o(0, t, a, pc);
-                    pc = pn;
-                }
+                for (int t = 0; t < 4; ++t) pt[t] = k2 == 0 ? pt0[t] : *(const lds_bf16x8*)pfrag_ptr(k, t, k2);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) mfma_o(0, t, a, pt[t]);
             }
         } else {
             // three dim tiles: the four P fragments of a k-step stay in

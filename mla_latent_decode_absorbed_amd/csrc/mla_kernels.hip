@@ -1966,8 +1966,10 @@ __device__ __forceinline__ i32x8 cat8(i32x4 a, i32x4 b) {
 }
 
 // Four e4m3 codes (round to nearest even, saturating) of v[0..3] in one dword.
-__device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+// (old: any value; both halves of it are replaced.  Passing the register the
+// result will overwrite saves the zero a constant would be moved in with.)
+__device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d, int old = 0) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -2694,6 +2696,8 @@ __device__ __forceinline__ void decode_fp8_ab_body(const DecodeParams& p, const 
             }
             l = l * __builtin_ldexpf(1.f, -d_out) +
                 (((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7])));
+            // (the lo word is built in the register of a value that dies there,
+            // so no zero is moved in first)
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const f32x16& sv = r < 4 ? s0 : s1;
@@ -2702,7 +2706,8 @@ __device__ __forceinline__ void decode_fp8_ab_body(const DecodeParams& p, const 
                 const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, false);
                 const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hw, true);
                 ph[r] = hw;
-                pl[r] = pack_e4m3(sv[i0] - h01[0], sv[i0 + 1] - h01[1], sv[i0 + 2] - h23[0], sv[i0 + 3] - h23[1]);
+                const float r0 = sv[i0] - h01[0];
+                pl[r] = pack_e4m3(r0, sv[i0 + 1] - h01[1], sv[i0 + 2] - h23[0], sv[i0 + 3] - h23[1], __float_as_int(r0));
             }
             const int e0 = ph[0] | spread_nibble(d_out), e1 = ph[1] | spread_nibble(d_out >> 4);
             *(lds_i32x4*)pbuf = (i32x4){e0, e1, ph[2], ph[3]};

@@ -44,6 +44,8 @@ CASES = [
                                               dtype="fp8"), 0),
     ("fp8 balanced plan, 128 requests", dict(batch=128, q_len=1, heads=16, seq_lens=balanced_plan_lens(),
                                              dtype="fp8"), 0),
+    ("bf16 forced 128 splits in groups of 4", dict(batch=4, q_len=2, heads=128, seq_lens=[3000, 4100, 700, 8192],
+                                                   dtype="bf16"), 128),
 ]
 
 

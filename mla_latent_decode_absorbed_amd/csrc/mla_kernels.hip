@@ -1673,8 +1673,8 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
         float lt[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) lt[t] = lb[t * 32 + lrf];
-        // the lse first: nothing after the stores may wait on this wave's
-        // memory counter
+        // the lse before the rows: any load after the stores (an address
+        // reloaded from scratch, say) would wait for them
         if (A && Gf == 0 && w.mt * kMTile + s * 32 + lrf < p.rows)
             p.ws_lse[(size_t)slot_j * kMTile + s * 32 + lrf] = l_row > 0.f ? (m_f + __log2f(l_row)) * kLn2 : -INFINITY;
         uint8_t* const gbase = (uint8_t*)p.ws_o + (size_t)slot_j * kMTile * kV * 2;

@@ -1522,7 +1522,8 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
 
     // (A) S^T of half page k for the wave's 32 rows: all 36 k-steps in one
     // accumulation chain, K fragments read kKAhead ahead (inline-assembly MFMAs
-    // with S tied to VGPRs; wait states before S is read are inserted at the end)
+    // with S tied to VGPRs; the 12 wait states an 8-pass MFMA's result needs
+    // before a VALU instruction reads or writes it follow the chain)
     auto qk = [&](int k, f32x16& sacc) {
         lds_u8* cur = slot_ptr(k);
         bf16x8_t kf[kKAhead];
@@ -1538,7 +1539,7 @@ __device__ __forceinline__ void decode_bf16_ab_body(const DecodeParams& p, const
             else
                 asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sacc) : "v"(a), "v"(qf[ks]));
         }
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sacc));
+        asm volatile("s_nop 7\n\ts_nop 3" : "+v"(sacc));
     };
     // (A) online softmax of half page k: masks invisible tokens (element i is
     // token 32 k + 8 (i / 4) + 4 G + i % 4), moves the reference max (whole

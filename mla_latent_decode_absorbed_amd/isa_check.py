@@ -8,8 +8,12 @@ verifies the final instruction stream instead of trusting that:
 
   * VALU write of a VGPR/AGPR -> MFMA read of it: at least 2 wait states;
   * MFMA write -> VALU (or v_accvgpr_read) read of the result, or a VALU
-    write of the same registers: at least 18 wait states (a 16-pass XDL
-    instruction);
+    write of the same registers: at least 12 wait states after an 8-pass
+    v_mfma_f32_32x32x16_bf16 and 20 after a 16-pass
+    v_mfma_f32_32x32x64_f8f6f4 (any other MFMA: 20).  These are the counts
+    hipcc inserts for gfx950 after its own MFMAs (an MFMA builtin followed
+    by a VALU read of the result compiles to s_nop 11, resp. s_nop 15 +
+    s_nop 3);
   * f8f6f4 MFMA read of a source (A, B or C operand) -> VALU write of it: at
     least 4 wait states (measured: a VALU write one wait state after such an
     MFMA gave wrong results, three and more did not; bf16 MFMAs read their
@@ -27,11 +31,11 @@ Limits of the check (what it does not prove):
   * it treats only VALU instructions (v_* other than MFMAs) as readers or
     writers: DS / buffer / global stores that read an MFMA destination, and
     loads that overwrite an MFMA operand, are not modelled;
-  * it applies one threshold (18) to every MFMA, including the 16-pass
-    v_mfma_f32_32x32x64_f8f6f4.
+  * it knows the result latencies of the two MFMA opcodes the kernels
+    issue; any other MFMA gets the larger one.
 The kernels therefore do not rely on it alone: every inline-assembly MFMA
-chain ends with explicit s_nop drains of 24 wait states before any other
-instruction can read its results, on every path.
+chain ends with an explicit s_nop drain of at least its opcode's count
+before any other instruction can read its results, on every path.
 """
 from __future__ import annotations
 
@@ -39,8 +43,13 @@ import re
 import sys
 
 VALU_TO_MFMA = 2
-MFMA_TO_VALU = 18
+MFMA_TO_VALU = {"v_mfma_f32_32x32x16_bf16": 12, "v_mfma_f32_32x32x64_f8f6f4": 20}
+MFMA_TO_VALU_DEFAULT = 20
 MFMA_SRC_TO_VALU_WRITE = 4
+
+
+def _mfma_to_valu(op: str) -> int:
+    return MFMA_TO_VALU.get(op, MFMA_TO_VALU_DEFAULT)
 
 
 def _regs(tok: str):
@@ -100,12 +109,12 @@ def check_function(lines, name=""):
                 reads = _regs(ops[1])
             writes = _regs(ops[0])
             ws, j = 0, i - 1
-            while j >= 0 and ws < max(MFMA_TO_VALU, MFMA_SRC_TO_VALU_WRITE):
+            while j >= 0 and ws < max(MFMA_TO_VALU_DEFAULT, MFMA_SRC_TO_VALU_WRITE):
                 pop, pops = _operands(ins[j])
                 if pop.startswith("v_mfma") and pops:
                     dst = _regs(pops[0])
                     srcs = set().union(*[_regs(o) for o in pops[1:4]]) if len(pops) >= 4 else set()
-                    if ws < MFMA_TO_VALU and dst & (reads | writes):
+                    if ws < _mfma_to_valu(pop) and dst & (reads | writes):
                         what = "reads" if dst & reads else "overwrites"
                         bad.append(f"{name}: MFMA {ins[j]!r} -> VALU {line!r} {what} its result after {ws} wait states")
                         break

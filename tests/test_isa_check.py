@@ -37,10 +37,13 @@ def test_accvgpr_write_then_mfma_accumulator_read():
     assert len(bad) == 1
 
 
-def test_mfma_result_read_by_valu_needs_eighteen_wait_states():
+def test_mfma_result_read_by_valu_needs_the_opcodes_wait_states():
+    """12 wait states after the 8-pass bf16 MFMA, 20 after the 16-pass f8f6f4
+    one (the counts the compiler inserts after its own MFMAs on gfx950)."""
     bad = run("""
         v_mfma_f32_32x32x16_bf16 v[10:25], v[2:5], v[6:9], 0
         s_nop 7
+        s_nop 2
         v_add_f32_e32 v1, v10, v11
     """)
     assert len(bad) == 1 and "MFMA" in bad[0]
@@ -53,10 +56,31 @@ def test_mfma_result_read_by_valu_needs_eighteen_wait_states():
     assert run("""
         v_mfma_f32_32x32x16_bf16 v[10:25], v[2:5], v[6:9], 0
         s_nop 7
-        s_nop 7
-        s_nop 7
+        s_nop 3
         v_add_f32_e32 v1, v10, v11
     """) == []
+    # the f8f6f4 MFMA: 12 (or 19) wait states are not enough, 20 are
+    for nops in ("s_nop 7\n s_nop 3", "s_nop 7\n s_nop 7\n s_nop 2"):
+        bad = run(f"""
+            v_mfma_f32_32x32x64_f8f6f4 v[10:25], v[30:37], v[40:47], 0
+            {nops}
+            v_add_f32_e32 v1, v10, v11
+        """)
+        assert len(bad) == 1 and "MFMA" in bad[0], nops
+    assert run("""
+        v_mfma_f32_32x32x64_f8f6f4 v[10:25], v[30:37], v[40:47], 0
+        s_nop 7
+        s_nop 7
+        s_nop 3
+        v_add_f32_e32 v1, v10, v11
+    """) == []
+    # a VALU write of the result counts like a read
+    bad = run("""
+        v_mfma_f32_32x32x16_bf16 v[10:25], v[2:5], v[6:9], 0
+        s_nop 7
+        v_mov_b32_e32 v12, 0
+    """)
+    assert len(bad) == 1 and "overwrites" in bad[0]
 
 
 def test_every_kernel_of_a_listing_is_checked():

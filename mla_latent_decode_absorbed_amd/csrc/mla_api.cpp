@@ -31,26 +31,6 @@ int target_units_for_current_device() {
     return cus < mla::kTargetUnits ? cus : mla::kTargetUnits;
 }
 
-// The bf16 decode kernel: two waves per SIMD unless MLA_BF16_DECODE_KERNEL=w4
-// selects the one-wave-per-SIMD kernel (same results; kept for measurement).
-int bf16_four_waves() {
-    static const int v = [] {
-        const char* e = getenv("MLA_BF16_DECODE_KERNEL");
-        return e && strcmp(e, "w4") == 0 ? 1 : 0;
-    }();
-    return v;
-}
-
-// The fp8 decode kernel: two waves per SIMD unless MLA_FP8_DECODE_KERNEL=w4
-// selects the one-wave-per-SIMD kernel (same results; kept for measurement).
-int fp8_four_waves() {
-    static const int v = [] {
-        const char* e = getenv("MLA_FP8_DECODE_KERNEL");
-        return e && strcmp(e, "w4") == 0 ? 1 : 0;
-    }();
-    return v;
-}
-
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
@@ -127,7 +107,7 @@ mla::PlanParams plan_params(const mla_decode_desc* d, const WorkspaceLayout& L) 
     // may be grouped (consecutive splits of a request in one workgroup): the
     // two-role bf16 kernel has an instance for such lists
     const int64_t per_req = d->num_splits > 0 ? std::min<int64_t>(d->num_splits, d->max_pages_per_seq) : 0;
-    pp.group_ok = d->kv_dtype == MLA_BF16 && !bf16_four_waves() && per_req > 1 &&
+    pp.group_ok = d->kv_dtype == MLA_BF16 && per_req > 1 &&
                           (int64_t)d->batch * per_req * L.m_tiles > pp.target_units
                       ? 1
                       : 0;
@@ -205,8 +185,6 @@ int decode_impl(const mla_decode_desc* d, const void* q, const void* kv, const f
     dp.max_pages = d->max_pages_per_seq;
     dp.num_pages = d->num_pages;
     dp.out_bf16 = d->out_dtype == MLA_BF16;
-    dp.bf16_four_waves = bf16_four_waves();
-    dp.fp8_four_waves = fp8_four_waves();
     const hipError_t de = d->kv_dtype == MLA_FP8_E4M3
                               ? mla::launch_decode_fp8(dp, (int)L.units_max, s, (hipEvent_t)ev0, (hipEvent_t)ev1)
                               : mla::launch_decode_bf16(dp, (int)L.units_max, s, (hipEvent_t)ev0, (hipEvent_t)ev1);

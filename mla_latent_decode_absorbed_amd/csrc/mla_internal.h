@@ -78,8 +78,6 @@ struct DecodeParams {
     int32_t max_pages;
     int32_t num_pages;          // pages in the cache pool: every page id is clamped into [0, num_pages)
     int32_t out_bf16;
-    int32_t bf16_four_waves;    // bf16 cache: 1 = the one-wave-per-SIMD kernel, 0 = two waves per SIMD
-    int32_t fp8_four_waves;     // fp8 cache: 1 = the one-wave-per-SIMD kernel, 0 = two waves per SIMD
 };
 
 // A block-table entry as a page index that stays inside the pool: one

@@ -479,7 +479,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p, const int32_t*
 // item, which it also stores to the work list; workgroup 0 stores the
 // per-request values the combine reads.  The item is the same value in every
 // lane; readfirstlane makes that visible to the compiler.
-template <int NT = 256>
+template <int NT>
 __device__ __forceinline__ WorkItem decode_work_item(const DecodeParams& p, uint8_t* lds) {
     static_assert(NT % 64 == 0 && NT <= 1024, "whole waves, at most 16");
     if (!p.fused_plan) {
@@ -570,9 +570,8 @@ __device__ __forceinline__ Piece group_piece(const DecodeParams& p, const WorkIt
 // Runs body(piece) for each piece of work item w in turn (a barrier between
 // pieces: every piece reuses the whole LDS).  Pieces after the first start at
 // page 0 of the next non-empty request; the balanced plan's global page
-// arithmetic gives each its piece count.  kMulti = false: the kernel runs
-// single-piece items only (plans for it never use the balanced layout).
-template <bool kMulti, typename Body>
+// arithmetic gives each its piece count.
+template <typename Body>
 __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const WorkItem& w, Body&& body) {
     const int cap = p.max_pages * kPage;
     // (the lengths through the scalar unit: the piece loop keeps no VGPR)
@@ -606,7 +605,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const Work
         const int took = pc.page_end - pc.page_begin;
         left -= took;
         done += took;
-        if (!kMulti || w.chunk <= 0 || left <= 0 || took <= 0) break;
+        if (w.chunk <= 0 || left <= 0 || took <= 0) break;
         int b = pc.b + 1;
         while (b < p.plan.batch && pages_of(b) == 0) ++b;
         if (b >= p.plan.batch) break;
@@ -620,30 +619,16 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, const Work
 }
 
 // ---------------------------------------------------------------------------
-// split-KV decode, bf16 cache
+// split-KV decode, bf16 cache: shared layout and helpers
 //
-// Workgroup = 4 waves (one per SIMD), kMTile = 128 query rows, one work item
-// (request, 128-row tile, page range) per workgroup, so every cache page is
-// ingested once per 128 rows.  Both contractions run on
-// v_mfma_f32_32x32x16_bf16 with the query rows as the MFMA N dimension:
+// kMTile = 128 query rows per work item (request, 128-row tile, page range),
+// so every cache page is ingested once per 128 rows.  Both contractions run
+// on v_mfma_f32_32x32x16_bf16 with the query rows as the MFMA N dimension:
 //   S^T[32 tok][32 rows]  += K[32 tok][16 dims]  . Q^T[16 dims][32 rows]
 //   O^T[32 dims][32 rows] += V^T[32 dims][16 tok] . P^T[16 tok][32 rows]
-// Wave w owns query rows 32 w .. 32 w + 31: it contracts all 576 dims of
-// every token against them (its Q^T stays in 144 VGPRs), runs their online
-// softmax and owns their max and row sum.  For the PV product every wave
-// accumulates O^T for ALL four row tiles (128 rows) over one quarter of the
-// 512 output dims (128 w .. 128 w + 127), so every V^T fragment read from LDS
-// feeds four MFMAs: the LDS transpose reads, the slowest LDS access a single
-// wave per SIMD can issue, are a quarter of the cache bytes per wave.  The
-// waves trade their bf16 P^T tiles (and, when a row max moves, the rescale
-// factor) through LDS once per half page.
-//
 // The cache streams through LDS in half pages of 32 tokens (36,864 bytes)
-// held in a ring of 4 slots with direct HBM -> LDS loads; the copy of half
-// page k + 3 is issued while half page k + 1 is contracted.  One loop
-// iteration k (all in one basic block in the common case) contracts
-// QK^T of half page k + 1, then issues the PV of half page k interleaved with
-// the softmax of half page k + 1.
+// held in a ring of 4 slots, filled by direct HBM -> LDS loads three half
+// pages ahead of the one being contracted.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -655,10 +640,6 @@ constexpr int kHalfTok = 32;                          // tokens per ring slot
 constexpr int kSlotBytes = kHalfTok * kRowBytes;      // 36,864
 constexpr int kSlots = 4;
 constexpr int kRingBytes = kSlots * kSlotBytes;       // 147,456
-constexpr int kPBufOff = kRingBytes;                  // [wave][k2][lane] 16 B: P^T fragments
-constexpr int kABufOff = kPBufOff + 4 * 2 * 64 * 16;  // [wave][lane] float: rescale factor / row sum
-constexpr int kLdsBytes = kABufOff + 4 * 64 * 4;      // 156,672
-constexpr float kRescaleSlack = 8.f;                  // lazy max: rescale when the max grows by > 2^8
 
 // One direct HBM -> LDS load of 16 bytes per lane: lane i writes LDS bytes
 // [lds_addr + 16 i, +16) with the 16 bytes at gbase + voff.  Issued as inline
@@ -673,17 +654,6 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* gbase, uint
 // s_waitcnt immediates (gfx9 layout: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8) that wait for vector memory only.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-// Wait until at most `ahead` groups of 9 copies (one ring slot per wave) are
-// still in flight.  Issued through the builtin (not inline assembly) so that
-// the compiler's own wait tracking sees it: a value it loaded earlier (a
-// block-table entry) is then known to have arrived, and it does not add a
-// vmcnt(0) of its own that would drain the copies in flight.
-__device__ __forceinline__ void wait_copies(int ahead) {
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(18));
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(9));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-}
 
 // Workgroup barrier for LDS traffic only (outstanding copies stay in flight).
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -716,523 +686,11 @@ __device__ __forceinline__ int lane_id_fresh() {
     return v;
 }
 
-__device__ __forceinline__ void decode_bf16_body(const DecodeParams& p, const Piece& w, uint8_t* lds,
-                                                 const int wave) {
-    const int lane = lane_id_fresh();
-    const int tid = wave * 64 + lane;
-    const int G = lane >> 5;        // MFMA k-group of this lane (0/1)
-    const int lr = lane & 31;       // query row of this lane within its 32-row tile
-    const int b = w.b;
-    const int n = min(max(p.seq_lens[b], 0), p.max_pages * kPage);
-    const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
-    const uint8_t* kvbase = (const uint8_t*)p.kv;
-    lds_u8* const ring = (lds_u8*)lds;
-    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
-    // exchange buffers: P^T fragments of tile t at pbuf + 2048 t (k-step k2 at
-    // + 1024 k2), rescale factor / row sum of tile t at abuf + 64 t
-    lds_u8* const pbuf = (lds_u8*)lds + kPBufOff + lane * 16;
-    lds_f32* const abuf = (lds_f32*)(lds + kABufOff) + lane;
-    lds_u8* const pbuf_mine = pbuf + wave * 2048;
-    lds_f32* const abuf_mine = abuf + wave * 64;
-
-    // half pages of this unit that hold at least one token
-    const int half_begin = 2 * w.page_begin;
-    const int half_end = min(2 * w.page_end, (n + kHalfTok - 1) / kHalfTok);
-
-    // per-lane copy offsets within an 8-token group: LDS chunk q = 64 j + lane
-    // of copy j holds (token q / 72, position q % 72) of the group; wave w
-    // copies slot tokens 8w .. 8w + 7, so that position holds global chunk
-    // (position ^ swz(8 w + token)) of its token
-    int cp_off[9];
-#pragma unroll
-    for (int j = 0; j < 9; ++j) {
-        const int qc = j * 64 + lane;
-        const int t = qc / kRowChunks;
-        const int pc = qc - t * kRowChunks;
-        cp_off[j] = t * kRowBytes + ((pc ^ swz(8 * wave + t)) << 4);
-    }
-    // Page ids come through the scalar unit (the block table is read-only
-    // while the kernel runs, and a page id is the same for the whole wave):
-    // scalar loads are counted by lgkmcnt, so waiting for a page id never
-    // waits for the HBM -> LDS copies in flight, which vmcnt counts.  Callers
-    // pass half pages inside [half_begin, half_end).
-    const __attribute__((address_space(4))) int32_t* bt_s = (const __attribute__((address_space(4))) int32_t*)bt;
-    auto page_id = [&](int k) { return clamp_page(bt_s[k >> 1], p.num_pages); };
-    auto half_src_of = [&](int pid, int k) { return kvbase + (size_t)pid * kPageBytes + (k & 1) * kSlotBytes; };
-    auto half_src = [&](int k) { return half_src_of(page_id(k), k); };
-    auto slot_addr = [&](int k) { return ring_addr + ((k - half_begin) & 3) * kSlotBytes; };
-    auto slot_ptr = [&](int k) { return ring + ((k - half_begin) & 3) * kSlotBytes; };
-    auto issue_copy = [&](int k, int j, const uint8_t* src) {
-        dma16(slot_addr(k) + wave * 9 * 1024 + j * 1024, src + wave * 8 * kRowBytes, (uint32_t)cp_off[j]);
-    };
-    // prologue copies of the first three half pages (after the query, below);
-    // their page ids (half pages 0 and 1 share a page) are loaded now, so that
-    // the scalar loads' latency overlaps the query's
-    const int pid_first = half_begin < half_end ? page_id(half_begin) : 0;
-    const int pid_second = half_begin + 2 < half_end ? page_id(half_begin + 2) : 0;
-    auto issue_half = [&](int j3) {
-        if (half_begin + j3 < half_end) {
-            const uint8_t* src = half_src_of(j3 < 2 ? pid_first : pid_second, half_begin + j3);
-#pragma unroll
-            for (int j = 0; j < 9; ++j) issue_copy(half_begin + j3, j, src);
-        }
-    };
-    // this lane's query row, its visible length, and its Q^T fragments:
-    // k-step ks covers dims 16 ks .. + 15, lane holds dims 16 ks + 8 G .. + 7
-    const int row = w.mt * kMTile + wave * 32 + lr;
-    const bool row_ok = row < p.rows;
-    const int tq = row / p.heads;
-    // (capped at the end of this unit's token range, so that the dummy half
-    // page past the range is masked completely)
-    const int unit_end = half_end * kHalfTok;
-    const int nvis = min(p.causal ? max(n - (p.q_len - 1 - tq), 0) : n, unit_end);
-    // smallest visible length over every row of the workgroup: half pages
-    // entirely below it need no masking
-    const int nvis_min = min(p.causal ? max(n - (p.q_len - 1), 0) : n, unit_end);
-    // The query tile comes through the (still empty) LDS ring: wave w copies
-    // its 32 rows, 36,864 contiguous bytes, into ring slot w with 36 copies of
-    // 1 KB (whole cache lines; a direct load of the MFMA layout would touch 32
-    // rows x 32 bytes per instruction), waits for its own copies and reads
-    // its fragments back.  A row past the end of the tile copies the last row
-    // instead (its results are never stored).  Once every wave has its
-    // fragments, the ring takes the first three half pages of the cache.
-    bf16x8_t qf[36];
-    {
-        const uint8_t* qreq = (const uint8_t*)p.q + (size_t)b * p.rows * kRowBytes;
-        const int row0 = w.mt * kMTile + wave * 32;           // first row of this wave
-        const uint32_t qdst = ring_addr + wave * kSlotBytes;
-#pragma unroll
-        for (int j = 0; j < 36; ++j) {
-            // LDS chunk q of the wave's 32 rows is (row r, position pc), which
-            // holds chunk pc ^ swz(r) of that query row (the cache's layout)
-            const int qc = j * 64 + lane;
-            const int r = qc / kRowChunks;
-            const int pc = qc - r * kRowChunks;
-            const uint32_t src = (uint32_t)min(row0 + r, p.rows - 1) * kRowBytes + ((pc ^ swz(r)) << 4);
-            dma16(qdst + j * 1024, qreq, src);
-        }
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        // chunk 2 ks + G of row lr, read like a K fragment (bases for ks % 4,
-        // immediate 128 (ks / 4))
-        const lds_u8* qslot = ring + wave * kSlotBytes;
-        int qb[4];
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) qb[k4] = lr * kRowBytes + ((((2 * k4 + G) ^ swz(lr)) & 7) << 4);
-#pragma unroll
-        for (int ks = 0; ks < 36; ++ks) qf[ks] = *(const lds_bf16x8*)(qslot + qb[ks & 3] + (ks >> 2) * 128);
-    }
-    __syncthreads();   // every wave holds its query fragments: the ring is free
-    issue_half(0);
-    issue_half(1);
-    issue_half(2);
-
-    // LDS read offsets within a slot.  QK: token lr, chunk c(ks) = 2 ks + G at
-    // position (c & ~7) | ((c ^ swz(lr)) & 7); c(ks + 4) = c(ks) + 8, so four
-    // bases cover all 36 k-steps with immediate offsets 128 (ks / 4).
-    int qk_off[4];
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-        const int c = 2 * k4 + G;
-        qk_off[k4] = lr * kRowBytes + (((c ^ swz(lr)) & 7) << 4);
-    }
-    // PV transpose reads.  The 16-lane block bk = lane / 16 covers dims
-    // 16 (bk % 2) .. + 15 of a 32-dim tile and tokens 16 k2 + 4 G + e (first
-    // read) and + 8 (second read), e = (lane % 16) / 4; the lane supplies dims
-    // 4 (lane % 4) .. + 3 of its token.  Dim tile dq of quarter w starts at dim
-    // 128 w + 32 dq: chunk 16 w + 4 dq + 2 (bk % 2) + (lane % 4) / 2.  The
-    // first read's tokens have swizzle swz(4 G + e), the second read's that
-    // value ^ 2, i.e. byte offset ^ 32 (the XOR touches the 3 low chunk bits
-    // only, so 16 w and 4 (dq / 2) stay outside it, and every other term of
-    // the offset is a multiple of 128).
-    int tr_off[2];
-    {
-        const int li = lane & 15, e = li >> 2, cc = li & 3, dh = (lane >> 4) & 1;
-        const int t = 4 * G + e;
-        const int sw = swz(t);
-#pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2)
-            tr_off[d2] = t * kRowBytes + wave * 256 + (((4 * d2 + 2 * dh + (cc >> 1)) ^ sw) << 4) + (cc & 1) * 8;
-    }
-
-    // O^T accumulators: o[t][dq] = rows of tile t (32 t .. 32 t + 31) over dims
-    // 128 w + 32 dq .. + 31 (element i is dim + 8 (i / 4) + 4 G + i % 4).
-    f32x16 o[4][4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int dq = 0; dq < 4; ++dq) {
-            o[t][dq] = (f32x16)0.f;
-            asm volatile("" : "+a"(o[t][dq]));
-        }
-    float m = -INFINITY, l = 0.f;   // reference max (log2 units) and this lane's part of the row sum
-    // MFMA results of the inline-assembly PV read by VALU code: the compiler
-    // does not see those MFMAs, so their wait states are inserted here (more
-    // than an XDL write -> VALU read of a 16-pass MFMA needs).
-    auto pv_drain = [&]() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); };
-    // o *= a for the accumulators of one row tile, one register at a time
-    // through a single VGPR (the accumulators never leave the AGPRs).
-    auto scale_acc = [&](f32x16 (&ot)[4], float a) {
-#pragma unroll
-        for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float e = ot[dq][i];
-                float t;
-                asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                             : "+a"(e), "=&v"(t) : "v"(a));
-                ot[dq][i] = e;
-            }
-    };
-
-    auto kfrag = [&](lds_u8* cur, int ks) -> bf16x8_t {
-        return *(const lds_bf16x8*)(cur + qk_off[ks & 3] + (ks >> 2) * 128);
-    };
-    auto vfrag = [&](lds_u8* cur, int i) -> bf16x8_t {      // i = 4 k2 + dq
-        const int k2 = i >> 2, dq = i & 3;
-        const int off = tr_off[dq & 1] + (dq >> 1) * 128 + k2 * 16 * kRowBytes;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + off));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(cur + ((off ^ 32) + 8 * kRowBytes)));
-        return __builtin_bit_cast(bf16x8_t, (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-    };
-
-    // S^T of half page k: all 36 k-steps in one accumulation chain, K
-    // fragments read four k-steps ahead; `between(q)` runs after MFMA 4 q + 3
-    // (the copies of a later half page are issued there).
-    // The MFMAs are inline assembly with S tied to VGPRs, so that the compiler
-    // keeps every AGPR for O.  It does not see these MFMAs, so the wait states
-    // before VALU code reads S are inserted at the end.  The first MFMA of the chain
-    // takes the constant 0 as its accumulator (no VALU write precedes it);
-    // the others accumulate back to back into the same registers.
-    auto qk = [&](int k, f32x16& s, auto&& between) {
-        lds_u8* cur = slot_ptr(k);
-        constexpr int kKAhead = 6;
-        bf16x8_t kf[kKAhead];
-#pragma unroll
-        for (int ks = 0; ks < kKAhead; ++ks) kf[ks] = kfrag(cur, ks);
-#pragma unroll
-        for (int ks = 0; ks < 36; ++ks) {
-            const bf16x8_t a = kf[ks % kKAhead];
-            if (ks + kKAhead < 36) kf[ks % kKAhead] = kfrag(cur, ks + kKAhead);
-            if (ks == 0)
-                asm volatile("s_nop 3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                             : "=&v"(s) : "v"(a), "v"(qf[ks]));
-            else
-                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                             : "+v"(s) : "v"(a), "v"(qf[ks]));
-            if ((ks & 3) == 3) between(ks >> 2);
-        }
-        // wait states before VALU code reads the last MFMA's result
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));
-    };
-
-    // Online softmax of half page k for this lane's row: masks invisible
-    // tokens (element i is token 32 k + 8 (i / 4) + 4 G + i % 4), moves the
-    // reference max when the row max exceeds it by more than kRescaleSlack
-    // (log2 units), and returns
-    // the rescale factor of everything accumulated so far (1 when unchanged).
-    // Weights are exp2(c s - m) with c = scale * log2(e): one FMA and one exp.
-    auto mask_s = [&](int k, f32x16& s) {
-        const int lim = nvis - k * kHalfTok - 4 * G;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = (8 * (i >> 2) + (i & 3)) < lim ? s[i] : -INFINITY;
-    };
-    auto softmax = [&](int k, f32x16& s, bf16x8_t (&pf)[2], bool masked) -> float {
-        if (masked) mask_s(k, s);
-        float mx = s[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-        mx = pair_max(mx) * p.scale_log2;
-        const bool grow = mx > m + kRescaleSlack;
-        const float m_new = grow ? mx : m;
-        // (nothing has been accumulated while m is still -inf: no rescale)
-        const float alpha = grow && m != -INFINITY ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-        m = m_new;
-        const float c = p.scale_log2;
-        const float mneg = m == -INFINITY ? 0.f : -m;
-        float sum0 = 0.f, sum1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, mneg));
-            if (i & 1) sum1 += s[i]; else sum0 += s[i];
-        }
-        l = l * alpha + (sum0 + sum1);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pf[0][e] = (__bf16)s[e];
-            pf[1][e] = (__bf16)s[8 + e];
-        }
-        return alpha;
-    };
-    auto publish = [&](const bf16x8_t (&pf)[2], float alpha) {
-        *(lds_bf16x8*)pbuf_mine = pf[0];
-        *(lds_bf16x8*)(pbuf_mine + 1024) = pf[1];
-        *abuf_mine = alpha;
-    };
-
-    // O^T += V^T . P^T over half page k for all four row tiles, with the
-    // softmax of half page k + 1 cut into small pieces, one after each MFMA:
-    // a 32-clock MFMA hides about four VALU instructions, so the exp/max/
-    // convert work runs while the matrix core is busy (sched_barrier(0) pins
-    // the order).  Pieces: j = 0..3 running max over 4 logits each; 4 row max
-    // of the pair; 5 reference max, rescale factor, row sum rescale; 6..21
-    // one exp2 each; 22..25 bf16 conversion of 4 weights each; 26 row sum and
-    // publish.  Each of the 8 V^T fragments (2 k-steps x 4 dim tiles) feeds
-    // four MFMAs; fragments are read four ahead.  The MFMAs are inline
-    // assembly with O tied to its accumulation registers, so the compiler
-    // never moves O out of the AGPRs.  Their operands come straight from LDS
-    // reads (no VALU write precedes an MFMA read, which would need 2 wait
-    // states the compiler does not know to insert); the build scans the
-    // generated code for such a pair.
-    auto pv_softmax = [&](int k, const bf16x8_t (&pa)[4][2], const bf16x8_t (&vpre)[2], f32x16& s,
-                          bf16x8_t (&pf)[2], float& alpha_out, auto&& enter_next) {
-        lds_u8* cur = slot_ptr(k);
-        constexpr int kVAhead = 4;
-        bf16x8_t vf[kVAhead];
-        vf[0] = vpre[0];
-        vf[1] = vpre[1];
-        vf[2] = vfrag(cur, 2);
-        vf[3] = vfrag(cur, 3);
-        float mx, mneg, sum0 = 0.f, sum1 = 0.f;
-        const float c = p.scale_log2;
-        auto piece = [&](int j) {
-            if (j < 4) {
-                const int i = 4 * j;
-                const float v = fmaxf(fmaxf(s[i], s[i + 1]), fmaxf(s[i + 2], s[i + 3]));
-                mx = j == 0 ? v : fmaxf(mx, v);
-            } else if (j == 4) {
-                mx = pair_max(mx) * c;
-            } else if (j == 5) {
-                const bool grow = mx > m + kRescaleSlack;
-                const float m_new = grow ? mx : m;
-                // (nothing has been accumulated while m is still -inf: no rescale)
-                alpha_out = grow && m != -INFINITY ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
-                m = m_new;
-                mneg = m == -INFINITY ? 0.f : -m;
-                l *= alpha_out;
-            } else if (j < 22) {
-                const int i = j - 6;
-                s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, mneg));
-                // (the empty asm keeps each add here, between the MFMAs; the
-                // compiler would otherwise sink the whole sum to the loop end)
-                if (i & 1) {
-                    sum1 += s[i];
-                    asm volatile("" : "+v"(sum1));
-                } else {
-                    sum0 += s[i];
-                    asm volatile("" : "+v"(sum0));
-                }
-            } else if (j < 26) {
-                const int h = (j - 22) >> 1, e0 = 4 * ((j - 22) & 1);
-#pragma unroll
-                for (int e = e0; e < e0 + 4; ++e) pf[h][e] = (__bf16)s[8 * h + e];
-            } else if (j == 26) {
-                l += sum0 + sum1;
-                *(lds_bf16x8*)pbuf_mine = pf[0];
-                *(lds_bf16x8*)(pbuf_mine + 1024) = pf[1];
-                *abuf_mine = alpha_out;
-            }
-        };
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const bf16x8_t a = vf[i % kVAhead];
-            const int k2 = i >> 2, dq = i & 3;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                __builtin_amdgcn_sched_barrier(0);
-                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                             : "+a"(o[t][dq]) : "v"(a), "v"(pa[t][k2]));
-                if (t == 3 && i + kVAhead < 8) vf[i % kVAhead] = vfrag(cur, i + kVAhead);
-                // Every wave has consumed all of P(k) (its second k-step feeds
-                // the MFMAs from here on), so once all waves are past this
-                // point P(k+1) may overwrite it (piece 26).  The barrier needs
-                // no LDS wait: the reads of P(k) have returned.
-                if (i == 4 && t == 0) __builtin_amdgcn_s_barrier();
-                // the top-of-step barrier of the next half page, once P(k+1)
-                // is published (piece 26): the wait overlaps the last MFMAs
-                if (i == 7 && t == 0) enter_next();
-                __builtin_amdgcn_sched_barrier(0);
-                piece(4 * i + t);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // Zero the rows of half page k past the sequence end (they may hold
-    // anything, NaN included), so that a zero weight times V stays zero.
-    auto zero_tail = [&](int k) {
-        const int t0 = n - k * kHalfTok;     // callers pass half pages holding >= 1 token
-        if (t0 >= kHalfTok) return;
-        lds_u8* cur = slot_ptr(k);
-        for (int idx = tid; idx < (kHalfTok - t0) * kRowChunks; idx += 256) {
-            const int t = t0 + idx / kRowChunks;
-            const int c = idx % kRowChunks;
-            *(__attribute__((address_space(3))) i32x4*)(cur + t * kRowBytes + c * 16) = (i32x4)0;
-        }
-        lds_sync();
-    };
-    auto needs_mask = [&](int k) { return k * kHalfTok + kHalfTok > nvis_min; };
-
-    if (half_begin < half_end) {
-        bf16x8_t pa[4][2], pf_nxt[2];
-        float av[4];
-        // ---- prologue: S, softmax and P of the first half page
-        {
-            const int k = half_begin;
-            wait_copies(min(2, half_end - 1 - k));
-            lds_sync();
-            zero_tail(k);
-            f32x16 s;
-            qk(k, s, [&](int) {});
-            const float a0 = softmax(k, s, pf_nxt, needs_mask(k));
-            publish(pf_nxt, a0);
-        }
-        // Top of iteration k: the copies of half page k + 1 have landed, P(k)
-        // of every wave is visible, and every wave is past its reads of half
-        // page k - 1 (whose slot the next copy refills).
-        // copy source of iteration k: half page k + 3, or past the end of the
-        // range half page k again (into the dead slot of k - 1: a cache hit
-        // that keeps the loop body free of branches)
-        auto copy_half = [&](int k) { return k + 3 < half_end ? k + 3 : min(k, half_end - 1); };
-        int pid_copy;
-        // (the page id of iteration k's copy is loaded right before the
-        // barrier, whose lgkmcnt(0) covers the scalar load: no scalar load is
-        // then pending when the QK^T waits for its LDS reads)
-        auto enter_sync = [&](int k) {
-            wait_copies(k + 2 < half_end ? 1 : 0);
-            pid_copy = page_id(copy_half(k));
-            lds_sync();
-        };
-        auto enter = [&](int k) {
-            enter_sync(k);
-            if (k + 1 < half_end) zero_tail(k + 1);
-        };
-        // P(k) of all four tiles and their rescale factors, read late in the
-        // QK^T of half page k + 1 (after its last K fragment reads)
-        auto read_p = [&]() {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                pa[t][0] = *(const lds_bf16x8*)(pbuf + t * 2048);
-                pa[t][1] = *(const lds_bf16x8*)(pbuf + t * 2048 + 1024);
-                av[t] = abuf[t * 64];
-            }
-        };
-        int k = half_begin;
-        enter(k);
-        // Iteration k: QK^T of half page k + 1 (past the last half page a
-        // dummy, fully masked) while the copy of half page k + 3 is issued,
-        // then the PV of half page k interleaved with the softmax of k + 1.
-        for (;;) {
-            f32x16 s;
-            const uint8_t* csrc_w = half_src_of(pid_copy, copy_half(k)) + wave * 8 * kRowBytes;
-            const uint32_t cdst = slot_addr(k + 3) + wave * 9 * 1024;
-            // (the first two V^T fragments of half page k are read while the
-            // last QK^T MFMA runs)
-            bf16x8_t vpre[2];
-            qk(k + 1, s, [&](int j) {
-                dma16(cdst + j * 1024, csrc_w, (uint32_t)cp_off[j]);
-                if (j == 7) read_p();
-                if (j == 8) {
-                    vpre[0] = vfrag(slot_ptr(k), 0);
-                    vpre[1] = vfrag(slot_ptr(k), 1);
-                }
-            });
-            if (__builtin_expect(__any(av[0] != 1.f || av[1] != 1.f || av[2] != 1.f || av[3] != 1.f), 0)) {
-                // a row max moved: rescale what the tile has accumulated so far
-                pv_drain();
-#pragma unroll
-                for (int t = 0; t < 4; ++t) scale_acc(o[t], av[t]);
-            }
-            if (needs_mask(k + 1)) mask_s(k + 1, s);
-            float a_nxt;
-            // (the top of iteration k + 1 runs inside the PV, after P(k + 1) is
-            // published; only the rare zeroing of a sequence tail stays here)
-            const bool more = k + 1 < half_end;
-            pv_softmax(k, pa, vpre, s, pf_nxt, a_nxt, [&]() {
-                if (more) enter_sync(k + 1);
-            });
-            if (!more) break;
-            ++k;
-            if (k + 1 < half_end) zero_tail(k + 1);
-        }
-    }
-
-    // ---- epilogue: o = O / l for all four row tiles over this wave's dims, and
-    //      lse = ln(sum exp) for this wave's own rows.
-    // No copy may still be writing this workgroup's LDS when it exits.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    pv_drain();
-    const float l_own = pair_sum(l);
-    __syncthreads();                      // every wave is done reading the exchange buffers
-    *abuf_mine = l_own;
-    __syncthreads();
-    // element i of dim tile dq is dim 128 w + 32 dq + 8 (i / 4) + 4 G + i % 4.
-    // Rows leave through the idle ring: per half (64 rows) every wave writes
-    // its dims of the rows, scaled by 1 / l, as fp32 (a single piece to an
-    // fp32 output) or bf16 (a bf16 output, or a split partial), into rows of
-    // 512 e + 16 bytes; then the workgroup stores whole contiguous row pieces.
-    const int dim0 = 128 * wave + 4 * G;
-    {
-        const bool f32 = w.nsplit == 1 && !p.out_bf16;
-        const int e = f32 ? 4 : 2;
-        const int st_row = kV * e + 16;
-        const int row_chunks = kV * e / 16;
-        uint8_t* gbase = w.nsplit > 1 ? (uint8_t*)p.ws_o + (size_t)w.slot * kMTile * kV * 2
-                                      : (uint8_t*)p.out + ((size_t)b * p.rows + (size_t)w.mt * kMTile) * kV * e;
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const int t = 2 * hf + tt;
-                const float lt = abuf[t * 64];
-                const float inv = lt > 0.f ? 1.f / lt : 0.f;
-                lds_u8* srow = ring + (32 * tt + lr) * st_row + e * dim0;
-#pragma unroll
-                for (int dq = 0; dq < 4; ++dq)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const f32x4 v = (f32x4){o[t][dq][4 * q4], o[t][dq][4 * q4 + 1], o[t][dq][4 * q4 + 2],
-                                                o[t][dq][4 * q4 + 3]} * inv;
-                        if (f32) {
-                            *(__attribute__((address_space(3))) f32x4*)(srow + 4 * (32 * dq + 8 * q4)) = v;
-                        } else {
-                            __bf16 __attribute__((ext_vector_type(4))) h;
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) h[i] = (__bf16)v[i];
-                            *(lds_i16x4*)(srow + 2 * (32 * dq + 8 * q4)) = __builtin_bit_cast(i16x4, h);
-                        }
-                    }
-            }
-            __syncthreads();
-            for (int i = (int)tid; i < 64 * row_chunks; i += 256) {
-                const int rl = i / row_chunks, c = i - rl * row_chunks;
-                if (w.mt * kMTile + 64 * hf + rl < p.rows)
-                    *(i32x4*)(gbase + (size_t)(64 * hf + rl) * kV * e + 16 * c) =
-                        *(const __attribute__((address_space(3))) i32x4*)(ring + rl * st_row + 16 * c);
-            }
-            __syncthreads();
-        }
-    }
-    if (row_ok && G == 0) {
-        const float lse = l_own > 0.f ? (m + __log2f(l_own)) * kLn2 : -INFINITY;
-        if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
-        else p.ws_lse[(size_t)w.slot * kMTile + (row - w.mt * kMTile)] = lse;
-    }
-}
-
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void decode_bf16_kernel(DecodeParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes];
-    const WorkItem wi = decode_work_item(p, lds);
-    if (wi.b < 0) return;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for_each_piece<false>(p, wi, [&](const Piece& pc) { decode_bf16_body(p, pc, lds, wave); });
-}
-
 // ---------------------------------------------------------------------------
 // split-KV decode, bf16 cache, two waves per SIMD with split roles
 //
-// Workgroup = 8 waves over kMTile = 128 query rows (the work items of the
-// one-wave-per-SIMD kernel).  One wave per SIMD can only read about 24 bytes
+// Workgroup = 8 waves (two per SIMD) over one work item of kMTile = 128
+// query rows.  One wave per SIMD can only read about 24 bytes
 // of LDS per clock, while QK^T with Q resident in registers consumes a 1 KB
 // K fragment per 32-clock MFMA; a second wave on each SIMD supplies MFMAs of
 // its own while the first waits on LDS.  The register file decides the
@@ -1903,12 +1361,10 @@ void decode_bf16_ab_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// split-KV decode, OCP fp8 e4m3 cache and query
+// split-KV decode, OCP fp8 e4m3 cache and query: shared layout and helpers
 //
-// Same schedule as the bf16 kernel (128 query rows per workgroup, wave w owns
-// rows 32 w .. 32 w + 31 for QK^T and the softmax, wave pairs share their
-// P^T tiles so that every V^T fragment feeds two MFMAs, a 4-slot LDS ring
-// filled by direct HBM -> LDS loads), with these differences:
+// The work items, the ring of 4 LDS slots and the direct HBM -> LDS loads
+// are the bf16 kernel's, with these differences:
 //  - one ring slot holds a whole 64-token page (64 x 576 bytes = 36,864);
 //  - both contractions run on v_mfma_f32_32x32x64_f8f6f4 (fp8 x fp8 ->
 //    fp32, K = 64 per instruction):
@@ -1922,9 +1378,8 @@ void decode_bf16_ab_kernel(DecodeParams p) {
 //    few 1e-2 on short, peaked rows).  Weights are offset by 2^3 so that they
 //    span (0, 2^8]; the reference max takes integer values (log2 units) and
 //    moves once the row max exceeds it by 5, so every rescale factor is an
-//    exact power of two 2^-d.  The pair exchanges hi and lo through LDS; d
-//    (8 bits) rides in the sign bits of hi bytes 0-7, which are free because
-//    the weights are non-negative;
+//    exact power of two 2^-d; d (8 bits) rides in the sign bits of hi bytes
+//    0-7, which are free because the weights are non-negative;
 //  - the per-tensor cache scale multiplies the logits (folded into the exp2
 //    factor) and the output (in the epilogue); the query scale arrives folded
 //    into `scale`.
@@ -1947,10 +1402,7 @@ constexpr int kPageBytes8 = kPage * kRowBytes8;    // 36,864 = one ring slot
 constexpr int kRowChunks8 = kRowBytes8 / 16;       // 36
 constexpr float kRescaleSlack8 = 5.f;              // reference max moves when the max grows by > 2^5
 constexpr float kWeightOffset8 = 3.f;              // weights are exp2(s c - m + 3) <= 2^8 < 448
-constexpr int kPLoOff8 = kRingBytes + 4 * 2048;    // [wave][half][lane] 16 B: lo P^T terms (hi at kPBufOff)
-constexpr int kLdsBytes8 = kPLoOff8 + 4 * 2048;    // 163,840 (the whole LDS)
 static_assert(kPageBytes8 == kSlotBytes, "an fp8 page fills exactly one ring slot");
-static_assert(kLdsBytes8 <= 163840, "LDS budget");
 
 // d (0..255) into the sign bits of the bytes of two dwords (bits 8 i + 7),
 // and back: each is a multiply that spreads / gathers one nibble without carries.
@@ -1974,461 +1426,13 @@ __device__ __forceinline__ int pack_e4m3(float a, float b, float c, float d, int
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-__device__ __forceinline__ void decode_fp8_body(const DecodeParams& p, const Piece& w, uint8_t* lds,
-                                                const int wave) {
-    const int lane = lane_id_fresh();
-    const int tid = wave * 64 + lane;
-    const int h = wave & 1;         // PV: which half of the 512 output dims
-    const int G = lane >> 5;        // MFMA k-half of this lane (0/1)
-    const int lr = lane & 31;       // query row (QK B operand) / token (QK A operand) of this lane
-    const int b = w.b;
-    const int n = min(max(p.seq_lens[b], 0), p.max_pages * kPage);
-    const int32_t* bt = p.block_table + (size_t)b * p.max_pages;
-    const uint8_t* kvbase = (const uint8_t*)p.kv;
-    lds_u8* const ring = (lds_u8*)lds;
-    const uint32_t ring_addr = (uint32_t)(uintptr_t)ring;
-    lds_u8* const pbuf_mine = (lds_u8*)lds + kPBufOff + wave * 2048 + lane * 16;
-    lds_u8* const pbuf_other = (lds_u8*)lds + kPBufOff + (wave ^ 1) * 2048 + lane * 16;
-    lds_u8* const plo_mine = (lds_u8*)lds + kPLoOff8 + wave * 2048 + lane * 16;
-    lds_u8* const plo_other = (lds_u8*)lds + kPLoOff8 + (wave ^ 1) * 2048 + lane * 16;
-    // after the loop the hi buffer carries the row sums
-    lds_f32* const lsum_mine = (lds_f32*)(lds + kPBufOff) + wave * 64 + lane;
-    lds_f32* const lsum_other = (lds_f32*)(lds + kPBufOff) + (wave ^ 1) * 64 + lane;
-    const float kv_scale = *p.kv_scale;
-    const float c_exp = p.scale_log2 * kv_scale;   // logits in log2 units per unit of q.k
-
-    // pages of this unit that hold at least one token
-    const int pg_begin = w.page_begin;
-    const int pg_end = min(w.page_end, (n + kPage - 1) / kPage);
-
-    // copy offsets: wave w copies tokens 16 w .. 16 w + 15 of a page; LDS chunk
-    // q = 64 j + lane of copy j holds (token q / 36, position q % 36) = global
-    // chunk (position ^ swz8(token)) of that token
-    int cp_off[9];
-#pragma unroll
-    for (int j = 0; j < 9; ++j) {
-        const int qc = j * 64 + lane;
-        const int t = qc / kRowChunks8;
-        const int pc = qc - t * kRowChunks8;
-        cp_off[j] = t * kRowBytes8 + ((pc ^ swz8(t)) << 4);
-    }
-    // page ids through the scalar unit (see the bf16 kernel); callers pass
-    // pages inside [pg_begin, pg_end)
-    const __attribute__((address_space(4))) int32_t* bt_s = (const __attribute__((address_space(4))) int32_t*)bt;
-    auto page_src_of = [&](int pid) { return kvbase + (size_t)pid * kPageBytes8; };
-    auto page_id = [&](int k) { return clamp_page(bt_s[k], p.num_pages); };
-    auto slot_addr = [&](int k) { return ring_addr + ((k - pg_begin) & 3) * kSlotBytes; };
-    auto slot_ptr = [&](int k) { return ring + ((k - pg_begin) & 3) * kSlotBytes; };
-    // prologue: the first page, the query, then two more pages; loads retire
-    // in issue order, so the first QK^T (which needs the first page and the
-    // query) does not wait for the other two.  The three page ids are loaded
-    // together up front.
-    const int pid0 = pg_begin < pg_end ? page_id(pg_begin) : 0;
-    const int pid1 = pg_begin + 1 < pg_end ? page_id(pg_begin + 1) : 0;
-    const int pid2 = pg_begin + 2 < pg_end ? page_id(pg_begin + 2) : 0;
-    auto issue_page = [&](int j3) {
-        if (pg_begin + j3 < pg_end) {
-            const uint8_t* src = page_src_of(j3 == 0 ? pid0 : j3 == 1 ? pid1 : pid2) + wave * 16 * kRowBytes8;
-            const uint32_t dst = slot_addr(pg_begin + j3) + wave * 9 * 1024;
-#pragma unroll
-            for (int j = 0; j < 9; ++j) dma16(dst + j * 1024, src, (uint32_t)cp_off[j]);
-        }
-    };
-    issue_page(0);
-
-    const int row = w.mt * kMTile + wave * 32 + lr;
-    const bool row_ok = row < p.rows;
-    const int tq = row / p.heads;
-    const int unit_end = pg_end * kPage;
-    const int nvis = min(p.causal ? max(n - (p.q_len - 1 - tq), 0) : n, unit_end);
-    const int nvis_min = min(p.causal ? max(n - (p.q_len - 1), 0) : n, unit_end);
-    // Q^T fragments: k-step ks covers dims 64 ks .. + 63; lane holds dims 64 ks + 32 G .. + 31
-    i32x8 qf[9];
-    {
-        const uint8_t* qr = (const uint8_t*)p.q + ((size_t)b * p.rows + min(row, p.rows - 1)) * kQK + 32 * G;
-#pragma unroll
-        for (int ks = 0; ks < 9; ++ks) {
-            const i32x4 lo = *(const i32x4*)(qr + 64 * ks);
-            const i32x4 hi = *(const i32x4*)(qr + 64 * ks + 16);
-            qf[ks] = cat8(lo, hi);
-        }
-    }
-    issue_page(1);
-    issue_page(2);
-    // QK A fragments: token 32 tau + lr, chunks 4 ks + 2 G + e (e = 0, 1) at
-    // positions 4 ks + ((2 G + e) ^ swz8(lr)): two bases, immediates 64 ks and
-    // 32 rows (18,432 bytes) per token tile
-    int qk_off[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) qk_off[e] = lr * kRowBytes8 + (((2 * G + e) ^ swz8(lr)) << 4);
-    // PV A fragments (V^T, 32 dims x 64 tokens) by transpose reads: in each
-    // 16-lane group gl = lane / 16, source lane s = lane % 16 reads 8 bytes =
-    // dims D0 + 8 (s % 2) .. + 7 of token 16 r + 4 (gl / 2) + 8 (s / 8) + (s / 2) % 4
-    // (read r = 0..3), D0 = 256 h + 32 dt + 16 (gl % 2); the group then holds
-    // dims D0 .. D0 + 15 (one per lane) over those 8 tokens.  The token of byte
-    // j of k-half kh is then 32 (j / 16) + 8 ((j / 4) % 4) + 4 kh + j % 4, the
-    // same token the S^T accumulator element (j % 16) of token tile j / 16
-    // holds in lane (row, kh): the P^T operand is the accumulators in order.
-    int tr_off[2];
-    {
-        const int gl = lane >> 4, s = lane & 15, kh = gl >> 1;
-        const int t0 = 4 * kh + 8 * (s >> 3) + ((s >> 1) & 3);
-#pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2) {
-            const int c = 16 * h + 2 * d2 + (gl & 1);
-            tr_off[d2] = t0 * kRowBytes8 + ((c ^ swz8(t0)) << 4) + 8 * (s & 1);
-        }
-    }
-
-    f32x16 o0[8], o1[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        o0[dt] = (f32x16)0.f;
-        o1[dt] = (f32x16)0.f;
-        asm volatile("" : "+a"(o0[dt]));
-        asm volatile("" : "+a"(o1[dt]));
-    }
-    float m = -INFINITY, l = 0.f;
-
-    auto kfrag = [&](lds_u8* cur, int tau, int ks) -> i32x8 {
-        const i32x4 lo = *(const lds_i32x4*)(cur + qk_off[0] + tau * 32 * kRowBytes8 + 64 * ks);
-        const i32x4 hi = *(const lds_i32x4*)(cur + qk_off[1] + tau * 32 * kRowBytes8 + 64 * ks);
-        return cat8(lo, hi);
-    };
-    auto vfrag = [&](lds_u8* cur, int dt) -> i32x8 {
-        const int off = tr_off[dt & 1] + (dt >> 1) * 64;
-        const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + off));
-        const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + off + 16 * kRowBytes8));
-        const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + off + 32 * kRowBytes8));
-        const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(cur + off + 48 * kRowBytes8));
-        return (i32x8){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-    };
-    auto pv_drain = [&]() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); };
-    auto scale_acc = [&](f32x16 (&o)[8], float a) {
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float e = o[dt][i];
-                float t;
-                asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                             : "+a"(e), "=&v"(t) : "v"(a));
-                o[dt][i] = e;
-            }
-    };
-
-    // S^T of page k: two token tiles, 9 k-steps each, as two interleaved
-    // accumulation chains (inline assembly, S in VGPRs; the wait states before
-    // VALU code reads S are inserted at the end); K fragments are read two
-    // k-steps ahead; `between(q)` runs after MFMA pair q (copies go there).
-    auto qk = [&](int k, f32x16& s0, f32x16& s1, auto&& between) {
-        lds_u8* cur = slot_ptr(k);
-        i32x8 kf0[2], kf1[2];
-        kf0[0] = kfrag(cur, 0, 0);
-        kf1[0] = kfrag(cur, 1, 0);
-        kf0[1] = kfrag(cur, 0, 1);
-        kf1[1] = kfrag(cur, 1, 1);
-#pragma unroll
-        for (int ks = 0; ks < 9; ++ks) {
-            const i32x8 a0 = kf0[ks & 1], a1 = kf1[ks & 1];
-            if (ks + 2 < 9) {
-                kf0[ks & 1] = kfrag(cur, 0, ks + 2);
-                kf1[ks & 1] = kfrag(cur, 1, ks + 2);
-            }
-            if (ks == 0) {
-                asm volatile("s_nop 3\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0"
-                             : "=&v"(s0) : "v"(a0), "v"(qf[ks]));
-                asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0"
-                             : "=&v"(s1) : "v"(a1), "v"(qf[ks]));
-            } else {
-                asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
-                             : "+v"(s0) : "v"(a0), "v"(qf[ks]));
-                asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0"
-                             : "+v"(s1) : "v"(a1), "v"(qf[ks]));
-            }
-            between(ks);
-        }
-        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
-    };
-
-    // element i of token tile tau is token 64 k + 32 tau + 8 (i / 4) + 4 G + i % 4
-    auto mask_s = [&](int k, f32x16& s0, f32x16& s1) {
-        const int lim = nvis - k * kPage - 4 * G;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int t = 8 * (i >> 2) + (i & 3);
-            s0[i] = t < lim ? s0[i] : -INFINITY;
-            s1[i] = t + 32 < lim ? s1[i] : -INFINITY;
-        }
-    };
-    auto needs_mask = [&](int k) { return k * kPage + kPage > nvis_min; };
-
-    // Online softmax of one page for this lane's row (64 tokens, 32 per lane)
-    // as 30 small pieces, one after each PV MFMA (a 64-clock MFMA hides about
-    // a dozen VALU instructions; a larger block would leave the matrix core
-    // idle).  Produces the weights as hi/lo e4m3 operands (bytes 0-15 from
-    // tile 0, 16-31 from tile 1) and d_out, the rescale shift of everything
-    // accumulated so far (0 when unchanged).
-    //   j = 0..3   running max over 8 logits each
-    //   j = 4      row max of the pair, reference max, shift, row sum rescale
-    //   j = 5..28  4 groups of 8 logits (s0[0..7], s0[8..15], s1[0..7], s1[8..15]),
-    //              6 pieces each: exp2 of 4 + 4, then per 4 weights the hi
-    //              code (and its value), then the lo code
-    //   j = 29     row sum, publish
-    struct SoftmaxState {
-        float mx, mneg, sum;
-        int hw;
-        float h0, h1, h2, h3;
-    };
-    auto softmax_piece = [&](f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out, SoftmaxState& st,
-                             int j) {
-        if (j < 4) {
-            f32x16& s = j < 2 ? s0 : s1;
-            const int i0 = (j & 1) * 8;
-            float mx = j == 0 ? s[0] : fmaxf(st.mx, s[i0]);
-#pragma unroll
-            for (int i = i0 + 1; i < i0 + 8; ++i) mx = fmaxf(mx, s[i]);
-            st.mx = mx;
-        } else if (j == 4) {
-            const float mx = pair_max(st.mx) * c_exp;
-            const bool grow = mx > m + kRescaleSlack8;
-            const float m_new = grow ? __builtin_ceilf(mx) : m;
-            // (nothing has been accumulated while m is still -inf: no rescale)
-            d_out = grow && m != -INFINITY ? (int)fminf(m_new - m, 255.f) : 0;
-            m = m_new;
-            l *= __builtin_ldexpf(1.f, -d_out);
-            st.mneg = m == -INFINITY ? 0.f : kWeightOffset8 - m;
-            st.sum = 0.f;
-        } else if (j < 29) {
-            const int g = (j - 5) / 6, part = (j - 5) % 6;
-            f32x16& s = g < 2 ? s0 : s1;
-            const int i0 = (g & 1) * 8;
-            if (part < 2) {
-#pragma unroll
-                for (int i = i0 + 4 * part; i < i0 + 4 * part + 4; ++i) {
-                    s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c_exp, st.mneg));
-                    st.sum += s[i];
-                    asm volatile("" : "+v"(st.sum));   // keeps the add here (see the bf16 kernel)
-                }
-            } else {
-                const int q = (part - 2) >> 1, i = i0 + 4 * q, r = 2 * g + q;
-                if (((part - 2) & 1) == 0) {
-                    st.hw = pack_e4m3(s[i], s[i + 1], s[i + 2], s[i + 3]);
-                    const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(st.hw, false);
-                    const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(st.hw, true);
-                    st.h0 = h01[0]; st.h1 = h01[1]; st.h2 = h23[0]; st.h3 = h23[1];
-                    ph[r] = st.hw;
-                } else {
-                    pl[r] = pack_e4m3(s[i] - st.h0, s[i + 1] - st.h1, s[i + 2] - st.h2, s[i + 3] - st.h3);
-                }
-            }
-        } else if (j == 29) {
-            l += st.sum;
-            // publish (d in the sign bits of hi bytes 0-7; the own operand stays clean)
-            const int e0 = ph[0] | spread_nibble(d_out), e1 = ph[1] | spread_nibble(d_out >> 4);
-            *(lds_i32x4*)pbuf_mine = (i32x4){e0, e1, ph[2], ph[3]};
-            *(lds_i32x4*)(pbuf_mine + 1024) = (i32x4){ph[4], ph[5], ph[6], ph[7]};
-            *(lds_i32x4*)plo_mine = (i32x4){pl[0], pl[1], pl[2], pl[3]};
-            *(lds_i32x4*)(plo_mine + 1024) = (i32x4){pl[4], pl[5], pl[6], pl[7]};
-        }
-    };
-
-    // O^T += V^T . (P_hi + P_lo)^T over page k for both tiles of the pair (8
-    // dim tiles x 2 row tiles x 2 terms), with the softmax of page k + 1 in
-    // pieces between the MFMAs.  V^T fragments are read two ahead and each
-    // feeds four MFMAs.  MFMAs as inline assembly with O tied to its AGPRs;
-    // their operands come from LDS reads and registers no VALU instruction
-    // writes right before them (the build checks the wait states).
-    auto pv_softmax = [&](int k, const i32x8& ph_own, const i32x8& pl_own, const i32x8& ph_oth,
-                          const i32x8& pl_oth, f32x16& s0, f32x16& s1, i32x8& ph, i32x8& pl, int& d_out,
-                          auto&& enter_next) {
-        lds_u8* cur = slot_ptr(k);
-        i32x8 vf[2];
-        vf[0] = vfrag(cur, 0);
-        vf[1] = vfrag(cur, 1);
-        SoftmaxState st;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const i32x8 a = vf[dt & 1];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (q == 0)
-                    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(o0[dt]) : "v"(a), "v"(ph_own));
-                else if (q == 1)
-                    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(o1[dt]) : "v"(a), "v"(ph_oth));
-                else if (q == 2)
-                    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(o0[dt]) : "v"(a), "v"(pl_own));
-                else
-                    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(o1[dt]) : "v"(a), "v"(pl_oth));
-                if (q == 3 && dt + 2 < 8) vf[dt & 1] = vfrag(cur, dt + 2);
-                // Both waves of the pair have consumed the other's P(k) terms
-                // (the MFMAs above took them), so once both are past this
-                // point P(k+1) may overwrite them (piece 29).  No LDS wait is
-                // needed: those reads have returned.
-                if (dt == 0 && q == 3) __builtin_amdgcn_s_barrier();
-                // the top-of-step barrier of the next page, once P(k+1) is
-                // published (piece 29): the wait overlaps the last MFMAs
-                if (dt == 7 && q == 2) enter_next();
-                __builtin_amdgcn_sched_barrier(0);
-                softmax_piece(s0, s1, ph, pl, d_out, st, 4 * dt + q);
-            }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // Zero the rows of page k past the sequence end (they may hold anything,
-    // NaN included), so that a zero weight times V stays zero.
-    auto zero_tail = [&](int k) {
-        const int t0 = n - k * kPage;     // callers pass pages holding >= 1 token
-        if (t0 >= kPage) return;
-        lds_u8* cur = slot_ptr(k);
-        for (int idx = tid; idx < (kPage - t0) * kRowChunks8; idx += 256) {
-            const int t = t0 + idx / kRowChunks8;
-            const int c = idx % kRowChunks8;
-            *(lds_i32x4*)(cur + t * kRowBytes8 + c * 16) = (i32x4)0;
-        }
-        lds_sync();
-    };
-
-    if (pg_begin < pg_end) {
-        i32x8 ph_cur, pl_cur, ph_nxt, pl_nxt, ph_oth, pl_oth;
-        int d_cur, d_oth;
-        {
-            const int k = pg_begin;
-            wait_copies(min(2, pg_end - 1 - k));
-            lds_sync();
-            zero_tail(k);
-            f32x16 s0, s1;
-            qk(k, s0, s1, [&](int) {});
-            if (needs_mask(k)) mask_s(k, s0, s1);
-            SoftmaxState st;
-#pragma unroll
-            for (int j = 0; j < 30; ++j) softmax_piece(s0, s1, ph_cur, pl_cur, d_cur, st, j);
-        }
-        // top of iteration k: page k + 1 landed, P(k) of both waves visible,
-        // every wave past its reads of page k - 1.
-        // Copy source of iteration k: page k + 3, or past the end of the range
-        // page k again (into the dead slot of k - 1); its page id is loaded
-        // right before the barrier (see the bf16 kernel)
-        auto copy_page = [&](int k) { return k + 3 < pg_end ? k + 3 : min(k, pg_end - 1); };
-        int pid_copy;
-        auto enter_sync = [&](int k) {
-            wait_copies(k + 2 < pg_end ? 1 : 0);
-            pid_copy = page_id(copy_page(k));
-            lds_sync();
-        };
-        auto enter = [&](int k) {
-            enter_sync(k);
-            if (k + 1 < pg_end) zero_tail(k + 1);
-        };
-        // the partner's P(k) terms and rescale shift (published before the
-        // top-of-step barrier), read late in the QK^T of page k + 1
-        auto read_partner = [&]() {
-            const i32x4 h0 = *(const lds_i32x4*)pbuf_other;
-            const i32x4 h1 = *(const lds_i32x4*)(pbuf_other + 1024);
-            const i32x4 l0 = *(const lds_i32x4*)plo_other;
-            const i32x4 l1 = *(const lds_i32x4*)(plo_other + 1024);
-            d_oth = gather_nibble(h0[0]) | (gather_nibble(h0[1]) << 4);
-            ph_oth = (i32x8){h0[0] & 0x7f7f7f7f, h0[1] & 0x7f7f7f7f, h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-            pl_oth = cat8(l0, l1);
-        };
-        int k = pg_begin;
-        enter(k);
-        for (;;) {
-            f32x16 s0, s1;
-            const uint8_t* csrc_w = page_src_of(pid_copy) + wave * 16 * kRowBytes8;
-            const uint32_t cdst = slot_addr(k + 3) + wave * 9 * 1024;
-            qk(k + 1, s0, s1, [&](int j) {
-                dma16(cdst + j * 1024, csrc_w, (uint32_t)cp_off[j]);
-                if (j == 6) read_partner();
-            });
-            if (__builtin_expect(__any(d_cur != 0 || d_oth != 0), 0)) {
-                pv_drain();
-                scale_acc(o0, __builtin_ldexpf(1.f, -d_cur));
-                scale_acc(o1, __builtin_ldexpf(1.f, -d_oth));
-            }
-            if (needs_mask(k + 1)) mask_s(k + 1, s0, s1);
-            int d_nxt;
-            // (the top of iteration k + 1 runs inside the PV, after P(k + 1) is
-            // published; only the rare zeroing of a sequence tail stays here)
-            const bool more = k + 1 < pg_end;
-            pv_softmax(k, ph_cur, pl_cur, ph_oth, pl_oth, s0, s1, ph_nxt, pl_nxt, d_nxt, [&]() {
-                if (more) enter_sync(k + 1);
-            });
-            if (!more) break;
-            ++k;
-            ph_cur = ph_nxt;
-            pl_cur = pl_nxt;
-            d_cur = d_nxt;
-            if (k + 1 < pg_end) zero_tail(k + 1);
-        }
-    }
-
-    // ---- epilogue: o = kv_scale O / l, lse = ln(sum exp(s)) for both tiles of the pair.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    pv_drain();
-    const float l_own = pair_sum(l);
-    __syncthreads();
-    *lsum_mine = l_own;
-    __syncthreads();
-    const float l_oth = *lsum_other;
-    const int row_oth = w.mt * kMTile + (wave ^ 1) * 32 + lr;
-    const float inv_own = l_own > 0.f ? kv_scale / l_own : 0.f;
-    const float inv_oth = l_oth > 0.f ? kv_scale / l_oth : 0.f;
-    const int dim0 = 256 * h + 4 * G;
-    auto store_tile = [&](const f32x16 (&o)[8], int r, float inv) {
-        if (r >= p.rows) return;
-        const int rit = r - w.mt * kMTile;
-        if (w.nsplit > 1 || p.out_bf16) {
-            // a bf16 output row, or a split partial (bf16)
-            __bf16* dst = w.nsplit > 1 ? (__bf16*)p.ws_o + ((size_t)w.slot * kMTile + rit) * kV + dim0
-                                       : (__bf16*)p.out + ((size_t)b * p.rows + r) * kV + dim0;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    __bf16 __attribute__((ext_vector_type(4))) v;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = (__bf16)(o[dt][4 * q4 + i] * inv);
-                    *(__bf16 __attribute__((ext_vector_type(4)))*)(dst + 32 * dt + 8 * q4) = v;
-                }
-        } else {
-            float* dst = (float*)p.out + ((size_t)b * p.rows + r) * kV + dim0;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    *(f32x4*)(dst + 32 * dt + 8 * q4) =
-                        (f32x4){o[dt][4 * q4], o[dt][4 * q4 + 1], o[dt][4 * q4 + 2], o[dt][4 * q4 + 3]} * inv;
-        }
-    };
-    store_tile(o0, row, inv_own);
-    store_tile(o1, row_oth, inv_oth);
-    if (row_ok && G == 0) {
-        // l sums exp2(s c - m + 4): ln sum exp = (m - 4 + log2 l) ln 2
-        const float lse = l_own > 0.f ? (m - kWeightOffset8 + __log2f(l_own)) * kLn2 : -INFINITY;
-        if (w.nsplit == 1) p.lse[(size_t)b * p.rows + row] = lse;
-        else p.ws_lse[(size_t)w.slot * kMTile + (row - w.mt * kMTile)] = lse;
-    }
-}
-
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void decode_fp8_kernel(DecodeParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[kLdsBytes8];
-    const WorkItem wi = decode_work_item(p, lds);
-    if (wi.b < 0) return;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    for_each_piece<true>(p, wi, [&](const Piece& pc) { decode_fp8_body(p, pc, lds, wave); });
-}
-
 // ---------------------------------------------------------------------------
 // split-KV decode, fp8 cache, two waves per SIMD with split roles
 //
-// Workgroup = 8 waves over the same work items (kMTile = 128 query rows).
-// With one wave per SIMD (the kernel above) the softmax's VALU work (two e4m3
-// weight terms per logit) and the MFMAs of the same wave take turns; here the
-// two waves of a SIMD split the work of one 32-row tile (rows 32 s .. 32 s +
+// Workgroup = 8 waves (two per SIMD) over one work item of kMTile = 128 query
+// rows.  The softmax's VALU work (two e4m3 weight terms per logit) would take
+// turns with the MFMAs on a single wave; the two waves of a SIMD split the
+// work of one 32-row tile (rows 32 s .. 32 s +
 // 31 on SIMD s):
 //  - wave A holds the tile's Q^T (9 k-steps, 72 VGPRs), contracts QK^T over the
 //    page (2 token tiles x 9 k-steps), runs the online softmax (reference max
@@ -2448,8 +1452,8 @@ void decode_fp8_kernel(DecodeParams p) {
 //         reads of page k - 1 (B refills that slot with page k + 3);
 //   M(k): B holds P(k) in registers, so A may overwrite it with P(k + 1).
 // Phase 1 (T(k) .. M(k)): A contracts QK^T of page k + 1 (18 MFMAs); B reads
-// P(k) (the rescale shift d rides in the sign bits of hi bytes 0 - 7, as in
-// the kernel above), issues the copy of page k + 3 and zeroes a sequence tail.
+// P(k) (the rescale shift d rides in the sign bits of hi bytes 0 - 7, as
+// described above), issues the copy of page k + 3 and zeroes a sequence tail.
 // Phase 2 (M(k) .. T(k + 1)): A runs the softmax of page k + 1, with its PV
 // share of page k (6 MFMAs, the weights of page k still in its registers)
 // issued between the softmax's pieces, and publishes P(k + 1); B runs the PV
@@ -2514,8 +1518,8 @@ __device__ __forceinline__ void decode_fp8_ab_body(const DecodeParams& p, const 
     const int nvis = min(p.causal ? max(n - (p.q_len - 1 - tq), 0) : n, unit_end);
     const int nvis_min = min(p.causal ? max(n - (p.q_len - 1), 0) : n, unit_end);
 
-    // PV A operands (V^T, 32 dims x 64 tokens) by transpose reads, as in the
-    // kernel above: dim tile D reads at tr_off[D % 2] + 64 (D / 2) (the
+    // PV A operands (V^T, 32 dims x 64 tokens) by transpose reads: dim tile
+    // D reads at tr_off[D % 2] + 64 (D / 2) (the
     // swizzle permutes chunks inside aligned groups of 4, and 2 D + (lane / 16) % 2
     // stays in the group of chunk 4 (D / 2))
     int tr_off[2];
@@ -2907,7 +1911,7 @@ void decode_fp8_ab_kernel(DecodeParams p) {
     const bool by_hw = cnt0 == 2 && cnt1 == 2 && cnt2 == 2 && cnt3 == 2;
     const bool is_a = by_hw ? lower == 0 : wv < 4;
     const int s = by_hw ? sid : (wv & 3);
-    for_each_piece<true>(p, w, [&](const Piece& pc) {
+    for_each_piece(p, w, [&](const Piece& pc) {
         if (is_a) decode_fp8_ab_body<true>(p, pc, lds, s, wv);
         else decode_fp8_ab_body<false>(p, pc, lds, s, wv);
     });
@@ -3149,8 +2153,7 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int units, hipStream_t stre
         if (e != hipSuccess) return e;
     }
     clear_stale_error();
-    if (p.bf16_four_waves) hipLaunchKernelGGL(decode_bf16_kernel, dim3(units), dim3(256), 0, stream, p);
-    else if (p.plan.group_ok) hipLaunchKernelGGL(decode_bf16_ab_kernel<true>, dim3(units), dim3(512), 0, stream, p);
+    if (p.plan.group_ok) hipLaunchKernelGGL(decode_bf16_ab_kernel<true>, dim3(units), dim3(512), 0, stream, p);
     else hipLaunchKernelGGL(decode_bf16_ab_kernel<false>, dim3(units), dim3(512), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -3165,8 +2168,7 @@ hipError_t launch_decode_fp8(const DecodeParams& p, int units, hipStream_t strea
         if (e != hipSuccess) return e;
     }
     clear_stale_error();
-    if (p.fp8_four_waves) hipLaunchKernelGGL(decode_fp8_kernel, dim3(units), dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(decode_fp8_ab_kernel, dim3(units), dim3(512), 0, stream, p);
+    hipLaunchKernelGGL(decode_fp8_ab_kernel, dim3(units), dim3(512), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (ev_after) return hipEventRecord(ev_after, stream);

@@ -289,6 +289,26 @@ def test_forced_splits_grouped_one_page_splits():
     compare(out, lse, o_ref, l_ref, what="grouped one-page splits")
 
 
+@pytest.mark.parametrize("dtype,num_splits", [("bf16", 1), ("bf16", 0), ("bf16", 3), ("bf16", 48),
+                                             ("fp8", 1), ("fp8", 0), ("fp8", 5)])
+def test_reference_max_moves(dtype, num_splits):
+    """Keys whose logits climb along each sequence, so that the lazy reference
+    maximum of a row moves several times inside one request: bf16 (slack 2^8)
+    with a logit step of 96 every 512 tokens (about 6 moves per row), fp8
+    (slack 2^5) with the rope part of the keys ramped up 12-fold (about 2).
+    With the plain N(0,1) inputs of the other tests it almost never moves.
+    The flags in the published weights and the rescale of every wave's
+    accumulators and sums all run; one piece, the auto plan, 3 splits and 48
+    forced splits (grouped runs for bf16, where the maximum restarts at each
+    split inside a run)."""
+    say(f"reference max moves {dtype} splits={num_splits}")
+    extra = dict(logit_step=96.0) if dtype == "bf16" else dict(rope_ramp=12.0)
+    inp = workloads.make_decode_inputs(3, 2, 128, [3100, 3500, 4000], dtype, seed=47, device=dev(), **extra)
+    o_ref, l_ref = run_oracle(inp)
+    out, lse = run_hip(inp, num_splits=num_splits)
+    compare(out, lse, o_ref, l_ref, dtype=dtype, what=f"max moves {dtype} splits={num_splits}")
+
+
 def test_more_fixed_splits_than_pages():
     """num_splits = 8 on sequences of 1-3 pages: each request gets min(8, pages) splits."""
     say("num_splits=8, 1-3 pages")

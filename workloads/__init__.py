@@ -152,12 +152,23 @@ def _seq_lens_for(cfg: dict, gen_cpu: torch.Generator):
 def make_decode_inputs(batch: int, q_len: int, heads: int, seq_lens, dtype: str = "bf16",
                        seed: int = 0, device="cpu", poison: bool = True, extra_pages: int = 3,
                        scale: float = DEFAULT_SCALE, causal: bool | None = None,
-                       dcp: int = 1, max_pages: int | None = None):
+                       dcp: int = 1, max_pages: int | None = None, rope_ramp: float = 0.0,
+                       logit_step: float = 0.0):
     """Inputs for one cache, or for D DCP shards of one logical cache.
 
     Returns a DecodeInputs when dcp == 1, else (global DecodeInputs, [shard DecodeInputs]).
     Shard r holds the global tokens t with t mod D == r, in order, in its own
     shuffled pool; all shards and the global cache see the same query.
+
+    rope_ramp > 0 multiplies the rope part (the last 64 dims) of token t of a
+    request of n tokens by 1 + rope_ramp * t / (n - 1) before storage, so that
+    the logits' spread, and with it the running row maximum, grows along the
+    sequence (the values, the first 512 dims, keep their distribution).
+
+    logit_step > 0 sets the last query dim to 1 and the last key dim of token t
+    to logit_step * floor(t / 512): every 512 tokens every row's logits rise by
+    scale * logit_step, so the running maximum of every row moves several times
+    along a long sequence while the softmax stays as spread as without it.
     """
     assert dtype in ("bf16", "fp8")
     seq_lens = [int(n) for n in seq_lens]
@@ -168,6 +179,17 @@ def make_decode_inputs(batch: int, q_len: int, heads: int, seq_lens, dtype: str 
     gen_dev = make_generator(seed + 1_000_003, device)
     q32 = torch.randn((batch, q_len, heads, QK_DIM), generator=gen_dev, device=device)
     rows32 = [torch.randn((n, QK_DIM), generator=gen_dev, device=device) for n in seq_lens]
+    if logit_step > 0:
+        q32[..., -1] = 1.0
+        for r in rows32:
+            r[:, -1] = logit_step * torch.div(torch.arange(r.shape[0], device=device), 512,
+                                              rounding_mode="floor").to(torch.float32)
+    if rope_ramp > 0:
+        for r in rows32:
+            n = r.shape[0]
+            if n > 1:
+                f = 1.0 + rope_ramp * torch.arange(n, device=device, dtype=torch.float32) / (n - 1)
+                r[:, V_DIM:] *= f[:, None]
 
     if dtype == "bf16":
         q = to_bf16(q32)
